@@ -1,0 +1,278 @@
+/*
+ * ssd.h -- C ABI of the MI355X (gfx950) Mamba2 SSD selective-state-space scan library.
+ *
+ * Three calls make up the path:
+ *   ssd_build_chunk_metadata  host, integer: split a varlen prefill batch into chunks;
+ *   ssd_prefill               device: chunked varlen prefill with initial states gathered
+ *                             from a state pool and the state written at every chunk end;
+ *   ssd_state_update          device: padded single-token / speculative decode update.
+ *
+ * The recurrence (per head h, state in R^{P x N}):
+ *     h_t = exp(delta_t * A_h) * h_{t-1} + delta_t * x_t B_t^T,   y_t = h_t C_t + D_h x_t
+ * is the selective SSM whose Delta, B and C depend on the input ("[vLLM] Mamba (SSM):
+ * linear-time sequence modeling", intro and paper key content).  Heads map onto B/C
+ * groups in contiguous blocks, g(h) = h / (H / G).
+ *
+ * Conventions shared by every call:
+ *   - Sizes and counts are int32; strides are in ELEMENTS of the tensor's dtype.
+ *   - "device" pointers are HIP device (or managed) memory; "host" pointers are ordinary
+ *     CPU memory.  The caller owns every buffer.  The library allocates nothing, keeps no
+ *     pointer after a call returns, never synchronises and launches only on `stream`.
+ *   - Every argument check that does not need device data runs before the first launch:
+ *     a call that returns an error launched nothing.  Checks that need device data
+ *     (index ranges, metadata consistency) run in the kernels: the offending item is
+ *     skipped (nothing of it is written) and *device_error_flag, when non-NULL, is set to
+ *     a nonzero SSD_DEVERR_* bit mask (the flag is only ever OR-ed, never cleared).
+ *   - No global mutable state: calls on different streams may run concurrently as long
+ *     as they do not write the same memory.
+ */
+#ifndef SSD_MI355X_H
+#define SSD_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSD_ABI_VERSION 1
+
+typedef enum ssd_status {
+  SSD_OK = 0,
+  SSD_ERR_NULL_POINTER = 1,  /* a required pointer is NULL                              */
+  SSD_ERR_BAD_SHAPE = 2,     /* a size or stride is out of range / inconsistent         */
+  SSD_ERR_BAD_METADATA = 3,  /* host metadata inputs are inconsistent                   */
+  SSD_ERR_UNSUPPORTED = 4,   /* (dtype, head_dim, dstate, chunk_size) not instantiated  */
+  SSD_ERR_CAPACITY = 5,      /* an output array is too small; the required size is
+                                reported through the *_out count argument              */
+  SSD_ERR_WORKSPACE = 6,     /* workspace NULL or smaller than ssd_prefill_workspace_size */
+  SSD_ERR_HIP = 7            /* a HIP launch failed                                     */
+} ssd_status;
+
+/* device-side error bits OR-ed into *device_error_flag */
+#define SSD_DEVERR_CHUNK_RANGE 1   /* a chunk is empty, longer than chunk_size or leaves
+                                      its sequence                                     */
+#define SSD_DEVERR_SLOT_RANGE 2    /* a state index is outside [0, num_slots)           */
+#define SSD_DEVERR_ACCEPTED 4      /* num_accepted_tokens outside [1, ntok]            */
+
+typedef enum ssd_dtype { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
+
+typedef enum ssd_a_kind {
+  SSD_A_SCALAR = 0,  /* Mamba2: A[H], one decay per head                                 */
+  SSD_A_DIAG = 1     /* Mamba1: A[H, N], one decay per (channel, state); requires P == 1 */
+} ssd_a_kind;
+
+/* A hipStream_t passed as an opaque pointer (NULL = the null stream). */
+typedef void* ssd_stream_t;
+
+/* ---------------------------------------------------------------------------------------
+ * Library information
+ * ------------------------------------------------------------------------------------- */
+int ssd_abi_version(void);
+const char* ssd_status_string(ssd_status status); /* static string, never NULL */
+
+/* ---------------------------------------------------------------------------------------
+ * Chunk metadata (host, integer, bit-exact)
+ *
+ * Defined by the chunk-metadata section of "[vLLM] Mamba (SSM): linear-time sequence
+ * modeling" (_compute_chunk_metadata): every chunk holds tokens of ONE sequence, and a
+ * chunk ends at every absolute multiple of chunk_size so the state can be taken out
+ * there.  A resumed sequence whose num_computed is not a multiple of chunk_size first
+ * finishes the open chunk with min(cdiv(nc, cs) * cs - nc, new_tokens) tokens; the rest
+ * is cut into chunks of min(cs, remaining) tokens.  The page's listing stops after the
+ * partial-chunk branch; the rest (full chunks, then the tail) is the plain reading of its
+ * two stated guarantees.  The single-chunk case matches the warm-up inputs of "vLLM Mamba2
+ * SSD kernel warm-up" (mamba_mixer2.py section): cu_seqlens=[0,cs] gives
+ * cu_chunk_seqlens=[0,cs], seq_idx=[0], last_chunk_indices=[0].
+ *
+ *   num_seqs            S >= 0
+ *   cu_seqlens          host int32 [S+1], cu_seqlens[0] == 0, strictly increasing (every
+ *                       sequence has >= 1 new token)
+ *   num_computed        host int32 [S] tokens already processed per sequence (>= 0), or
+ *                       NULL for all zero
+ *   chunk_size          > 0
+ *   capacity            entries available in seq_idx (cu_chunk_seqlens must hold
+ *                       capacity + 1 entries); last_chunk_indices must hold S entries
+ *   cu_chunk_seqlens    host int32 [C+1] out: token offset of every chunk start, then T
+ *   seq_idx             host int32 [C]   out: sequence of every chunk
+ *   last_chunk_indices  host int32 [S]   out: index of every sequence's last chunk
+ *   num_chunks_out      host int32       out: C (also on SSD_ERR_CAPACITY)
+ *
+ * Errors: SSD_ERR_NULL_POINTER, SSD_ERR_BAD_SHAPE (S < 0, chunk_size <= 0),
+ * SSD_ERR_BAD_METADATA (cu_seqlens[0] != 0, a sequence with < 1 token, num_computed < 0,
+ * an int32 overflow), SSD_ERR_CAPACITY (C > capacity; nothing but *num_chunks_out is
+ * written).
+ * ------------------------------------------------------------------------------------- */
+ssd_status ssd_chunk_metadata_count(int32_t num_seqs, const int32_t* cu_seqlens,
+                                    const int32_t* num_computed, int32_t chunk_size,
+                                    int32_t* num_chunks_out);
+ssd_status ssd_build_chunk_metadata(int32_t num_seqs, const int32_t* cu_seqlens,
+                                    const int32_t* num_computed, int32_t chunk_size,
+                                    int32_t capacity, int32_t* cu_chunk_seqlens,
+                                    int32_t* seq_idx, int32_t* last_chunk_indices,
+                                    int32_t* num_chunks_out);
+
+/* ---------------------------------------------------------------------------------------
+ * Prefill
+ *
+ * The argument set follows the varlen SSD call made by the warm-up code of "vLLM Mamba2
+ * SSD kernel warm-up" (mamba_mixer2.py section): x, dt, A, B, C, chunk_size, cu_seqlens,
+ * cu_chunk_seqlens, last_chunk_indices, seq_idx, out, D, dt_bias, initial_states,
+ * dt_softplus, dt_limit and an fp32 state dtype.  Initial states are gathered from a state
+ * pool laid out [slots, H, P, N] (the SSM block shape (num_heads, head_dim, state_size) of
+ * "vLLM v0.20.0 adds disaggregated serving for hybrid SSM models"), selected per sequence
+ * by state_indices and has_initial_state ("[vLLM] Mamba (SSM)", metadata dataclass:
+ * has_initial_states_p, state_indices_tensor_p).  The state at the end of every chunk is
+ * written out for prefix caching ("why this design", item 3).
+ *
+ * Computes, for every sequence r (tokens [cu_seqlens[r], cu_seqlens[r+1])):
+ *   h = has_initial_state[r] ? pool[state_indices[r]] : 0
+ *   for each token t, head h:  delta = clamp(softplus?(dt[t,h] + dt_bias[h]), dt_min, dt_max)
+ *       state = exp(delta*A) state + delta x[t,h,:] B[t,g,:]^T;  y[t,h,:] = state C[t,g,:] + D x
+ *   chunk_states_out[k] = state after the last token of chunk k (every chunk)
+ *   if write_final_to_pool: pool[state_indices[r]] = state after the sequence's last token
+ * The pool slots are read before any is written (a sequence may resume from, and write
+ * back to, the same slot).  state_indices of different sequences must be distinct.
+ * ------------------------------------------------------------------------------------- */
+typedef struct ssd_prefill_args {
+  /* sizes */
+  int32_t T;            /* total tokens (sum of sequence lengths)                      */
+  int32_t H;            /* heads (SSD_A_SCALAR) or channels d_inner (SSD_A_DIAG)        */
+  int32_t P;            /* head_dim (1 for SSD_A_DIAG)                                  */
+  int32_t G;            /* B/C groups; H % G == 0 (1 for SSD_A_DIAG)                    */
+  int32_t N;            /* dstate                                                       */
+  int32_t chunk_size;   /* cs                                                           */
+  int32_t num_seqs;     /* S                                                            */
+  int32_t num_chunks;   /* C, as returned by ssd_build_chunk_metadata                   */
+  int32_t in_dtype;     /* ssd_dtype of x, dt, B, C and y                                */
+  int32_t a_kind;       /* ssd_a_kind                                                   */
+
+  /* token tensors (device).  Within one token the layout is contiguous ([H,P] / [H] /
+   * [G,N]); the *_stride_t arguments give the distance between consecutive tokens, so x,
+   * B and C may be views into one projection buffer. */
+  const void* x;  int64_t x_stride_t;   /* [T, H, P], stride >= H*P                       */
+  const void* dt; int64_t dt_stride_t;  /* [T, H],    stride >= H                         */
+  const void* B;                        /* [T, G, N]                                      */
+  const void* C;  int64_t bc_stride_t;  /* [T, G, N], stride >= G*N (shared by B and C)    */
+  void* y;        int64_t y_stride_t;   /* [T, H, P] out, in_dtype, stride >= H*P         */
+
+  /* parameters (device, fp32) */
+  const float* A;        /* [H] (SSD_A_SCALAR) or [H, N] (SSD_A_DIAG); not NULL         */
+  const float* D;        /* [H] skip connection, NULL = 0                                */
+  const float* dt_bias;  /* [H], NULL = 0                                                */
+  int32_t dt_softplus;   /* 0/1: apply log(1 + e^v) after adding dt_bias                 */
+  float dt_min, dt_max;  /* clamp applied last; (0, +inf) is the usual limit             */
+
+  /* chunk metadata (device int32), from ssd_build_chunk_metadata */
+  const int32_t* cu_seqlens;         /* [S+1] */
+  const int32_t* cu_chunk_seqlens;   /* [C+1] */
+  const int32_t* seq_idx;            /* [C]   */
+  const int32_t* last_chunk_indices; /* [S]   */
+
+  /* state pool (device, fp32, [num_slots, H, P, N] with slot_stride elements between
+   * slots, slot_stride >= H*P*N).  May be NULL when no sequence has an initial state and
+   * write_final_to_pool == 0. */
+  float* state_pool;
+  int64_t slot_stride;
+  int32_t num_slots;
+  const int32_t* state_indices;      /* [S] slot per sequence (device); NULL only without a pool */
+  const int32_t* has_initial_state;  /* [S] 0/1 (device); NULL = no initial states          */
+  int32_t write_final_to_pool;       /* 0/1                                               */
+
+  /* outputs (device) */
+  float* chunk_states_out;   /* [C, H, P, N] fp32 state at the end of every chunk; NULL =
+                                not wanted (a workspace holds them instead)              */
+  int32_t* device_error_flag;/* NULL or an int32 that receives SSD_DEVERR_* bits         */
+
+  /* optional per-step outputs (device, NULL = not wanted; SSD_A_SCALAR only) */
+  float* dA_cumsum_out;      /* [H, T] fp32: inclusive within-chunk cumsum of delta*A     */
+  float* cb_out;             /* [C, G, cs, cs] fp32: C_l . B_s for s <= l < chunk length,
+                                other entries untouched                                   */
+  float* chunk_local_states_out; /* [C, H, P, N] fp32: the state each chunk produces from a
+                                zero state (before the inter-chunk pass)                  */
+
+  /* optional timing hook: NULL, or SSD_PREFILL_MAX_KERNELS + 1 hipEvent_t handles (created
+   * by the caller) that the call records on `stream` before each of its kernels and after
+   * the last one; entries past the kernels this call launches are not touched.  The number
+   * of kernels launched is reported by ssd_prefill_kernel_count. */
+  void* const* profile_events;
+} ssd_prefill_args;
+
+#define SSD_PREFILL_MAX_KERNELS 3
+
+/* Number of kernels ssd_prefill launches for these arguments (3 for SSD_A_SCALAR, 1 for
+ * SSD_A_DIAG, 0 for an empty batch) and, when `names` is not NULL, a static name for each
+ * kernel in launch order (names must hold SSD_PREFILL_MAX_KERNELS entries). */
+ssd_status ssd_prefill_kernel_count(const ssd_prefill_args* args, int32_t* count,
+                                    const char** names);
+
+/* Bytes of device workspace ssd_prefill needs for these arguments (0 is possible).  The
+ * workspace must be 256-byte aligned and must not alias any argument.  It holds no state
+ * between calls.  Errors: as ssd_prefill's host checks. */
+ssd_status ssd_prefill_workspace_size(const ssd_prefill_args* args, size_t* bytes);
+
+/* Run the prefill on `stream`.  workspace: device memory of >= the reported size (may be
+ * NULL when that size is 0).  Errors: SSD_ERR_NULL_POINTER, SSD_ERR_BAD_SHAPE,
+ * SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ERR_HIP.  T == 0 (with S == 0) is a no-op. */
+ssd_status ssd_prefill(const ssd_prefill_args* args, void* workspace,
+                       size_t workspace_bytes, ssd_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Decode state update
+ *
+ * One decode step for a padded, uniform batch ("[vLLM] Mamba (SSM)": decode metadata,
+ * MetadataBuilder init with a (max batch, 1 + num_spec_tokens) index tensor, and the CUDA
+ * Graph section, which pads the rows past the live ones with NULL_BLOCK_ID so one graph
+ * serves every batch size).  Every row carries ntok = 1 + num_spec_tokens tokens.
+ *
+ * For every row r with state_indices[r, 0] != null_block_id (other rows are skipped: no
+ * state read, no write, y untouched):
+ *   a = num_accepted_tokens[r] (1 if the pointer is NULL)
+ *   state = pool[state_indices[r, a-1]]        (read before any slot is written; this is
+ *                                               the restore from the right checkpoint of
+ *                                               "why this design", item 4)
+ *   for j in 0..ntok-1:  advance state by token (r, j); y[r, j] = state C + D x;
+ *                        pool[state_indices[r, j]] = state
+ * Slot indices of live rows must be distinct across rows (a row may read the slot it
+ * writes).  All ntok outputs are produced: acceptance is decided after this step.
+ * ------------------------------------------------------------------------------------- */
+typedef struct ssd_decode_args {
+  int32_t B_pad;        /* rows, including padding rows                                 */
+  int32_t ntok;         /* tokens per row = 1 + speculative tokens, >= 1                */
+  int32_t H, P, G, N;
+  int32_t in_dtype;     /* ssd_dtype of x, dt, B, C and y                                */
+  int32_t a_kind;       /* SSD_A_SCALAR only                                            */
+
+  /* token tensors (device, contiguous) */
+  const void* x;        /* [B_pad, ntok, H, P] */
+  const void* dt;       /* [B_pad, ntok, H]    */
+  const void* B;        /* [B_pad, ntok, G, N] */
+  const void* C;        /* [B_pad, ntok, G, N] */
+  void* y;              /* [B_pad, ntok, H, P] out */
+
+  const float* A;       /* [H] */
+  const float* D;       /* [H] or NULL */
+  const float* dt_bias; /* [H] or NULL */
+  int32_t dt_softplus;
+  float dt_min, dt_max;
+
+  float* state_pool;    /* [num_slots, H, P, N] fp32, slot_stride >= H*P*N */
+  int64_t slot_stride;
+  int32_t num_slots;
+  const int32_t* state_indices;       /* [B_pad, ntok] (device) */
+  const int32_t* num_accepted_tokens; /* [B_pad] (device) or NULL */
+  int32_t null_block_id;
+  int32_t* device_error_flag;         /* NULL or an int32 receiving SSD_DEVERR_* bits */
+  void* const* profile_events;        /* NULL or 2 hipEvent_t recorded before and after
+                                         the update kernel (timing hook)              */
+} ssd_decode_args;
+
+/* Errors: SSD_ERR_NULL_POINTER, SSD_ERR_BAD_SHAPE, SSD_ERR_UNSUPPORTED, SSD_ERR_HIP.
+ * B_pad == 0 is a no-op. */
+ssd_status ssd_state_update(const ssd_decode_args* args, ssd_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SSD_MI355X_H */

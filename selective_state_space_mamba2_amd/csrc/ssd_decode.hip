@@ -1,0 +1,144 @@
+// ssd_decode.hip -- padded speculative decode state update (one workgroup per row x head).
+//
+// Decode is a sequential per-token update ("[vLLM] Mamba (SSM)", why-this-design item 2);
+// rows padded with NULL_BLOCK_ID are skipped (CUDA Graph section) and the starting state is
+// restored from column num_accepted-1 of the row's index list (item 4).
+//
+// Work split: one 256-thread workgroup owns the P x N fp32 state of one (row, head).  Each
+// thread keeps ITERS float4 of it in registers: thread t holds columns n0 = 4*(t % NQ) ..
+// n0+3 (NQ = N/4) of rows p = i*(256/NQ) + t/NQ.  One wave-wide float4 load therefore reads
+// contiguous 1 KB of the slot (coalesced gather), and y[p] = sum_n h[p,n] C[n] is a
+// reduction across the NQ lanes that share p.  The state is read once before any write
+// (the source slot may be one of the destinations), then written after every token with
+// non-temporal stores (the checkpoints are not re-read by this call).
+#include "ssd_params.h"
+
+namespace ssd {
+
+template <typename T, int N, int ITERS>
+__global__ __launch_bounds__(256) void k_state_update(DecodeParams p) {
+  constexpr int NQ = N / 4;          // float4 per state row
+  constexpr int RP = 256 / NQ;       // state rows covered per iteration
+  extern __shared__ __attribute__((aligned(16))) float lds[];
+  const int h = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
+  const int ntok = p.ntok, P = p.P, H = p.H;
+  const int* idx_r = p.idx + int64_t(r) * ntok;
+  if (idx_r[0] == p.null_id) return;  // padding row: nothing read, nothing written
+
+  const int acc_tok = p.num_acc ? p.num_acc[r] : 1;
+  bool bad = acc_tok < 1 || acc_tok > ntok;
+  if (!bad) {
+    for (int j = 0; j < ntok; ++j) {
+      const int s = idx_r[j];
+      bad |= (s < 0 || s >= p.num_slots);
+    }
+  }
+  if (bad) {
+    if (tid == 0)
+      raise_flag(p.flag, (acc_tok < 1 || acc_tok > ntok) ? SSD_DEVERR_ACCEPTED
+                                                         : SSD_DEVERR_SLOT_RANGE);
+    return;
+  }
+
+  // Stage this row's token data for head h: x[ntok][P], B[ntok][N], C[ntok][N], delta.
+  // B and C first: N is a multiple of 16, so their float4 reads stay 16-byte aligned.
+  float* bs = lds;
+  float* cs = bs + ntok * N;
+  float* xs = cs + ntok * N;
+  float* ys = xs + ntok * P;
+  float* ds = ys + ntok * P;
+  const int g = h / (H / p.G);
+  const T* xg = static_cast<const T*>(p.x);
+  const T* bg = static_cast<const T*>(p.B);
+  const T* cg = static_cast<const T*>(p.Cm);
+  const T* dg = static_cast<const T*>(p.dt);
+  for (int e = tid; e < ntok * P; e += 256) {
+    const int j = e / P, pp = e - j * P;
+    xs[e] = Elem<T>::load(xg + ((int64_t(r) * ntok + j) * H + h) * P + pp);
+  }
+  for (int e = tid; e < ntok * N; e += 256) {
+    const int j = e / N, n = e - j * N;
+    const int64_t off = ((int64_t(r) * ntok + j) * p.G + g) * N + n;
+    bs[e] = Elem<T>::load(bg + off);
+    cs[e] = Elem<T>::load(cg + off);
+  }
+  if (tid < ntok) ds[tid] = p.prep(Elem<T>::load(dg + (int64_t(r) * ntok + tid) * H + h), h);
+
+  // Gather the source state before any write.
+  const int lane_q = tid % NQ, prow = tid / NQ;
+  const int64_t head_off = int64_t(h) * P * N;
+  const float4_v* src = reinterpret_cast<const float4_v*>(
+      p.pool + int64_t(idx_r[acc_tok - 1]) * p.slot_stride + head_off);
+  float4_v st[ITERS];
+#pragma unroll
+  for (int i = 0; i < ITERS; ++i) {
+    const int pr = i * RP + prow;
+    st[i] = pr < P ? src[pr * NQ + lane_q] : float4_v{0.f, 0.f, 0.f, 0.f};
+  }
+  __syncthreads();
+
+  const float Ah = p.A[h];
+  const float Dh = p.D ? p.D[h] : 0.f;
+  for (int j = 0; j < ntok; ++j) {
+    const float delta = ds[j];
+    const float decay = fast_exp(delta * Ah);
+    const float4_v bv = *reinterpret_cast<const float4_v*>(bs + j * N + 4 * lane_q);
+    const float4_v cv = *reinterpret_cast<const float4_v*>(cs + j * N + 4 * lane_q);
+    float4_v* dst = reinterpret_cast<float4_v*>(
+        p.pool + int64_t(idx_r[j]) * p.slot_stride + head_off);
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) {
+      const int pr = i * RP + prow;
+      const float xp = pr < P ? xs[j * P + pr] : 0.f;
+      const float dx = delta * xp;
+      st[i] = decay * st[i] + dx * bv;
+      float part = st[i].x * cv.x + st[i].y * cv.y + st[i].z * cv.z + st[i].w * cv.w;
+#pragma unroll
+      for (int off = NQ / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
+      if (pr < P) {
+        if (lane_q == 0) ys[j * P + pr] = part + Dh * xp;
+        __builtin_nontemporal_store(st[i], dst + pr * NQ + lane_q);
+      }
+    }
+  }
+  __syncthreads();
+  T* yg = static_cast<T*>(p.y);
+  for (int e = tid; e < ntok * P; e += 256) {
+    const int j = e / P, pp = e - j * P;
+    Elem<T>::store(yg + ((int64_t(r) * ntok + j) * H + h) * P + pp, ys[e]);
+  }
+}
+
+template <typename T, int N>
+static hipError_t launch_n(const DecodeParams& p, hipStream_t s, void* const* ev) {
+  const int rows_per_iter = 256 / (N / 4);
+  const int iters = (p.P + rows_per_iter - 1) / rows_per_iter;
+  const dim3 grid(p.H, p.B_pad);
+  const size_t lds = decode_lds_bytes(p.ntok, p.P, N);
+  record_event(ev, 0, s);
+  if (iters <= 1) hipLaunchKernelGGL((k_state_update<T, N, 1>), grid, dim3(256), lds, s, p);
+  else if (iters <= 2) hipLaunchKernelGGL((k_state_update<T, N, 2>), grid, dim3(256), lds, s, p);
+  else if (iters <= 4) hipLaunchKernelGGL((k_state_update<T, N, 4>), grid, dim3(256), lds, s, p);
+  else if (iters <= 8) hipLaunchKernelGGL((k_state_update<T, N, 8>), grid, dim3(256), lds, s, p);
+  else hipLaunchKernelGGL((k_state_update<T, N, 16>), grid, dim3(256), lds, s, p);
+  record_event(ev, 1, s);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_t(const DecodeParams& p, hipStream_t s, void* const* ev) {
+  switch (p.N) {
+    case 16: return launch_n<T, 16>(p, s, ev);
+    case 32: return launch_n<T, 32>(p, s, ev);
+    case 64: return launch_n<T, 64>(p, s, ev);
+    case 128: return launch_n<T, 128>(p, s, ev);
+    default: return launch_n<T, 256>(p, s, ev);
+  }
+}
+
+hipError_t launch_state_update(int in_dtype, const DecodeParams& p, hipStream_t s,
+                               void* const* events) {
+  return in_dtype == SSD_BF16 ? launch_t<bf16_t>(p, s, events) : launch_t<float>(p, s, events);
+}
+
+}  // namespace ssd

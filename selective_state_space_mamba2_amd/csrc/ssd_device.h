@@ -1,0 +1,126 @@
+// ssd_device.h -- device helpers shared by the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+typedef uint16_t bf16_t;  // raw bf16 bits in global memory and LDS
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_v;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_v;
+typedef float float4_v __attribute__((ext_vector_type(4)));
+typedef float float2_v __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2_v __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_v __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// exp(v) through the hardware base-2 exponential: exp(v) = 2^(v * log2(e)).
+__device__ __forceinline__ float fast_exp(float v) {
+  return __builtin_amdgcn_exp2f(v * kLog2e);
+}
+
+// softplus(v) = log(1 + e^v); for v > 20 the result equals v to < 2.1e-9 absolute.
+__device__ __forceinline__ float softplus_f(float v) {
+  return v > 20.f ? v : __logf(1.f + __expf(v));
+}
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t v) {
+  return __uint_as_float(uint32_t(v) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return bf16_t((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return bf16_t(u >> 16);
+}
+
+// Two fp32 -> packed pair of bf16 (low half = a).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return uint32_t(f32_to_bf16(a)) | (uint32_t(f32_to_bf16(b)) << 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float load(const float* p) { return *p; }
+  static __device__ __forceinline__ void store(float* p, float v) { *p = v; }
+};
+template <> struct Elem<bf16_t> {
+  static __device__ __forceinline__ float load(const bf16_t* p) { return bf16_to_f32(*p); }
+  static __device__ __forceinline__ void store(bf16_t* p, float v) { *p = f32_to_bf16(v); }
+};
+
+// delta from raw dt: + bias, optional softplus, clamp.
+struct DtPrep {
+  const float* bias;
+  int softplus;
+  float lo, hi;
+  __device__ __forceinline__ float operator()(float raw, int h) const {
+    float v = raw + (bias ? bias[h] : 0.f);
+    if (softplus) v = softplus_f(v);
+    return fminf(fmaxf(v, lo), hi);
+  }
+};
+
+// ---------------------------------------------------------------------------------------
+// MFMA 16x16 tiles.  A 16x16 fp32 accumulator tile lives in f32x4_v per lane: lane L holds
+// rows 4*(L/16)+r (r = 0..3) of column L%16.  An operand fragment is 8 values per lane:
+// for the A operand lane L supplies row L%16, for the B operand column L%16, and the 8
+// values fill the lane's 8 k-slots.  The contraction runs over all 32 (lane-group, slot)
+// pairs, so any consistent assignment of the contracted index to k-slots is valid as long
+// as A and B use the same one.
+// ---------------------------------------------------------------------------------------
+struct Frag8 {  // 8 operand values held as 4 packed bf16 pairs
+  uint32_t w[4];
+};
+
+__device__ __forceinline__ f32x4_v mma_bf16(const Frag8& a, const Frag8& b, f32x4_v c) {
+  bf16x8_v av, bv;
+  __builtin_memcpy(&av, a.w, 16);
+  __builtin_memcpy(&bv, b.w, 16);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, c, 0, 0, 0);
+}
+
+struct Frag8f {  // 8 fp32 operand values (the fp32 path issues 8 K=4 instructions)
+  float v[8];
+};
+
+__device__ __forceinline__ f32x4_v mma_f32(const Frag8f& a, const Frag8f& b, f32x4_v c) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[i], b.v[i], c, 0, 0, 0);
+  return c;
+}
+
+// ---------------------------------------------------------------------------------------
+// Block-wide inclusive prefix sum of one float per thread (wave64 scans + LDS).
+// `scratch` must hold blockDim.x / 64 floats.  All threads must call it.
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ float wave_inclusive_scan(float v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    float o = __shfl_up(v, off, 64);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+__device__ __forceinline__ float block_inclusive_scan(float v, float* scratch) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  v = wave_inclusive_scan(v);
+  if (lane == 63) scratch[wave] = v;
+  __syncthreads();
+  float base = 0.f;
+  for (int w = 0; w < wave; ++w) base += scratch[w];
+  __syncthreads();
+  return v + base;
+}
+
+__device__ __forceinline__ void raise_flag(int* flag, int bits) {
+  if (flag) atomicOr(flag, bits);
+}
+
+}  // namespace ssd

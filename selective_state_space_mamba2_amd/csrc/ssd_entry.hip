@@ -1,0 +1,126 @@
+// ssd_entry.hip -- C-ABI entry points that launch kernels: argument resolution, the
+// device-facing checks (alignment of vector accesses, workspace), and the launch sequence.
+#include <cstdint>
+
+#include "ssd_params.h"
+
+namespace {
+
+bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+// The chunked kernels read x, B, C rows and write y rows with 16-byte vector accesses and
+// move states as float4: check the pointers and strides allow that.
+ssd_status check_vector_access(const ssd_prefill_args* a) {
+  const int esz = a->in_dtype == SSD_BF16 ? 2 : 4;
+  const int64_t per16 = 16 / esz;
+  if (!aligned(a->x, 16) || !aligned(a->B, 16) || !aligned(a->C, 16) || !aligned(a->y, 16))
+    return SSD_ERR_UNSUPPORTED;
+  if (a->x_stride_t % per16 || a->bc_stride_t % per16 || a->y_stride_t % per16)
+    return SSD_ERR_UNSUPPORTED;
+  if (a->state_pool && (!aligned(a->state_pool, 16) || a->slot_stride % 4))
+    return SSD_ERR_UNSUPPORTED;
+  if (a->chunk_states_out && !aligned(a->chunk_states_out, 16)) return SSD_ERR_UNSUPPORTED;
+  return SSD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ssd_status ssd_prefill_workspace_size(const ssd_prefill_args* a, size_t* bytes) {
+  if (!bytes) return SSD_ERR_NULL_POINTER;
+  ssd::PrefillPlan plan;
+  const ssd_status st = ssd::plan_prefill(a, &plan);
+  if (st != SSD_OK) return st;
+  *bytes = plan.ws_bytes;
+  return SSD_OK;
+}
+
+ssd_status ssd_prefill(const ssd_prefill_args* a, void* workspace, size_t workspace_bytes,
+                       ssd_stream_t stream) {
+  ssd::PrefillPlan plan;
+  ssd_status st = ssd::plan_prefill(a, &plan);
+  if (st != SSD_OK) return st;
+  if (a->num_seqs == 0) return SSD_OK;
+  if (plan.ws_bytes > 0 &&
+      (!workspace || workspace_bytes < plan.ws_bytes || !aligned(workspace, 256)))
+    return SSD_ERR_WORKSPACE;
+  if (plan.kind == ssd::PrefillKind::kChunked) {
+    st = check_vector_access(a);
+    if (st != SSD_OK) return st;
+  } else if (a->state_pool && (!aligned(a->state_pool, 16) || a->slot_stride % 4)) {
+    return SSD_ERR_UNSUPPORTED;
+  } else if (a->chunk_states_out && !aligned(a->chunk_states_out, 16)) {
+    return SSD_ERR_UNSUPPORTED;
+  }
+
+  ssd::PrefillParams p{};
+  p.T = a->T; p.H = a->H; p.P = a->P; p.G = a->G; p.N = a->N;
+  p.S = a->num_seqs; p.C = a->num_chunks; p.cs = a->chunk_size;
+  p.x = a->x; p.x_st = a->x_stride_t;
+  p.dt = a->dt; p.dt_st = a->dt_stride_t;
+  p.B = a->B; p.Cm = a->C; p.bc_st = a->bc_stride_t;
+  p.y = a->y; p.y_st = a->y_stride_t;
+  p.A = a->A; p.D = a->D;
+  p.prep = ssd::DtPrep{a->dt_bias, a->dt_softplus ? 1 : 0, a->dt_min, a->dt_max};
+  p.cu_seqlens = a->cu_seqlens; p.cu_chunk = a->cu_chunk_seqlens;
+  p.seq_idx = a->seq_idx; p.last_chunk = a->last_chunk_indices;
+  p.pool = a->state_pool; p.slot_stride = a->slot_stride; p.num_slots = a->num_slots;
+  p.state_idx = a->state_indices; p.has_init = a->has_initial_state;
+  p.write_final = (a->write_final_to_pool && a->state_pool) ? 1 : 0;
+  p.flag = a->device_error_flag;
+  p.dA_cumsum_out = a->dA_cumsum_out;
+  p.cb_out = a->cb_out;
+  p.local_states_out = a->chunk_local_states_out;
+  char* ws = static_cast<char*>(workspace);
+  p.states = a->chunk_states_out;
+  if (plan.kind == ssd::PrefillKind::kChunked) {
+    p.dA_last = reinterpret_cast<float*>(ws + plan.off_dA_last);
+    p.init_copy = plan.has_init_copy ? reinterpret_cast<float*>(ws + plan.off_init) : nullptr;
+    if (plan.states_in_ws) p.states = reinterpret_cast<float*>(ws + plan.off_states);
+  }
+
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = plan.kind == ssd::PrefillKind::kChunked
+                           ? ssd::launch_chunked_prefill(plan.variant, p, s, a->profile_events)
+                           : ssd::launch_diag_prefill(a->in_dtype, p, s, a->profile_events);
+  return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+}
+
+ssd_status ssd_prefill_kernel_count(const ssd_prefill_args* a, int32_t* count,
+                                    const char** names) {
+  if (!count) return SSD_ERR_NULL_POINTER;
+  ssd::PrefillPlan plan;
+  const ssd_status st = ssd::plan_prefill(a, &plan);
+  if (st != SSD_OK) return st;
+  static const char* const kChunked[] = {"k_chunk_state", "k_state_passing", "k_chunk_scan"};
+  static const char* const kDiag[] = {"k_diag_scan"};
+  *count = 0;
+  if (a->num_seqs == 0) return SSD_OK;
+  const char* const* list = plan.kind == ssd::PrefillKind::kChunked ? kChunked : kDiag;
+  *count = plan.kind == ssd::PrefillKind::kChunked ? 3 : 1;
+  if (names)
+    for (int i = 0; i < *count; ++i) names[i] = list[i];
+  return SSD_OK;
+}
+
+ssd_status ssd_state_update(const ssd_decode_args* a, ssd_stream_t stream) {
+  ssd_status st = ssd::check_decode(a);
+  if (st != SSD_OK) return st;
+  if (a->B_pad == 0) return SSD_OK;
+  if (ssd::decode_lds_bytes(a->ntok, a->P, a->N) > 64 * 1024) return SSD_ERR_UNSUPPORTED;
+  if (!aligned(a->state_pool, 16) || a->slot_stride % 4) return SSD_ERR_UNSUPPORTED;
+  ssd::DecodeParams p{};
+  p.B_pad = a->B_pad; p.ntok = a->ntok; p.H = a->H; p.P = a->P; p.G = a->G; p.N = a->N;
+  p.x = a->x; p.dt = a->dt; p.B = a->B; p.Cm = a->C; p.y = a->y;
+  p.A = a->A; p.D = a->D;
+  p.prep = ssd::DtPrep{a->dt_bias, a->dt_softplus ? 1 : 0, a->dt_min, a->dt_max};
+  p.pool = a->state_pool; p.slot_stride = a->slot_stride; p.num_slots = a->num_slots;
+  p.idx = a->state_indices; p.num_acc = a->num_accepted_tokens;
+  p.null_id = a->null_block_id; p.flag = a->device_error_flag;
+  const hipError_t e = ssd::launch_state_update(a->in_dtype, p, static_cast<hipStream_t>(stream),
+                                                a->profile_events);
+  return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,212 @@
+// ssd_host.cpp -- host half of the C ABI: status strings, the chunk-metadata builder,
+// argument validation and workspace planning.  Plain C++; needs no GPU.
+#include <cmath>
+#include <cstdint>
+#include <limits>
+
+#include "ssd.h"
+#include "ssd_plan.h"
+
+namespace ssd {
+
+// Chunked-prefill instantiations: (dtype, head_dim, dstate, chunk_size).  The kernels'
+// launch table in ssd_prefill.hip lists the same shapes in the same order.
+const ChunkedShape kChunkedShapes[] = {
+    {SSD_BF16, 64, 128, 256}, {SSD_BF16, 64, 128, 128}, {SSD_BF16, 64, 128, 64},
+    {SSD_BF16, 16, 16, 64},   {SSD_F32, 16, 16, 64},    {SSD_F32, 64, 128, 64},
+};
+const int kNumChunkedShapes = sizeof(kChunkedShapes) / sizeof(kChunkedShapes[0]);
+
+bool decode_supports_n(int N) {
+  return N == 16 || N == 32 || N == 64 || N == 128 || N == 256;
+}
+
+static bool valid_dtype(int32_t d) { return d == SSD_F32 || d == SSD_BF16; }
+
+ssd_status plan_prefill(const ssd_prefill_args* a, PrefillPlan* plan) {
+  if (!a || !plan) return SSD_ERR_NULL_POINTER;
+  *plan = PrefillPlan{};
+  if (a->T < 0 || a->num_seqs < 0 || a->num_chunks < 0) return SSD_ERR_BAD_SHAPE;
+  if (a->H < 1 || a->P < 1 || a->G < 1 || a->N < 1 || a->chunk_size < 1)
+    return SSD_ERR_BAD_SHAPE;
+  if (a->H % a->G != 0) return SSD_ERR_BAD_SHAPE;
+  if (!valid_dtype(a->in_dtype)) return SSD_ERR_BAD_SHAPE;
+  if (a->a_kind != SSD_A_SCALAR && a->a_kind != SSD_A_DIAG) return SSD_ERR_BAD_SHAPE;
+  if (a->num_seqs == 0) {
+    // an empty batch: nothing to do
+    if (a->T != 0 || a->num_chunks != 0) return SSD_ERR_BAD_SHAPE;
+    return SSD_OK;
+  }
+  // every sequence has >= 1 token and every chunk >= 1 token
+  if (a->T < a->num_seqs || a->num_chunks < a->num_seqs || a->num_chunks > a->T)
+    return SSD_ERR_BAD_SHAPE;
+  const int64_t HP = int64_t(a->H) * a->P;
+  const int64_t state = HP * a->N;
+  if (a->x_stride_t < HP || a->y_stride_t < HP || a->dt_stride_t < a->H ||
+      a->bc_stride_t < int64_t(a->G) * a->N)
+    return SSD_ERR_BAD_SHAPE;
+  if (!a->x || !a->dt || !a->B || !a->C || !a->y || !a->A) return SSD_ERR_NULL_POINTER;
+  if (!a->cu_seqlens || !a->cu_chunk_seqlens || !a->seq_idx || !a->last_chunk_indices)
+    return SSD_ERR_NULL_POINTER;
+  const bool need_pool = a->has_initial_state != nullptr || a->write_final_to_pool != 0;
+  if (need_pool) {
+    if (!a->state_pool || !a->state_indices) return SSD_ERR_NULL_POINTER;
+  }
+  if (a->state_pool) {
+    if (a->num_slots < 1 || a->slot_stride < state) return SSD_ERR_BAD_SHAPE;
+  }
+  if (std::isnan(a->dt_min) || std::isnan(a->dt_max) || a->dt_min > a->dt_max)
+    return SSD_ERR_BAD_SHAPE;
+
+  const int64_t C = a->num_chunks, S = a->num_seqs;
+  if (a->a_kind == SSD_A_DIAG) {
+    if (a->P != 1 || a->G != 1) return SSD_ERR_BAD_SHAPE;
+    if (a->N != kDiagN) return SSD_ERR_UNSUPPORTED;
+    if (a->dA_cumsum_out || a->cb_out || a->chunk_local_states_out) return SSD_ERR_UNSUPPORTED;
+    plan->kind = PrefillKind::kDiag;
+    plan->ws_bytes = 0;
+    return SSD_OK;
+  }
+
+  int variant = -1;
+  for (int i = 0; i < kNumChunkedShapes; ++i) {
+    const ChunkedShape& s = kChunkedShapes[i];
+    if (s.dtype == a->in_dtype && s.P == a->P && s.N == a->N && s.CS == a->chunk_size) {
+      variant = i;
+      break;
+    }
+  }
+  if (variant < 0) return SSD_ERR_UNSUPPORTED;
+  plan->kind = PrefillKind::kChunked;
+  plan->variant = variant;
+
+  size_t off = 0;
+  plan->off_dA_last = off;
+  off = align_up(off + size_t(C) * a->H * sizeof(float), 256);
+  plan->has_init_copy = a->has_initial_state != nullptr;
+  if (plan->has_init_copy) {
+    plan->off_init = off;
+    off = align_up(off + size_t(S) * size_t(state) * sizeof(float), 256);
+  }
+  plan->states_in_ws = a->chunk_states_out == nullptr;
+  if (plan->states_in_ws) {
+    plan->off_states = off;
+    off = align_up(off + size_t(C) * size_t(state) * sizeof(float), 256);
+  }
+  plan->ws_bytes = off;
+  return SSD_OK;
+}
+
+ssd_status check_decode(const ssd_decode_args* a) {
+  if (!a) return SSD_ERR_NULL_POINTER;
+  if (a->B_pad < 0) return SSD_ERR_BAD_SHAPE;
+  if (a->ntok < 1 || a->H < 1 || a->P < 1 || a->G < 1 || a->N < 1) return SSD_ERR_BAD_SHAPE;
+  if (a->H % a->G != 0) return SSD_ERR_BAD_SHAPE;
+  if (!valid_dtype(a->in_dtype)) return SSD_ERR_BAD_SHAPE;
+  if (a->a_kind != SSD_A_SCALAR) return SSD_ERR_UNSUPPORTED;
+  if (a->ntok > kDecodeMaxTokens) return SSD_ERR_UNSUPPORTED;
+  if (!decode_supports_n(a->N) || int64_t(a->P) * a->N > kDecodeMaxStateElems)
+    return SSD_ERR_UNSUPPORTED;
+  if (std::isnan(a->dt_min) || std::isnan(a->dt_max) || a->dt_min > a->dt_max)
+    return SSD_ERR_BAD_SHAPE;
+  if (a->B_pad == 0) return SSD_OK;
+  if (!a->x || !a->dt || !a->B || !a->C || !a->y || !a->A || !a->state_pool ||
+      !a->state_indices)
+    return SSD_ERR_NULL_POINTER;
+  if (a->num_slots < 1 || a->slot_stride < int64_t(a->H) * a->P * a->N)
+    return SSD_ERR_BAD_SHAPE;
+  return SSD_OK;
+}
+
+}  // namespace ssd
+
+// ----------------------------------------------------------------------------------------
+// C ABI: library information and the chunk-metadata builder
+// ----------------------------------------------------------------------------------------
+extern "C" {
+
+int ssd_abi_version(void) { return SSD_ABI_VERSION; }
+
+const char* ssd_status_string(ssd_status s) {
+  switch (s) {
+    case SSD_OK: return "ok";
+    case SSD_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case SSD_ERR_BAD_SHAPE: return "a size or stride is out of range or inconsistent";
+    case SSD_ERR_BAD_METADATA: return "inconsistent sequence metadata";
+    case SSD_ERR_UNSUPPORTED: return "shape or dtype not instantiated";
+    case SSD_ERR_CAPACITY: return "output capacity too small";
+    case SSD_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case SSD_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+// Walks the sequences once; when `emit` is false only counts.  The first chunk of a
+// resumed sequence closes the open chunk (cs - nc % cs tokens at most); after it every
+// chunk holds min(cs, remaining) tokens.
+static ssd_status chunk_walk(int32_t S, const int32_t* cu, const int32_t* nc, int32_t cs,
+                             int32_t capacity, bool emit, int32_t* cu_chunk,
+                             int32_t* seq_idx, int32_t* last, int32_t* count_out) {
+  if (!count_out || (S > 0 && !cu)) return SSD_ERR_NULL_POINTER;
+  if (S < 0 || cs <= 0) return SSD_ERR_BAD_SHAPE;
+  if (cu && cu[0] != 0) return SSD_ERR_BAD_METADATA;
+  int64_t count = 0;
+  for (int32_t r = 0; r < S; ++r) {
+    const int64_t new_tokens = int64_t(cu[r + 1]) - cu[r];
+    const int64_t done = nc ? nc[r] : 0;
+    if (new_tokens < 1 || done < 0) return SSD_ERR_BAD_METADATA;
+    int64_t left = new_tokens;
+    if (done % cs != 0) {
+      const int64_t open = cs - done % cs;
+      left -= (open < left ? open : left);
+      ++count;
+    }
+    count += (left + cs - 1) / cs;
+    if (count > std::numeric_limits<int32_t>::max()) return SSD_ERR_BAD_METADATA;
+  }
+  *count_out = int32_t(count);
+  if (!emit) return SSD_OK;
+  if (!cu_chunk || !seq_idx || (S > 0 && !last)) return SSD_ERR_NULL_POINTER;
+  if (count > capacity) return SSD_ERR_CAPACITY;
+
+  int32_t k = 0;
+  cu_chunk[0] = 0;
+  for (int32_t r = 0; r < S; ++r) {
+    int64_t pos = cu[r];
+    const int64_t end = cu[r + 1];
+    const int64_t done = nc ? nc[r] : 0;
+    if (done % cs != 0) {
+      const int64_t open = cs - done % cs;
+      pos += (open < end - pos ? open : end - pos);
+      cu_chunk[k + 1] = int32_t(pos);
+      seq_idx[k] = r;
+      ++k;
+    }
+    while (pos < end) {
+      pos += (cs < end - pos ? cs : end - pos);
+      cu_chunk[k + 1] = int32_t(pos);
+      seq_idx[k] = r;
+      ++k;
+    }
+    last[r] = k - 1;
+  }
+  return SSD_OK;
+}
+
+ssd_status ssd_chunk_metadata_count(int32_t num_seqs, const int32_t* cu_seqlens,
+                                    const int32_t* num_computed, int32_t chunk_size,
+                                    int32_t* num_chunks_out) {
+  return chunk_walk(num_seqs, cu_seqlens, num_computed, chunk_size, 0, false, nullptr,
+                    nullptr, nullptr, num_chunks_out);
+}
+
+ssd_status ssd_build_chunk_metadata(int32_t num_seqs, const int32_t* cu_seqlens,
+                                    const int32_t* num_computed, int32_t chunk_size,
+                                    int32_t capacity, int32_t* cu_chunk_seqlens,
+                                    int32_t* seq_idx, int32_t* last_chunk_indices,
+                                    int32_t* num_chunks_out) {
+  return chunk_walk(num_seqs, cu_seqlens, num_computed, chunk_size, capacity, true,
+                    cu_chunk_seqlens, seq_idx, last_chunk_indices, num_chunks_out);
+}
+
+}  // extern "C"

@@ -1,0 +1,76 @@
+// ssd_params.h -- kernel parameter blocks and launcher declarations.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ssd.h"
+#include "ssd_device.h"
+#include "ssd_plan.h"
+
+namespace ssd {
+
+// Everything the prefill kernels read, resolved from ssd_prefill_args and the plan.
+struct PrefillParams {
+  int T, H, P, G, N, S, C, cs;
+  const void* x;  int64_t x_st;
+  const void* dt; int64_t dt_st;
+  const void* B;
+  const void* Cm; int64_t bc_st;
+  void* y;        int64_t y_st;
+  const float* A;
+  const float* D;
+  DtPrep prep;
+  const int* cu_seqlens;
+  const int* cu_chunk;
+  const int* seq_idx;
+  const int* last_chunk;
+  float* pool; int64_t slot_stride; int num_slots;
+  const int* state_idx;
+  const int* has_init;
+  int write_final;
+  float* states;       // [C, H, P, N]: chunk_states_out or workspace
+  float* dA_last;      // [C, H] workspace
+  float* init_copy;    // [S, H, P, N] workspace (NULL when no initial states)
+  int* flag;
+  float* dA_cumsum_out;
+  float* cb_out;
+  float* local_states_out;
+};
+
+struct DecodeParams {
+  int B_pad, ntok, H, P, G, N;
+  const void* x;
+  const void* dt;
+  const void* B;
+  const void* Cm;
+  void* y;
+  const float* A;
+  const float* D;
+  DtPrep prep;
+  float* pool; int64_t slot_stride; int num_slots;
+  const int* idx;
+  const int* num_acc;
+  int null_id;
+  int* flag;
+};
+
+// `events` (may be NULL): hipEvent_t handles recorded before each launch and after the
+// last one (the timing hook of the C ABI).
+hipError_t launch_chunked_prefill(int variant, const PrefillParams& p, hipStream_t s,
+                                  void* const* events);
+hipError_t launch_diag_prefill(int in_dtype, const PrefillParams& p, hipStream_t s,
+                               void* const* events);
+hipError_t launch_state_update(int in_dtype, const DecodeParams& p, hipStream_t s,
+                               void* const* events);
+
+inline void record_event(void* const* events, int i, hipStream_t s) {
+  if (events && events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
+}
+
+// Dynamic LDS of the decode kernel for these sizes (host checks it against the limit).
+inline size_t decode_lds_bytes(int ntok, int P, int N) {
+  return size_t(ntok) * (2 * P + 2 * N + 1) * sizeof(float);
+}
+
+}  // namespace ssd

@@ -1,0 +1,51 @@
+// ssd_plan.h -- host-side planning shared by the C-ABI entry points and the launchers.
+// Plain C++ (no HIP headers): validation, instantiation lookup and workspace layout.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "ssd.h"
+
+namespace ssd {
+
+// Which prefill implementation runs.
+enum class PrefillKind { kNone = 0, kChunked = 1, kDiag = 2 };
+
+// Workspace carve-up of one prefill call (byte offsets into the caller's workspace).
+struct PrefillPlan {
+  PrefillKind kind = PrefillKind::kNone;
+  int variant = -1;          // index into the chunked-kernel instantiation table
+  size_t ws_bytes = 0;
+  size_t off_dA_last = 0;    // fp32 [C, H]   within-chunk total of delta*A
+  size_t off_init = 0;       // fp32 [S, H, P, N] copy of the gathered initial states
+  size_t off_states = 0;     // fp32 [C, H, P, N] chunk states when chunk_states_out is NULL
+  bool has_init_copy = false;
+  bool states_in_ws = false;
+};
+
+// One instantiated chunked-prefill shape.
+struct ChunkedShape {
+  int dtype;   // ssd_dtype
+  int P, N, CS;
+};
+
+// The table of chunked instantiations (defined next to the kernels' dispatch table, but
+// the shapes are plain data so the host can validate without a device).
+extern const ChunkedShape kChunkedShapes[];
+extern const int kNumChunkedShapes;
+
+// Decode: supported dstates (template instantiations of the update kernel) and limits.
+constexpr int kDecodeMaxTokens = 16;
+constexpr int kDecodeMaxStateElems = 16384;   // P * N per head
+bool decode_supports_n(int N);
+
+// Diagonal (Mamba1) scan: the one instantiated dstate.
+constexpr int kDiagN = 16;
+
+ssd_status plan_prefill(const ssd_prefill_args* a, PrefillPlan* plan);
+ssd_status check_decode(const ssd_decode_args* a);
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+}  // namespace ssd

@@ -1,0 +1,205 @@
+"""The C ABI on the CPU: every declared symbol is exported, the ctypes mirror matches the
+header's struct layout, and every host-side check returns its status before any launch
+(the fake device pointers used here are never dereferenced)."""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+from selective_state_space_mamba2_amd import _abi
+from selective_state_space_mamba2_amd._abi import DecodeArgs, PrefillArgs, lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssd.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssd_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported():
+    names = _declared_functions()
+    assert set(names) == set(_abi.EXPORTS), names
+    out = subprocess.run(["nm", "-D", "--defined-only", _abi.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    for n in names:
+        assert n in exported, n
+        getattr(lib(), n)
+
+
+def test_abi_version_and_status_strings():
+    assert lib().ssd_abi_version() == 1
+    for s in range(8):
+        assert lib().ssd_status_string(s)
+    assert lib().ssd_status_string(99) == b"unknown status"
+
+
+def _c_layout(struct_name, fields):
+    src = ['#include <stdio.h>', '#include <stddef.h>', '#include "ssd.h"', 'int main(void){',
+           f'printf("%zu\\n", sizeof({struct_name}));']
+    for f in fields:
+        src.append(f'printf("%zu\\n", offsetof({struct_name}, {f}));')
+    src.append("return 0;}")
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "l.c")
+        open(c, "w").write("\n".join(src))
+        exe = os.path.join(d, "l")
+        subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), c, "-o", exe], check=True)
+        return [int(v) for v in subprocess.run([exe], capture_output=True, text=True,
+                                               check=True).stdout.split()]
+
+
+@pytest.mark.parametrize("struct,cls", [("ssd_prefill_args", PrefillArgs),
+                                        ("ssd_decode_args", DecodeArgs)])
+def test_struct_layout_matches_header(struct, cls):
+    names = [f[0] for f in cls._fields_]
+    got = _c_layout(struct, names)
+    assert got[0] == ctypes.sizeof(cls)
+    for name, off in zip(names, got[1:]):
+        assert getattr(cls, name).offset == off, name
+
+
+# ----------------------------------------------------------------------------------------
+# host-side validation (no launch happens for any of these)
+# ----------------------------------------------------------------------------------------
+FAKE = 0x10000   # a 256-byte aligned non-null "device" address; never dereferenced
+
+
+def _good_prefill(**over):
+    a = PrefillArgs()
+    a.T, a.H, a.P, a.G, a.N, a.chunk_size = 512, 8, 64, 2, 128, 256
+    a.num_seqs, a.num_chunks = 2, 3
+    a.in_dtype, a.a_kind = _abi.SSD_BF16, _abi.SSD_A_SCALAR
+    a.x = a.dt = a.B = a.C = a.y = a.A = FAKE
+    a.x_stride_t = a.y_stride_t = 8 * 64
+    a.dt_stride_t = 8
+    a.bc_stride_t = 2 * 128
+    a.cu_seqlens = a.cu_chunk_seqlens = a.seq_idx = a.last_chunk_indices = FAKE
+    a.dt_min, a.dt_max = 0.0, float("inf")
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+def _ws(a):
+    n = ctypes.c_size_t(0)
+    return lib().ssd_prefill_workspace_size(ctypes.byref(a), ctypes.byref(n)), n.value
+
+
+def test_workspace_size_layout():
+    st, n = _ws(_good_prefill())
+    # dA_last [C,H] fp32 then chunk states [C,H,P,N] fp32 (no chunk_states_out), 256-aligned
+    assert st == 0 and n == 256 + 3 * 8 * 64 * 128 * 4
+    st, n = _ws(_good_prefill(chunk_states_out=FAKE))
+    assert st == 0 and n == 256
+    st, n = _ws(_good_prefill(chunk_states_out=FAKE, has_initial_state=FAKE, state_pool=FAKE,
+                              state_indices=FAKE, num_slots=4, slot_stride=8 * 64 * 128))
+    assert st == 0 and n == 256 + 2 * 8 * 64 * 128 * 4
+    st, n = _ws(_good_prefill(a_kind=_abi.SSD_A_DIAG, H=64, P=1, G=1, N=16, x_stride_t=64,
+                              y_stride_t=64, dt_stride_t=64, bc_stride_t=16))
+    assert st == 0 and n == 0
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(H=6, G=4), _abi.SSD_ERR_BAD_SHAPE),             # H % G != 0
+    (dict(P=0), _abi.SSD_ERR_BAD_SHAPE),
+    (dict(chunk_size=0), _abi.SSD_ERR_BAD_SHAPE),
+    (dict(in_dtype=7), _abi.SSD_ERR_BAD_SHAPE),
+    (dict(a_kind=5), _abi.SSD_ERR_BAD_SHAPE),
+    (dict(num_chunks=1), _abi.SSD_ERR_BAD_SHAPE),         # fewer chunks than sequences
+    (dict(num_chunks=600), _abi.SSD_ERR_BAD_SHAPE),       # more chunks than tokens
+    (dict(T=1), _abi.SSD_ERR_BAD_SHAPE),                  # fewer tokens than sequences
+    (dict(x_stride_t=100), _abi.SSD_ERR_BAD_SHAPE),
+    (dict(dt_stride_t=4), _abi.SSD_ERR_BAD_SHAPE),
+    (dict(bc_stride_t=128), _abi.SSD_ERR_BAD_SHAPE),
+    (dict(dt_min=1.0, dt_max=0.5), _abi.SSD_ERR_BAD_SHAPE),
+    (dict(dt_min=float("nan")), _abi.SSD_ERR_BAD_SHAPE),
+    (dict(x=None), _abi.SSD_ERR_NULL_POINTER),
+    (dict(A=None), _abi.SSD_ERR_NULL_POINTER),
+    (dict(seq_idx=None), _abi.SSD_ERR_NULL_POINTER),
+    (dict(has_initial_state=FAKE), _abi.SSD_ERR_NULL_POINTER),   # no pool given
+    (dict(write_final_to_pool=1, state_pool=FAKE), _abi.SSD_ERR_NULL_POINTER),  # no indices
+    (dict(state_pool=FAKE, state_indices=FAKE, num_slots=0), _abi.SSD_ERR_BAD_SHAPE),
+    (dict(state_pool=FAKE, state_indices=FAKE, num_slots=2, slot_stride=10),
+     _abi.SSD_ERR_BAD_SHAPE),
+    (dict(P=32), _abi.SSD_ERR_UNSUPPORTED),                # not instantiated
+    (dict(chunk_size=100), _abi.SSD_ERR_UNSUPPORTED),
+    (dict(in_dtype=_abi.SSD_F32), _abi.SSD_ERR_UNSUPPORTED),   # fp32 at cs=256
+    (dict(a_kind=_abi.SSD_A_DIAG), _abi.SSD_ERR_BAD_SHAPE),    # diag needs P == 1
+])
+def test_prefill_host_checks(over, status):
+    a = _good_prefill(**over)
+    assert _ws(a)[0] == status
+    assert lib().ssd_prefill(ctypes.byref(a), FAKE, 1 << 40, None) == status
+
+
+def test_prefill_workspace_checks():
+    a = _good_prefill()
+    need = _ws(a)[1]
+    assert lib().ssd_prefill(ctypes.byref(a), None, need, None) == _abi.SSD_ERR_WORKSPACE
+    assert lib().ssd_prefill(ctypes.byref(a), FAKE, need - 1, None) == _abi.SSD_ERR_WORKSPACE
+    assert lib().ssd_prefill(ctypes.byref(a), FAKE + 8, need, None) == _abi.SSD_ERR_WORKSPACE
+
+
+def test_prefill_vector_access_checks():
+    a = _good_prefill(x=FAKE + 2)            # x not 16-byte aligned
+    assert lib().ssd_prefill(ctypes.byref(a), FAKE, 1 << 40, None) == _abi.SSD_ERR_UNSUPPORTED
+    a = _good_prefill(x_stride_t=8 * 64 + 3)  # row stride breaks 16-byte alignment
+    assert lib().ssd_prefill(ctypes.byref(a), FAKE, 1 << 40, None) == _abi.SSD_ERR_UNSUPPORTED
+
+
+def test_prefill_empty_batch_is_a_noop():
+    a = _good_prefill(T=0, num_seqs=0, num_chunks=0)
+    assert _ws(a) == (0, 0)
+    assert lib().ssd_prefill(ctypes.byref(a), None, 0, None) == 0
+    assert lib().ssd_prefill(None, None, 0, None) == _abi.SSD_ERR_NULL_POINTER
+
+
+def test_diag_host_checks():
+    base = dict(a_kind=_abi.SSD_A_DIAG, H=64, P=1, G=1, N=16, x_stride_t=64, y_stride_t=64,
+                dt_stride_t=64, bc_stride_t=16)
+    assert _ws(_good_prefill(**base))[0] == 0
+    assert _ws(_good_prefill(**{**base, "N": 32, "bc_stride_t": 32}))[0] == _abi.SSD_ERR_UNSUPPORTED
+    assert _ws(_good_prefill(**base, dA_cumsum_out=FAKE))[0] == _abi.SSD_ERR_UNSUPPORTED
+
+
+def _good_decode(**over):
+    a = DecodeArgs()
+    a.B_pad, a.ntok, a.H, a.P, a.G, a.N = 8, 4, 48, 64, 4, 128
+    a.in_dtype, a.a_kind = _abi.SSD_BF16, _abi.SSD_A_SCALAR
+    a.x = a.dt = a.B = a.C = a.y = a.A = a.state_pool = a.state_indices = FAKE
+    a.slot_stride, a.num_slots = 48 * 64 * 128, 16
+    a.dt_min, a.dt_max = 0.0, float("inf")
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(ntok=0), _abi.SSD_ERR_BAD_SHAPE),
+    (dict(ntok=17), _abi.SSD_ERR_UNSUPPORTED),
+    (dict(H=47), _abi.SSD_ERR_BAD_SHAPE),
+    (dict(N=48), _abi.SSD_ERR_UNSUPPORTED),
+    (dict(P=256), _abi.SSD_ERR_UNSUPPORTED),               # P*N above the per-head limit
+    (dict(a_kind=_abi.SSD_A_DIAG), _abi.SSD_ERR_UNSUPPORTED),
+    (dict(in_dtype=3), _abi.SSD_ERR_BAD_SHAPE),
+    (dict(state_pool=None), _abi.SSD_ERR_NULL_POINTER),
+    (dict(state_indices=None), _abi.SSD_ERR_NULL_POINTER),
+    (dict(slot_stride=100), _abi.SSD_ERR_BAD_SHAPE),
+    (dict(num_slots=0), _abi.SSD_ERR_BAD_SHAPE),
+    (dict(dt_min=2.0, dt_max=1.0), _abi.SSD_ERR_BAD_SHAPE),
+    (dict(state_pool=FAKE + 4), _abi.SSD_ERR_UNSUPPORTED),
+])
+def test_decode_host_checks(over, status):
+    a = _good_decode(**over)
+    assert lib().ssd_state_update(ctypes.byref(a), None) == status
+
+
+def test_decode_empty_batch_is_a_noop():
+    assert lib().ssd_state_update(ctypes.byref(_good_decode(B_pad=0, x=None)), None) == 0

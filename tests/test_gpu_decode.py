@@ -1,0 +1,131 @@
+"""GPU parity of the padded speculative decode update against the fp64 oracle.
+
+Checks per call: y of every live row (or a sample at full size), every written slot, NULL
+padding rows left bit-identical (y sentinel untouched), and every slot no live row writes
+left bit-identical."""
+import math
+
+import numpy as np
+import pytest
+
+from gpu_helpers import TOL, assert_close, host64, oracle_decode, run_decode
+from selective_state_space_mamba2_amd.inputs import make_decode, workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(inp, got, rows=None, tol=None, **okw):
+    tol = TOL[inp.in_dtype] if tol is None else tol
+    y_ref, writes = oracle_decode(inp, rows=rows, **okw)
+    y = host64(got["y"])
+    live = np.flatnonzero(inp.state_indices[:, 0] != inp.null_block_id)
+    for r, yr in y_ref.items():
+        assert_close(y[r], yr, tol, f"y row {r}")
+    for slot, st in writes.items():
+        assert_close(got["pool"][slot], st, tol, f"slot {slot}")
+    # padding rows: y untouched (sentinel 7.0 exactly)
+    pad = np.flatnonzero(inp.state_indices[:, 0] == inp.null_block_id)
+    assert np.all(y[pad] == 7.0)
+    # slots no live row writes: bit-identical
+    written = set(int(v) for v in inp.state_indices[live].ravel())
+    untouched = np.array([s for s in range(inp.pool.shape[0]) if s not in written])
+    np.testing.assert_array_equal(got["pool"][untouched], inp.pool[untouched])
+    return y_ref, writes
+
+
+@pytest.mark.parametrize("dtype,P,N,G,ntok", [("bf16", 64, 128, 2, 4), ("bf16", 16, 16, 1, 1),
+                                              ("f32", 64, 128, 4, 3), ("f32", 32, 64, 1, 2),
+                                              ("bf16", 64, 256, 1, 2)])
+def test_small_batches(dtype, P, N, G, ntok):
+    inp = make_decode(20 + P + N + ntok, in_dtype=dtype, B_pad=12, n_live=7, ntok=ntok, H=8,
+                      P=P, G=G, N=N, pool_slots=64)
+    got = run_decode(inp)
+    assert got["flag"] == 0
+    _check(inp, got)
+
+
+def test_every_restore_column():
+    """num_accepted 1..ntok on consecutive rows: each restores from its own column."""
+    inp = make_decode(30, in_dtype="bf16", B_pad=8, n_live=8, ntok=4, H=4, P=64, G=1, N=128,
+                      pool_slots=40)
+    inp.num_accepted[:] = [1, 2, 3, 4, 4, 3, 2, 1]
+    got = run_decode(inp)
+    _check(inp, got)
+
+
+def test_without_num_accepted_and_negative_null_id():
+    inp = make_decode(31, in_dtype="bf16", B_pad=10, n_live=6, ntok=1, H=8, P=64, G=2, N=128,
+                      pool_slots=20, null_block_id=-1)
+    got = run_decode(inp, use_acc=False)
+    _check(inp, got, use_acc=False)
+
+
+def test_softplus_bias_limit():
+    inp = make_decode(32, in_dtype="f32", B_pad=6, n_live=4, ntok=2, H=8, P=64, G=2, N=128,
+                      pool_slots=16)
+    bias = np.random.default_rng(3).normal(-1, 0.5, 8).astype(np.float32).astype(np.float64)
+    got = run_decode(inp, dt_bias=bias, softplus=True, dt_limit=(0.02, 0.3))
+    _check(inp, got, dt_bias=bias, softplus=True, dt_limit=(0.02, 0.3))
+
+
+def test_bad_num_accepted_skips_the_row_and_raises_the_flag():
+    inp = make_decode(33, in_dtype="bf16", B_pad=4, n_live=4, ntok=2, H=4, P=64, G=1, N=128,
+                      pool_slots=16)
+    acc = inp.num_accepted.copy()
+    acc[2] = 3                                          # > ntok
+    got = run_decode(inp, num_accepted=acc)
+    assert got["flag"] & 4
+    y = host64(got["y"])
+    assert np.all(y[2] == 7.0)
+    for s in inp.state_indices[2]:
+        np.testing.assert_array_equal(got["pool"][s], inp.pool[s])
+    y_ref, _ = oracle_decode(inp, rows=[0, 1, 3], num_accepted=acc)
+    for r, yr in y_ref.items():
+        assert_close(y[r], yr, TOL["bf16"], f"y row {r}")
+
+
+def test_full_decode_spec_workload():
+    inp = workload("decode_spec")
+    got = run_decode(inp)
+    assert got["flag"] == 0
+    rows = [0, 1, 77, 128, 200, 254, 255]
+    _check(inp, got, rows=rows)
+    assert np.isfinite(host64(got["y"])[:inp.n_live]).all()
+
+
+def test_graph_capture_and_replay():
+    """The decode launch captured in a HIP graph, replayed several times with eager work in
+    between, matches the eager call on every replay."""
+    import torch
+    from gpu_helpers import dev_f32, dev_i32, dev_token
+    from selective_state_space_mamba2_amd import api
+    inp = make_decode(34, in_dtype="bf16", B_pad=16, n_live=9, ntok=4, H=8, P=64, G=2, N=128,
+                      pool_slots=64)
+    x, dt, B, C = (dev_token(inp, n) for n in ("x", "dt", "B", "C"))
+    A, D = dev_f32(inp.A), dev_f32(inp.D)
+    idx, acc = dev_i32(inp.state_indices), dev_i32(inp.num_accepted)
+    pool0 = torch.from_numpy(inp.pool).cuda()
+    pool = pool0.clone()
+    y = torch.zeros_like(x)
+    api.ssd_state_update(x, dt, A, B, C, pool, idx, y=y, num_accepted_tokens=acc, D=D)
+    torch.cuda.synchronize()
+    y_eager, pool_eager = y.clone(), pool.clone()
+    pool.copy_(pool0)
+    y.zero_()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            api.ssd_state_update(x, dt, A, B, C, pool, idx, y=y, num_accepted_tokens=acc, D=D,
+                                 stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    for _ in range(3):
+        pool.copy_(pool0)
+        y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager)
+        assert torch.equal(pool, pool_eager)
+        _ = (x.float() * 2).sum().item()   # unrelated eager work between replays

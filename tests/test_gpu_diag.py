@@ -1,0 +1,43 @@
+"""GPU parity of the Mamba1-style diagonal selective scan (A[channel, state], P = 1)."""
+import numpy as np
+import pytest
+
+from gpu_helpers import TOL, assert_close, check_prefill, oracle_prefill, run_prefill
+from selective_state_space_mamba2_amd.inputs import make_prefill, workload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_small_diag_with_pool_and_checkpoints(dtype):
+    """200 channels (a ragged last block of 64), three sequences with unaligned resume
+    points, two of them starting from pool states."""
+    inp = make_prefill(40, in_dtype=dtype, H=200, P=1, G=1, N=16, chunk_size=128,
+                       lengths=[300, 77, 1000], num_computed=[0, 5, 130], a_kind="diag",
+                       init="pool", pool_slots=8)
+    inp.has_initial_state[1] = 0
+    got = run_prefill(inp)
+    assert got["flag"] == 0
+    check_prefill(inp, got, oracle_prefill(inp))
+    owned = set(int(v) for v in inp.state_indices)
+    for s in range(8):
+        if s not in owned:
+            np.testing.assert_array_equal(got["pool"][s], inp.pool[s])
+
+
+def test_diag_softplus_and_long_memory():
+    inp = make_prefill(41, in_dtype="f32", H=64, P=1, G=1, N=16, chunk_size=64,
+                       lengths=[500], a_kind="diag", A_range=(1e-3, 1e-2))
+    bias = np.random.default_rng(1).normal(-1, 0.3, 64).astype(np.float32).astype(np.float64)
+    got = run_prefill(inp, dt_bias=bias, softplus=True, dt_limit=(0.0, 0.5))
+    check_prefill(inp, got, oracle_prefill(inp, dt_bias=bias, softplus=True,
+                                           dt_limit=(0.0, 0.5)))
+
+
+def test_full_mamba1_long_diag():
+    inp = workload("mamba1_long_diag")
+    got = run_prefill(inp)
+    assert got["flag"] == 0 and np.isfinite(got["y"]).all()
+    assert len(got["metadata"][1]) == 64
+    chans = [0, 2501, 5119]
+    check_prefill(inp, got, oracle_prefill(inp, seqs=[3], heads=chans), heads=chans)
