@@ -1,0 +1,457 @@
+#!/usr/bin/env python
+"""Benchmark of the MI355X SSD scan path (one GPU).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--primary-only]
+
+One step is one pass of the prefill path over the Mamba2-2.7B-like layer batch (4 packed
+sequences x 2048 tokens, 80 heads, head_dim 64, dstate 128, chunk 256, bf16 in / fp32
+state, the state written at every chunk end): chunk metadata on the host, its copy to the
+device, and the three prefill kernels.  Inputs are resident in HBM before timing starts;
+four input/output buffer sets rotate so the 256 MB Infinity Cache cannot hold a step's
+working set.  The line printed also carries the decode state update (256 live requests of
+a 512-row padded batch, 1+3 tokens, [2048,48,64,128] fp32 pool), the Nemotron-H-like
+varlen prefill with prefix caching and the Mamba1 long-context diagonal scan as secondary
+objects.
+
+Roofline: each kernel's duration comes from HIP events the library records around its
+own launches on the launch stream (the C ABI's timing hook), averaged over the timed
+steps; achieved = the kernel's algorithmic bytes (or flops) per launch / that duration.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA, TFLOP/s
+# Vector-ALU peak: 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz = 39.3 T lane-ops/s; an FMA counts
+# 2 flops (78.6 TFLOP/s); the 157.3 TFLOP/s headline needs packed FP32, which this build
+# does not emit.
+VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9
+METRIC = "SSD prefill tokens/s (% MFMA peak) + decode state-updates/s (% HBM GB/s)"
+
+
+def _log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------------------
+# algorithmic work (bytes and flops a kernel must move / do; redundant work not counted)
+# ----------------------------------------------------------------------------------------
+def prefill_work(inp, cuc, sidx):
+    b = 2 if inp.in_dtype == "bf16" else 4
+    T, H, P, G, N = inp.T, inp.H, inp.P, inp.G, inp.N
+    S, C = inp.num_seqs, len(sidx)
+    st = H * P * N * 4
+    n_init = 0 if inp.has_initial_state is None else int(inp.has_initial_state.sum())
+    n_final = 0 if inp.pool is None else S
+    lens = [int(cuc[k + 1] - cuc[k]) for k in range(C)]
+    tok_in = T * (H * P * b + H * b + G * N * b)          # x, dt, B
+    k_state = dict(bytes=tok_in + C * st + C * H * 4,
+                   flops=sum(2 * l * P * N * H for l in lens))
+    k_pass = dict(bytes=2 * C * st + (n_init + n_final) * st + C * H * 4, flops=0)
+    k_scan = dict(bytes=T * (2 * H * P * b + H * b + 2 * G * N * b) + (C - S + n_init) * st,
+                  flops=sum(H * (2 * l * N * P + P * l * (l + 1)) + G * N * l * (l + 1)
+                            for l in lens))
+    path = dict(bytes=T * (2 * H * P * b + H * b + 2 * G * N * b) + (n_init + C + n_final) * st,
+                flops=sum(H * (4 * l * P * N + P * l * (l + 1)) + G * N * l * (l + 1)
+                          for l in lens))
+    return {"k_chunk_state": k_state, "k_state_passing": k_pass, "k_chunk_scan": k_scan,
+            "path": path}
+
+
+def decode_work(inp):
+    b = 2 if inp.in_dtype == "bf16" else 4
+    st = inp.H * inp.P * inp.N * 4
+    tok = inp.ntok * (2 * inp.H * inp.P * b + inp.H * b + 2 * inp.G * inp.N * b)
+    return dict(bytes=inp.n_live * ((1 + inp.ntok) * st + tok), updates=inp.n_live * inp.ntok)
+
+
+def diag_work(inp, C):
+    b = 2 if inp.in_dtype == "bf16" else 4
+    T, H, N = inp.T, inp.H, inp.N
+    return dict(bytes=T * (3 * H * b + 2 * N * b) + C * H * N * 4, steps=T * H * N)
+
+
+# ----------------------------------------------------------------------------------------
+# device plumbing
+# ----------------------------------------------------------------------------------------
+def _dev_token(torch, inp, name):
+    import numpy as np
+    a = getattr(inp, name)
+    if inp.in_dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.asarray(a, dtype=np.float32)).cuda()
+
+
+def _events(torch, n):
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for e in evs:
+        e.record()          # materialise the underlying hipEvent_t
+    return evs
+
+
+def _handles(evs):
+    import ctypes
+    arr = (ctypes.c_void_p * len(evs))(*[e.cuda_event for e in evs])
+    return arr
+
+
+def _kernel_times(evs_per_step, n_kernels):
+    tot = [0.0] * n_kernels
+    for evs in evs_per_step:
+        for i in range(n_kernels):
+            tot[i] += evs[i].elapsed_time(evs[i + 1])
+    return [t / len(evs_per_step) for t in tot]     # ms per launch
+
+
+def _source_digest(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "selective_state_space_mamba2_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _counter_traffic(kernel, workload, digest):
+    """HBM bytes per launch measured with rocprofv3 PMC counters (FETCH_SIZE + WRITE_SIZE,
+    scaled by a copy-kernel calibration), as recorded under profiles/.  None when no record
+    exists or the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(f"{kernel}@{workload}")
+    except (ValueError, OSError):
+        return None
+    if not rec or rec.get("source_digest") != digest:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def _roofline(bound, achieved, peak, unit, traffic=None, kernel=None):
+    r = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+         "frac": round(achieved / peak, 4), "traffic": traffic}
+    if kernel:
+        r["kernel"] = kernel
+    return r
+
+
+# ----------------------------------------------------------------------------------------
+# prefill (scalar A)
+# ----------------------------------------------------------------------------------------
+def bench_prefill(torch, name, steps, warmup, sets=4):
+    import numpy as np
+    from selective_state_space_mamba2_amd import api
+    from selective_state_space_mamba2_amd._abi import SSD_PREFILL_MAX_KERNELS, check, lib
+    from selective_state_space_mamba2_amd.inputs import workload
+    import ctypes
+
+    inp = workload(name)
+    cu_np = np.ascontiguousarray(inp.cu_seqlens, dtype=np.int32)
+    nc_np = np.ascontiguousarray(inp.num_computed, dtype=np.int32)
+    cuc, sidx, last = api.ssd_build_chunk_metadata(cu_np, nc_np, inp.chunk_size)
+    C = len(sidx)
+    S = inp.num_seqs
+    A = torch.tensor(inp.A, dtype=torch.float32).cuda()
+    D = torch.tensor(inp.D, dtype=torch.float32).cuda()
+    pool = torch.from_numpy(inp.pool).cuda() if inp.pool is not None else None
+    sidx_d = None if inp.state_indices is None else torch.from_numpy(inp.state_indices).cuda()
+    hinit_d = (None if inp.has_initial_state is None
+               else torch.from_numpy(inp.has_initial_state).cuda())
+    base = {n: _dev_token(torch, inp, n) for n in ("x", "dt", "B", "C")}
+    bufs = []
+    for i in range(sets):
+        d = {n: (t if i == 0 else t.clone()) for n, t in base.items()}
+        d["y"] = torch.empty_like(d["x"])
+        d["states"] = torch.empty(C, inp.H, inp.P, inp.N, dtype=torch.float32, device="cuda")
+        d["cu_seq"] = torch.empty(S + 1, dtype=torch.int32, device="cuda")
+        d["cu_chunk"] = torch.empty(C + 1, dtype=torch.int32, device="cuda")
+        d["seq_idx"] = torch.empty(C, dtype=torch.int32, device="cuda")
+        d["last"] = torch.empty(S, dtype=torch.int32, device="cuda")
+        d["host"] = torch.empty(S + 1 + C + 1 + C + S, dtype=torch.int32).pin_memory()
+        bufs.append(d)
+    args = [api.prefill_args(d["x"], d["dt"], A, d["B"], d["C"], inp.chunk_size, d["cu_seq"],
+                             d["cu_chunk"], d["seq_idx"], d["last"], d["y"], D=D,
+                             state_pool=pool, state_indices=sidx_d,
+                             has_initial_state=hinit_d, write_final_to_pool=pool is not None,
+                             chunk_states_out=d["states"]) for d in bufs]
+    ws_bytes = api.ssd_prefill_workspace_size(args[0])
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+    nk = ctypes.c_int32(0)
+    names = (ctypes.c_char_p * SSD_PREFILL_MAX_KERNELS)()
+    check("ssd_prefill_kernel_count", lib().ssd_prefill_kernel_count(ctypes.byref(args[0]),
+                                                                     ctypes.byref(nk), names))
+    knames = [names[i].decode() for i in range(nk.value)]
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def step(i, evs=None):
+        d, a = bufs[i % sets], args[i % sets]
+        # a0: chunk metadata on the host, then an asynchronous copy to the device
+        c2, s2, l2 = api.ssd_build_chunk_metadata(cu_np, nc_np, inp.chunk_size)
+        h = d["host"].numpy()
+        h[:S + 1], h[S + 1:S + C + 2] = cu_np, c2
+        h[S + C + 2:S + 2 * C + 2], h[S + 2 * C + 2:] = s2, l2
+        hd = d["host"].cuda(non_blocking=True)
+        d["cu_seq"].copy_(hd[:S + 1])
+        d["cu_chunk"].copy_(hd[S + 1:S + C + 2])
+        d["seq_idx"].copy_(hd[S + C + 2:S + 2 * C + 2])
+        d["last"].copy_(hd[S + 2 * C + 2:])
+        a.profile_events = None if evs is None else ctypes.cast(evs, ctypes.c_void_p)
+        check("ssd_prefill", lib().ssd_prefill(ctypes.byref(a), ws.data_ptr(), ws.numel(), sp))
+
+    for i in range(warmup):
+        step(i)
+    ev_sets = [_events(torch, nk.value + 1) for _ in range(steps)]
+    handles = [_handles(e) for e in ev_sets]
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        step(i, handles[i])
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    kt = _kernel_times(ev_sets, nk.value)
+    work = prefill_work(inp, cuc, sidx)
+    return dict(inp=inp, C=C, total_ms=total_ms, ms_per_step=total_ms / steps,
+                kernel_ms=dict(zip(knames, kt)), work=work)
+
+
+def prefill_report(res, name, with_counters=True):
+    inp = res["inp"]
+    tok_s = inp.T / (res["ms_per_step"] * 1e-3)
+    kms = res["kernel_ms"]
+    dom = max(kms, key=kms.get)
+    w = res["work"]
+    gbs = w[dom]["bytes"] / (kms[dom] * 1e-3) / 1e9
+    digest = _source_digest("ssd_prefill.hip", "ssd_device.h")
+    traffic = _counter_traffic(dom, name, digest) if with_counters else None
+    dev_ms = sum(kms.values())
+    path_tflops = w["path"]["flops"] / (dev_ms * 1e-3) / 1e12
+    path_gbs = w["path"]["bytes"] / (dev_ms * 1e-3) / 1e9
+    return dict(
+        tokens_per_s=tok_s,
+        roofline=_roofline("hbm", gbs, HBM_PEAK_GBS, "GB/s", traffic, dom),
+        kernels={k: {"ms": round(v, 5),
+                     "gb_s": round(w[k]["bytes"] / (v * 1e-3) / 1e9, 1),
+                     "tflop_s": round(w[k]["flops"] / (v * 1e-3) / 1e12, 2),
+                     "alg_bytes": w[k]["bytes"], "alg_flops": w[k]["flops"]}
+                 for k, v in kms.items()},
+        path={"device_ms": round(dev_ms, 5), "alg_bytes": w["path"]["bytes"],
+              "alg_flops": w["path"]["flops"], "hbm_frac": round(path_gbs / HBM_PEAK_GBS, 4),
+              "mfma_frac": round(path_tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
+    )
+
+
+def cpu_baseline_prefill(inp, n_seqs=2):
+    """The fp64 oracle on the first ``n_seqs`` sequences of the workload, all heads."""
+    from oracle import scan_prefill
+    from selective_state_space_mamba2_amd.inputs import bf16_from_bits
+    t1 = int(inp.cu_seqlens[n_seqs])
+    conv = (lambda a: bf16_from_bits(a)) if inp.in_dtype == "bf16" else (lambda a: a)
+    x, dt, B, C = (conv(getattr(inp, n)[:t1]) for n in ("x", "dt", "B", "C"))
+    w0, c0 = time.perf_counter(), time.process_time()
+    scan_prefill(x, dt, inp.A, B, C, inp.D, inp.cu_seqlens[:n_seqs + 1], inp.chunk_size)
+    wall, cpu = time.perf_counter() - w0, time.process_time() - c0
+    return {"value": round(t1 / wall, 2), "unit": "tokens/s",
+            "cores": max(1, round(cpu / wall)), "kind": "oracle",
+            "sample": f"first {n_seqs} of {inp.num_seqs} sequences ({t1} tokens), all "
+                      f"{inp.H} heads, fp64 sequential recurrence with every chunk-end state; "
+                      f"{wall:.1f} s wall, host has {os.cpu_count()} logical CPUs"}
+
+
+# ----------------------------------------------------------------------------------------
+# decode
+# ----------------------------------------------------------------------------------------
+def bench_decode(torch, steps, warmup, with_cpu=True):
+    import ctypes
+    from selective_state_space_mamba2_amd import api
+    from selective_state_space_mamba2_amd._abi import check, lib
+    from selective_state_space_mamba2_amd.inputs import workload
+    inp = workload("decode_spec")
+    x, dt, B, C = (_dev_token(torch, inp, n) for n in ("x", "dt", "B", "C"))
+    y = torch.empty_like(x)
+    pool = torch.from_numpy(inp.pool).cuda()
+    idx = torch.from_numpy(inp.state_indices).cuda()
+    acc = torch.from_numpy(inp.num_accepted).cuda()
+    A = torch.tensor(inp.A, dtype=torch.float32).cuda()
+    D = torch.tensor(inp.D, dtype=torch.float32).cuda()
+    a = api.decode_args(x, dt, A, B, C, y, pool, idx, num_accepted_tokens=acc,
+                        null_block_id=inp.null_block_id, D=D)
+    sp = torch.cuda.current_stream().cuda_stream
+    for _ in range(warmup):
+        check("ssd_state_update", lib().ssd_state_update(ctypes.byref(a), sp))
+    ev_sets = [_events(torch, 2) for _ in range(steps)]
+    handles = [_handles(e) for e in ev_sets]
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        a.profile_events = ctypes.cast(handles[i], ctypes.c_void_p)
+        check("ssd_state_update", lib().ssd_state_update(ctypes.byref(a), sp))
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    kms = _kernel_times(ev_sets, 1)[0]
+    w = decode_work(inp)
+    out = {"workload": "decode_spec", "metric": "state-updates/s",
+           "value": round(w["updates"] / (ms * 1e-3), 1), "unit": "state-updates/s",
+           "ms_per_step": round(ms, 5),
+           "roofline": _roofline("hbm", w["bytes"] / (kms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s",
+                                 _counter_traffic("k_state_update", "decode_spec",
+                                                  _source_digest("ssd_decode.hip", "ssd_device.h")),
+                                 "k_state_update"),
+           "kernel_ms": round(kms, 5), "alg_bytes": w["bytes"]}
+    if with_cpu:
+        from oracle import scan_decode
+        from selective_state_space_mamba2_amd.inputs import bf16_from_bits
+        rows = list(range(32))
+        w0, c0 = time.perf_counter(), time.process_time()
+        scan_decode(inp.pool, inp.state_indices, inp.num_accepted, bf16_from_bits(inp.x),
+                    bf16_from_bits(inp.dt), inp.A, bf16_from_bits(inp.B), bf16_from_bits(inp.C),
+                    inp.D, inp.null_block_id, rows=rows)
+        wall, cpu = time.perf_counter() - w0, time.process_time() - c0
+        out["cpu_baseline"] = {"value": round(len(rows) * inp.ntok / wall, 2),
+                               "unit": "state-updates/s", "cores": max(1, round(cpu / wall)),
+                               "kind": "oracle",
+                               "sample": f"{len(rows)} live rows x {inp.ntok} tokens"}
+    del pool
+    return out
+
+
+# ----------------------------------------------------------------------------------------
+# Mamba1 diagonal scan
+# ----------------------------------------------------------------------------------------
+def bench_diag(torch, steps, warmup):
+    import ctypes
+    import numpy as np
+    from selective_state_space_mamba2_amd import api
+    from selective_state_space_mamba2_amd._abi import check, lib
+    from selective_state_space_mamba2_amd.inputs import workload
+    inp = workload("mamba1_long_diag")
+    cuc, sidx, last = api.ssd_build_chunk_metadata(inp.cu_seqlens, None, inp.chunk_size)
+    C = len(sidx)
+    x, dt, B, Cm = (_dev_token(torch, inp, n) for n in ("x", "dt", "B", "C"))
+    y = torch.empty_like(x)
+    states = torch.empty(C, inp.H, 1, inp.N, dtype=torch.float32, device="cuda")
+    A = torch.tensor(inp.A, dtype=torch.float32).cuda()
+    D = torch.tensor(inp.D, dtype=torch.float32).cuda()
+    md = [torch.from_numpy(np.asarray(v, dtype=np.int32)).cuda()
+          for v in (inp.cu_seqlens, cuc, sidx, last)]
+    a = api.prefill_args(x, dt, A, B, Cm, inp.chunk_size, *md, y, D=D, chunk_states_out=states)
+    sp = torch.cuda.current_stream().cuda_stream
+    for _ in range(warmup):
+        check("ssd_prefill", lib().ssd_prefill(ctypes.byref(a), None, 0, sp))
+    ev_sets = [_events(torch, 2) for _ in range(steps)]
+    handles = [_handles(e) for e in ev_sets]
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        a.profile_events = ctypes.cast(handles[i], ctypes.c_void_p)
+        check("ssd_prefill", lib().ssd_prefill(ctypes.byref(a), None, 0, sp))
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    kms = _kernel_times(ev_sets, 1)[0]
+    w = diag_work(inp, C)
+    # VALU lane-ops per (token, channel, state): delta*A, exp (counted as 4: the
+    # transcendental unit runs at a quarter of the FMA rate), x*B, the state FMA, the y FMA.
+    lane_ops = w["steps"] * 8
+    return {"workload": "mamba1_long_diag", "metric": "tokens/s",
+            "value": round(inp.T / (ms * 1e-3), 1), "unit": "tokens/s",
+            "ms_per_step": round(ms, 5), "kernel_ms": round(kms, 5),
+            "roofline": _roofline("alu", lane_ops / (kms * 1e-3) / 1e12,
+                                  round(VALU_LANE_OPS / 1e12, 2), "T lane-op/s", None,
+                                  "k_diag_scan"),
+            "hbm_gb_s": round(w["bytes"] / (kms * 1e-3) / 1e9, 1), "alg_bytes": w["bytes"]}
+
+
+def copy_calibration(torch, mib=1024, reps=3):
+    """A plain device copy of known size (for scaling the HBM byte counters)."""
+    a = torch.empty(mib * (1 << 20) // 4, dtype=torch.float32, device="cuda").normal_()
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    _log(f"copy calibration: {reps} copies of {mib} MiB")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--primary-only", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(torch)
+
+    name = "mamba2_2.7b_prefill"
+    _log(f"prefill {name}: {args.steps} steps after {args.warmup} warm-up")
+    res = bench_prefill(torch, name, args.steps, args.warmup)
+    rep = prefill_report(res, name)
+    inp = res["inp"]
+    line = {
+        "metric": METRIC,
+        "value": round(rep["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(res["ms_per_step"], 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": name, "num_seqs": inp.num_seqs, "seq_len": 2048,
+                   "tokens": inp.T, "nheads": inp.H, "headdim": inp.P, "ngroups": inp.G,
+                   "dstate": inp.N, "chunk_size": inp.chunk_size,
+                   "states": "every chunk end", "parallelism": "single GPU"},
+        "roofline": rep["roofline"],
+        "kernels": rep["kernels"],
+        "path": rep["path"],
+    }
+    if not args.no_cpu_baseline:
+        _log("cpu baseline (oracle)")
+        line["cpu_baseline"] = cpu_baseline_prefill(inp)
+    del res
+    if not args.primary_only:
+        _log("decode_spec")
+        line["decode"] = bench_decode(torch, args.steps, args.warmup,
+                                      with_cpu=not args.no_cpu_baseline)
+        torch.cuda.empty_cache()
+        _log("nemotron_h_prefix_cache")
+        res2 = bench_prefill(torch, "nemotron_h_prefix_cache", args.steps, args.warmup)
+        rep2 = prefill_report(res2, "nemotron_h_prefix_cache")
+        line["prefill_nemotron"] = {
+            "workload": "nemotron_h_prefix_cache", "value": round(rep2["tokens_per_s"], 1),
+            "unit": "tokens/s", "tokens": res2["inp"].T, "chunks": res2["C"],
+            "ms_per_step": round(res2["ms_per_step"], 5), "roofline": rep2["roofline"],
+            "kernels": rep2["kernels"], "path": rep2["path"]}
+        del res2
+        torch.cuda.empty_cache()
+        _log("mamba1_long_diag")
+        line["diag"] = bench_diag(torch, max(3, args.steps // 5), max(1, args.warmup // 5))
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

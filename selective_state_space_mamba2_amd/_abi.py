@@ -98,6 +98,12 @@ def lib() -> ctypes.CDLL:
             raise RuntimeError(
                 f"{LIB_PATH} is missing: build it with "
                 "`python -m selective_state_space_mamba2_amd.build`")
+        # torch ships its own HIP runtime under the same soname; loading torch first makes
+        # libssd.so bind to that one instance, so torch's streams and events are valid here.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         handle = ctypes.CDLL(LIB_PATH)
         for name, (res, argtypes) in EXPORTS.items():
             fn = getattr(handle, name)
