@@ -30,18 +30,22 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t v) {
   return __uint_as_float(uint32_t(v) << 16);
 }
 
-// fp32 -> bf16, round to nearest even (NaN kept quiet).
-__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return bf16_t((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return bf16_t(u >> 16);
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed pair of bf16 (low half = a), round to nearest even: one
+// v_cvt_pk_bf16_f32 on gfx950.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2_v v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
-// Two fp32 -> packed pair of bf16 (low half = a).
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return uint32_t(f32_to_bf16(a)) | (uint32_t(f32_to_bf16(b)) << 16);
+// fp32 -> bf16, round to nearest even.
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  return bf16_t(pack_bf16x2(f, 0.f) & 0xffffu);
 }
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16_t v) { return bf16_to_f32(v); }
 
 template <typename T> struct Elem;
 template <> struct Elem<float> {

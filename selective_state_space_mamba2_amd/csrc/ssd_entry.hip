@@ -75,9 +75,8 @@ ssd_status ssd_prefill(const ssd_prefill_args* a, void* workspace, size_t worksp
   char* ws = static_cast<char*>(workspace);
   p.states = a->chunk_states_out;
   if (plan.kind == ssd::PrefillKind::kChunked) {
-    p.dA_last = reinterpret_cast<float*>(ws + plan.off_dA_last);
-    p.init_copy = plan.has_init_copy ? reinterpret_cast<float*>(ws + plan.off_init) : nullptr;
-    if (plan.states_in_ws) p.states = reinterpret_cast<float*>(ws + plan.off_states);
+    p.cbw = ws + plan.off_cb;
+    p.btw = ws + plan.off_bt;
   }
 
   const hipStream_t s = static_cast<hipStream_t>(stream);
@@ -93,12 +92,12 @@ ssd_status ssd_prefill_kernel_count(const ssd_prefill_args* a, int32_t* count,
   ssd::PrefillPlan plan;
   const ssd_status st = ssd::plan_prefill(a, &plan);
   if (st != SSD_OK) return st;
-  static const char* const kChunked[] = {"k_chunk_state", "k_state_passing", "k_chunk_scan"};
+  static const char* const kChunked[] = {"k_chunk_prep", "k_chunk_march"};
   static const char* const kDiag[] = {"k_diag_scan"};
   *count = 0;
   if (a->num_seqs == 0) return SSD_OK;
   const char* const* list = plan.kind == ssd::PrefillKind::kChunked ? kChunked : kDiag;
-  *count = plan.kind == ssd::PrefillKind::kChunked ? 3 : 1;
+  *count = plan.kind == ssd::PrefillKind::kChunked ? 2 : 1;
   if (names)
     for (int i = 0; i < *count; ++i) names[i] = list[i];
   return SSD_OK;

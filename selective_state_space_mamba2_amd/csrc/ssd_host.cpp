@@ -58,7 +58,7 @@ ssd_status plan_prefill(const ssd_prefill_args* a, PrefillPlan* plan) {
   if (std::isnan(a->dt_min) || std::isnan(a->dt_max) || a->dt_min > a->dt_max)
     return SSD_ERR_BAD_SHAPE;
 
-  const int64_t C = a->num_chunks, S = a->num_seqs;
+  const int64_t C = a->num_chunks;
   if (a->a_kind == SSD_A_DIAG) {
     if (a->P != 1 || a->G != 1) return SSD_ERR_BAD_SHAPE;
     if (a->N != kDiagN) return SSD_ERR_UNSUPPORTED;
@@ -77,22 +77,18 @@ ssd_status plan_prefill(const ssd_prefill_args* a, PrefillPlan* plan) {
     }
   }
   if (variant < 0) return SSD_ERR_UNSUPPORTED;
+  // The chunked kernels factor exp(c_l - c_s) through reference points inside a chunk,
+  // which needs delta >= 0 (a monotone cumsum of delta*A): dt_min must not be negative.
+  if (!(a->dt_min >= 0.f)) return SSD_ERR_UNSUPPORTED;
   plan->kind = PrefillKind::kChunked;
   plan->variant = variant;
 
   size_t off = 0;
-  plan->off_dA_last = off;
-  off = align_up(off + size_t(C) * a->H * sizeof(float), 256);
-  plan->has_init_copy = a->has_initial_state != nullptr;
-  if (plan->has_init_copy) {
-    plan->off_init = off;
-    off = align_up(off + size_t(S) * size_t(state) * sizeof(float), 256);
-  }
-  plan->states_in_ws = a->chunk_states_out == nullptr;
-  if (plan->states_in_ws) {
-    plan->off_states = off;
-    off = align_up(off + size_t(C) * size_t(state) * sizeof(float), 256);
-  }
+  const size_t esz = a->in_dtype == SSD_BF16 ? 2 : 4;
+  plan->off_cb = off;
+  off = align_up(off + size_t(C) * a->G * a->chunk_size * a->chunk_size * esz, 256);
+  plan->off_bt = off;
+  off = align_up(off + size_t(C) * a->G * a->N * a->chunk_size * esz, 256);
   plan->ws_bytes = off;
   return SSD_OK;
 }

@@ -29,9 +29,9 @@ struct PrefillParams {
   const int* state_idx;
   const int* has_init;
   int write_final;
-  float* states;       // [C, H, P, N]: chunk_states_out or workspace
-  float* dA_last;      // [C, H] workspace
-  float* init_copy;    // [S, H, P, N] workspace (NULL when no initial states)
+  float* states;       // [C, H, P, N] chunk_states_out (NULL: not written)
+  void* cbw;           // [C, G, cs, cs] workspace, input dtype: C_l . B_s per chunk, group
+  void* btw;           // [C, G, N, cs] workspace, input dtype: B^T per chunk, group
   int* flag;
   float* dA_cumsum_out;
   float* cb_out;

@@ -17,11 +17,8 @@ struct PrefillPlan {
   PrefillKind kind = PrefillKind::kNone;
   int variant = -1;          // index into the chunked-kernel instantiation table
   size_t ws_bytes = 0;
-  size_t off_dA_last = 0;    // fp32 [C, H]   within-chunk total of delta*A
-  size_t off_init = 0;       // fp32 [S, H, P, N] copy of the gathered initial states
-  size_t off_states = 0;     // fp32 [C, H, P, N] chunk states when chunk_states_out is NULL
-  bool has_init_copy = false;
-  bool states_in_ws = false;
+  size_t off_cb = 0;         // input dtype [C, G, cs, cs]: C_l . B_s per chunk and group
+  size_t off_bt = 0;         // input dtype [C, G, N, cs]: B^T per chunk and group
 };
 
 // One instantiated chunked-prefill shape.

@@ -92,18 +92,37 @@ def _ws(a):
     return lib().ssd_prefill_workspace_size(ctypes.byref(a), ctypes.byref(n)), n.value
 
 
+def _al(v):
+    return (v + 255) // 256 * 256
+
+
 def test_workspace_size_layout():
-    st, n = _ws(_good_prefill())
-    # dA_last [C,H] fp32 then chunk states [C,H,P,N] fp32 (no chunk_states_out), 256-aligned
-    assert st == 0 and n == 256 + 3 * 8 * 64 * 128 * 4
-    st, n = _ws(_good_prefill(chunk_states_out=FAKE))
-    assert st == 0 and n == 256
-    st, n = _ws(_good_prefill(chunk_states_out=FAKE, has_initial_state=FAKE, state_pool=FAKE,
-                              state_indices=FAKE, num_slots=4, slot_stride=8 * 64 * 128))
-    assert st == 0 and n == 256 + 2 * 8 * 64 * 128 * 4
+    C, H, P, N, G, cs = 3, 8, 64, 128, 2, 256
+    # C.B^T [C,G,cs,cs] and B^T [C,G,N,cs] in the input dtype, shared by the heads of a group
+    prep = _al(C * G * cs * cs * 2) + _al(C * G * N * cs * 2)
+    for over in ({}, dict(chunk_states_out=FAKE),
+                 dict(chunk_states_out=FAKE, has_initial_state=FAKE, state_pool=FAKE,
+                      state_indices=FAKE, num_slots=4, slot_stride=8 * 64 * 128)):
+        st, n = _ws(_good_prefill(**over))
+        assert st == 0 and n == prep
     st, n = _ws(_good_prefill(a_kind=_abi.SSD_A_DIAG, H=64, P=1, G=1, N=16, x_stride_t=64,
                               y_stride_t=64, dt_stride_t=64, bc_stride_t=16))
     assert st == 0 and n == 0
+
+
+def test_kernel_count():
+    n = ctypes.c_int32(-1)
+    names = (ctypes.c_char_p * _abi.SSD_PREFILL_MAX_KERNELS)()
+    assert lib().ssd_prefill_kernel_count(ctypes.byref(_good_prefill()), ctypes.byref(n), names) == 0
+    assert n.value == 2
+    assert [names[i] for i in range(2)] == [b"k_chunk_prep", b"k_chunk_march"]
+    diag = _good_prefill(a_kind=_abi.SSD_A_DIAG, H=64, P=1, G=1, N=16, x_stride_t=64,
+                         y_stride_t=64, dt_stride_t=64, bc_stride_t=16)
+    assert lib().ssd_prefill_kernel_count(ctypes.byref(diag), ctypes.byref(n), names) == 0
+    assert n.value == 1 and names[0] == b"k_diag_scan"
+    empty = _good_prefill(T=0, num_seqs=0, num_chunks=0)
+    assert lib().ssd_prefill_kernel_count(ctypes.byref(empty), ctypes.byref(n), None) == 0
+    assert n.value == 0
 
 
 @pytest.mark.parametrize("over,status", [
@@ -132,6 +151,7 @@ def test_workspace_size_layout():
     (dict(chunk_size=100), _abi.SSD_ERR_UNSUPPORTED),
     (dict(in_dtype=_abi.SSD_F32), _abi.SSD_ERR_UNSUPPORTED),   # fp32 at cs=256
     (dict(a_kind=_abi.SSD_A_DIAG), _abi.SSD_ERR_BAD_SHAPE),    # diag needs P == 1
+    (dict(dt_min=-1.0), _abi.SSD_ERR_UNSUPPORTED),          # chunked path needs delta >= 0
 ])
 def test_prefill_host_checks(over, status):
     a = _good_prefill(**over)
