@@ -57,7 +57,7 @@ class PrefillArgs(ctypes.Structure):
     ]
 
 
-SSD_PREFILL_MAX_KERNELS = 2
+SSD_PREFILL_MAX_KERNELS = 3
 
 
 class DecodeArgs(ctypes.Structure):

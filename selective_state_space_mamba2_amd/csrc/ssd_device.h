@@ -62,12 +62,25 @@ struct DtPrep {
   const float* bias;
   int softplus;
   float lo, hi;
-  __device__ __forceinline__ float operator()(float raw, int h) const {
-    float v = raw + (bias ? bias[h] : 0.f);
+  __device__ __forceinline__ float bias_of(int h) const { return bias ? bias[h] : 0.f; }
+  // with the bias value already loaded (kernels that reuse one head's bias many times)
+  __device__ __forceinline__ float apply(float raw, float b) const {
+    float v = raw + b;
     if (softplus) v = softplus_f(v);
     return fminf(fmaxf(v, lo), hi);
   }
+  __device__ __forceinline__ float operator()(float raw, int h) const {
+    return apply(raw, bias_of(h));
+  }
 };
+
+// Read-only metadata read through the constant address space: with a wave-uniform index
+// this is a scalar load, which a wave does not have to drain its vector loads to use.
+// Only for arrays no kernel of the launch writes.
+typedef const __attribute__((address_space(4))) int32_t const_i32;
+__device__ __forceinline__ int ld_meta(const int32_t* q, int i) {
+  return ((const_i32*)q)[i];
+}
 
 // ---------------------------------------------------------------------------------------
 // MFMA 16x16 tiles.  A 16x16 fp32 accumulator tile lives in f32x4_v per lane: lane L holds

@@ -85,10 +85,13 @@ ssd_status plan_prefill(const ssd_prefill_args* a, PrefillPlan* plan) {
 
   size_t off = 0;
   const size_t esz = a->in_dtype == SSD_BF16 ? 2 : 4;
+  const size_t cs = size_t(a->chunk_size);
   plan->off_cb = off;
-  off = align_up(off + size_t(C) * a->G * a->chunk_size * a->chunk_size * esz, 256);
+  off = align_up(off + size_t(C) * a->G * size_t(cb_frag_base(int(cs / 16))) * 512 * esz, 256);
   plan->off_bt = off;
-  off = align_up(off + size_t(C) * a->G * a->N * a->chunk_size * esz, 256);
+  off = align_up(off + size_t(C) * a->G * a->N * cs * esz, 256);
+  plan->off_dc = off;
+  off = align_up(off + size_t(C) * a->H * 2 * cs * sizeof(float), 256);
   plan->ws_bytes = off;
   return SSD_OK;
 }

@@ -30,8 +30,9 @@ struct PrefillParams {
   const int* has_init;
   int write_final;
   float* states;       // [C, H, P, N] chunk_states_out (NULL: not written)
-  void* cbw;           // [C, G, cs, cs] workspace, input dtype: C_l . B_s per chunk, group
-  void* btw;           // [C, G, N, cs] workspace, input dtype: B^T per chunk, group
+  void* cbw;           // workspace, input dtype: C.B^T fragments per chunk and group
+  void* btw;           // workspace, input dtype: B^T fragments per chunk and group
+  float* dcw;          // workspace [C, H, 2, cs]: cumsum of delta*A, then delta
   int* flag;
   float* dA_cumsum_out;
   float* cb_out;

@@ -17,9 +17,15 @@ struct PrefillPlan {
   PrefillKind kind = PrefillKind::kNone;
   int variant = -1;          // index into the chunked-kernel instantiation table
   size_t ws_bytes = 0;
-  size_t off_cb = 0;         // input dtype [C, G, cs, cs]: C_l . B_s per chunk and group
-  size_t off_bt = 0;         // input dtype [C, G, N, cs]: B^T per chunk and group
+  size_t off_cb = 0;         // input dtype, per (chunk, group): the C.B^T blocks of every
+                             // row tile, cb_frag_base(cs/16) fragments of 512 values
+  size_t off_bt = 0;         // input dtype [C, G, N * cs]: B^T per chunk and group
+  size_t off_dc = 0;         // fp32 [C, H, 2, cs]: cumsum of delta*A, then delta
 };
+
+// C.B^T fragments of the 16-row tiles 0..i-1 of a chunk: tile i needs the 32-token blocks
+// 0..i/2 (one fragment each).
+constexpr int cb_frag_base(int i) { return (i / 2) * (i / 2 + 1) + (i % 2) * (i / 2 + 1); }
 
 // One instantiated chunked-prefill shape.
 struct ChunkedShape {

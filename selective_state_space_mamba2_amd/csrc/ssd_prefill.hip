@@ -7,22 +7,24 @@
 // c_t = sum_{r<=t} delta_r A (chunk-local), unrolling the recurrence gives
 //   h_end  = exp(c_last) h_in + sum_s delta_s exp(c_last - c_s) x_s B_s^T
 //   y_l    = exp(c_l) (h_in C_l) + sum_{s<=l} (C_l . B_s) exp(c_l - c_s) delta_s x_s + D x_l
-// which two kernels evaluate:
-//   k_chunk_prep   per (chunk, group): C.B^T (lower-triangular 16x16 tiles) and B^T in the
-//                  input dtype, computed once and shared by every head of the group
-//   k_chunk_march  per (head, sequence): walks the sequence's chunks with the fp32 state in
-//                  registers, producing y, the state after every chunk (the prefix-caching
-//                  checkpoint, "why this design", item 3) and the final state for the pool
-// Both contractions of a chunk run on bf16 MFMA with fp32 accumulation; the state and its
-// decay stay fp32.  Decay factors are products of exp of cumsum differences that are all
-// <= 0 for A <= 0 and delta >= 0 (never exp(+c) * exp(-c)), so they stay in [0, 1].
+// which three kernels evaluate:
+//   k_chunk_cumsum per (chunk, 16 heads): delta and the chunk-local cumsum c of delta*A,
+//                  one wavefront scan per head
+//   k_chunk_prep   per (chunk, group): B^T and the lower-triangular C.B^T blocks in the
+//                  input dtype, written in MFMA-fragment order and shared by every head
+//   k_chunk_march  per (head, sequence, slice of the head dim): walks the sequence's chunks
+//                  with the fp32 state in registers, producing y, the state after every
+//                  chunk (the prefix-caching checkpoint, "why this design", item 3) and the
+//                  final state for the pool
+// The contractions run on bf16 MFMA with fp32 accumulation; the state and its decay stay
+// fp32.  Decay factors are products of exp of cumsum differences that are all <= 0 for
+// A <= 0 and delta >= 0 (never exp(+c) * exp(-c)), so they stay in [0, 1].
 //
 // MFMA fragments (v_mfma_f32_16x16x32_bf16; fp32 inputs use 8 x v_mfma_f32_16x16x4_f32 on
-// the same 8-values-per-lane fragments): the 16x16 fp32 result tile gives lane L rows
-// 4*(L/16)+r of column L%16.  k_chunk_prep computes C.B^T transposed (rows s, columns l),
-// so each lane stores four consecutive s of one row l.  In k_chunk_march the A operand of
-// the (L o CB) X product is a C.B^T row fragment whose slots j<4 hold s = s0+4*(L/16)+j and
-// slots j>=4 hold s = s0+16+4*(L/16)+(j-4); X^T is read with the same slot -> s map.
+// the same 8-values-per-lane fragments): lane L supplies row (A) or column (B) L%16 and
+// the contracted indices 8*(L/16) + j, j = 0..7; the 16x16 fp32 result gives lane L rows
+// 4*(L/16) + r of column L%16.  The march kernel computes y transposed (rows p, columns l)
+// so that a lane's result is four consecutive p of one token row, stored directly.
 #include "ssd_params.h"
 
 namespace ssd {
@@ -35,25 +37,14 @@ template <typename T> struct Ops;
 template <> struct Ops<bf16_t> {
   using lds_t = bf16_t;
   using frag = Frag8;
-  static constexpr int kPad = 8;  // 16 B of row padding (spreads rows over LDS banks)
+  static constexpr int kPad = 8;  // 16 B of row padding
   static __device__ __forceinline__ frag ld8(const lds_t* q) {
     const u32x4_v v = *reinterpret_cast<const u32x4_v*>(q);
     return frag{{v.x, v.y, v.z, v.w}};
   }
-  static __device__ __forceinline__ frag ld44(const lds_t* a, const lds_t* b) {
-    const u32x2_v va = *reinterpret_cast<const u32x2_v*>(a);
-    const u32x2_v vb = *reinterpret_cast<const u32x2_v*>(b);
-    return frag{{va.x, va.y, vb.x, vb.y}};
-  }
   static __device__ __forceinline__ frag from8(const float* v) {
     return frag{{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
                  pack_bf16x2(v[6], v[7])}};
-  }
-  // 8 consecutive global elements (16 B aligned), zeros when !ok
-  static __device__ __forceinline__ frag gld8(const bf16_t* q, bool ok) {
-    if (!ok) return frag{{0u, 0u, 0u, 0u}};
-    const u32x4_v v = *reinterpret_cast<const u32x4_v*>(q);
-    return frag{{v.x, v.y, v.z, v.w}};
   }
   // 8 consecutive global elements (16 B aligned), always loaded: callers pass a valid
   // address and mask the values where they are used
@@ -61,19 +52,37 @@ template <> struct Ops<bf16_t> {
     const u32x4_v v = *reinterpret_cast<const u32x4_v*>(q);
     return frag{{v.x, v.y, v.z, v.w}};
   }
-  // 4 + 4 consecutive global elements (8-byte aligned)
-  static __device__ __forceinline__ frag gld44(const bf16_t* a, const bf16_t* b) {
-    const u32x2_v va = *reinterpret_cast<const u32x2_v*>(a);
-    const u32x2_v vb = *reinterpret_cast<const u32x2_v*>(b);
-    return frag{{va.x, va.y, vb.x, vb.y}};
+  // 8 consecutive global elements (16 B aligned), zeros when !ok
+  static __device__ __forceinline__ frag gld8(const bf16_t* q, bool ok) {
+    if (!ok) return frag{{0u, 0u, 0u, 0u}};
+    return gld8u(q);
+  }
+  static __device__ __forceinline__ void st8(bf16_t* q, const frag& f) {
+    *reinterpret_cast<u32x4_v*>(q) = u32x4_v{f.w[0], f.w[1], f.w[2], f.w[3]};
+  }
+  // four fp32 values -> 4 consecutive elements
+  static __device__ __forceinline__ void st4(bf16_t* q, f32x4_v v) {
+    *reinterpret_cast<u32x2_v*>(q) = u32x2_v{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
   }
   static __device__ __forceinline__ f32x4_v mma(const frag& a, const frag& b, f32x4_v c) {
     return mma_bf16(a, b, c);
   }
   static __device__ __forceinline__ lds_t cvt(float v) { return f32_to_bf16(v); }
-  static __device__ __forceinline__ float tof(lds_t v) { return bf16_to_f32(v); }
   static __device__ __forceinline__ float val(const frag& f, int j) {
     return bf16_to_f32(bf16_t(f.w[j >> 1] >> ((j & 1) * 16)));
+  }
+  // elements j of four fragments, scaled, as 4 consecutive LDS elements
+  static __device__ __forceinline__ void put4(lds_t* d, const frag* v, int j, const float* sc) {
+    *reinterpret_cast<u32x2_v*>(d) =
+        u32x2_v{pack_bf16x2(val(v[0], j) * sc[0], val(v[1], j) * sc[1]),
+                pack_bf16x2(val(v[2], j) * sc[2], val(v[3], j) * sc[3])};
+  }
+  // the same, unscaled (a pure 16-bit shuffle)
+  static __device__ __forceinline__ void put4raw(lds_t* d, const frag* v, int j) {
+    const uint32_t sh = (j & 1) * 16;
+    const uint32_t e0 = (v[0].w[j >> 1] >> sh) & 0xffffu, e1 = (v[1].w[j >> 1] >> sh) & 0xffffu;
+    const uint32_t e2 = (v[2].w[j >> 1] >> sh) & 0xffffu, e3 = (v[3].w[j >> 1] >> sh) & 0xffffu;
+    *reinterpret_cast<u32x2_v*>(d) = u32x2_v{e0 | (e1 << 16), e2 | (e3 << 16)};
   }
 };
 
@@ -86,28 +95,33 @@ template <> struct Ops<float> {
     const float4_v b = *reinterpret_cast<const float4_v*>(q + 4);
     return frag{{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w}};
   }
-  static __device__ __forceinline__ frag ld44(const lds_t* a, const lds_t* b) {
-    const float4_v va = *reinterpret_cast<const float4_v*>(a);
-    const float4_v vb = *reinterpret_cast<const float4_v*>(b);
-    return frag{{va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w}};
-  }
   static __device__ __forceinline__ frag from8(const float* v) {
     return frag{{v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]}};
   }
+  static __device__ __forceinline__ frag gld8u(const float* q) { return ld8(q); }
   static __device__ __forceinline__ frag gld8(const float* q, bool ok) {
     if (!ok) return frag{{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}};
     return ld8(q);
   }
-  static __device__ __forceinline__ frag gld8u(const float* q) { return ld8(q); }
-  static __device__ __forceinline__ frag gld44(const float* a, const float* b) {
-    return ld44(a, b);
+  static __device__ __forceinline__ void st8(float* q, const frag& f) {
+    *reinterpret_cast<float4_v*>(q) = float4_v{f.v[0], f.v[1], f.v[2], f.v[3]};
+    *reinterpret_cast<float4_v*>(q + 4) = float4_v{f.v[4], f.v[5], f.v[6], f.v[7]};
+  }
+  static __device__ __forceinline__ void st4(float* q, f32x4_v v) {
+    *reinterpret_cast<float4_v*>(q) = float4_v{v[0], v[1], v[2], v[3]};
   }
   static __device__ __forceinline__ f32x4_v mma(const frag& a, const frag& b, f32x4_v c) {
     return mma_f32(a, b, c);
   }
   static __device__ __forceinline__ lds_t cvt(float v) { return v; }
-  static __device__ __forceinline__ float tof(lds_t v) { return v; }
   static __device__ __forceinline__ float val(const frag& f, int j) { return f.v[j]; }
+  static __device__ __forceinline__ void put4(lds_t* d, const frag* v, int j, const float* sc) {
+    *reinterpret_cast<float4_v*>(d) = float4_v{v[0].v[j] * sc[0], v[1].v[j] * sc[1],
+                                               v[2].v[j] * sc[2], v[3].v[j] * sc[3]};
+  }
+  static __device__ __forceinline__ void put4raw(lds_t* d, const frag* v, int j) {
+    *reinterpret_cast<float4_v*>(d) = float4_v{v[0].v[j], v[1].v[j], v[2].v[j], v[3].v[j]};
+  }
 };
 
 // Chunk k's token range and sequence; false if the metadata is bad.
@@ -129,106 +143,74 @@ __device__ __forceinline__ void wave_lds_sync() {
   asm volatile("" ::: "memory");
 }
 
-// The l-tiles (16 rows each) a wave owns: tiles t with t % (2*NW) in {w, 2*NW-1-w}, which
-// balances the causal (lower-triangular) work across the waves.
-template <int NTILES, int NW>
-struct TileSet {
-  static constexpr int kPer = (NTILES + NW - 1) / NW;
-  __device__ static __forceinline__ int tile(int w, int q) {
-    const int period = q / 2, second = q & 1;
-    return period * 2 * NW + (second ? 2 * NW - 1 - w : w);
+// The transposed x tiles in LDS are [column p][token s]; token groups of 16 are XOR-ed with
+// bits 3..4 of p, which spreads the staging writes of consecutive column groups over all
+// banks and keeps every 8-token fragment contiguous and 16 B aligned.
+__device__ __forceinline__ int xsw(int p, int s) { return s ^ (((p >> 3) & 3) << 4); }
+
+// ---------------------------------------------------------------------------------------
+// k_chunk_cumsum: delta = clamp(softplus(dt + bias)) and the chunk-local inclusive cumsum
+// c of delta*A per (chunk, head), written [C][H][2][CS] (c then delta).  Positions at or past
+// the chunk end hold delta = 0 and c = c_last, the flat continuation the march relies on.
+// One wavefront per head: four tokens per lane, a lane-local prefix, a wave scan.
+// ---------------------------------------------------------------------------------------
+constexpr int kCumHeads = 16;   // heads per workgroup (4 per wavefront)
+
+template <typename T, int CS>
+__global__ __launch_bounds__(256) void k_chunk_cumsum(PrefillParams p) {
+  static_assert(CS <= 256 && CS % 4 == 0, "chunk size");
+  const int k = blockIdx.x, tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  int cs0, L, r;
+  if (!chunk_bounds(p, k, CS, cs0, L, r)) {
+    if (tid == 0 && blockIdx.y == 0) raise_flag(p.flag, SSD_DEVERR_CHUNK_RANGE);
+    return;
   }
-};
-
-// Staging of a row-major [token][W] chunk into LDS transposed (token index contiguous).  A
-// work item moves a 4-token x 8-column block: four 16-byte row loads (eight consecutive
-// lanes cover one 128-byte row, so loads are coalesced) and eight 4-token column writes.
-// The loads are issued early into registers (stage_load) and written out once the scale
-// factors are known (stage_store).  Loads are unguarded (rows past the chunk end repeat its
-// last row) so that no branch forces an early wait on them.
-template <typename T>
-__device__ __forceinline__ void put4(typename Ops<T>::lds_t* d, const typename Ops<T>::frag* v,
-                                     int j, const float* sc) {
-  using O = Ops<T>;
-  if constexpr (sizeof(T) == 2) {
-    if (sc) {
-      *reinterpret_cast<u32x2_v*>(d) =
-          u32x2_v{pack_bf16x2(O::val(v[0], j) * sc[0], O::val(v[1], j) * sc[1]),
-                  pack_bf16x2(O::val(v[2], j) * sc[2], O::val(v[3], j) * sc[3])};
-    } else {
-      const uint32_t sh = (j & 1) * 16;
-      const uint32_t e0 = (v[0].w[j >> 1] >> sh) & 0xffffu, e1 = (v[1].w[j >> 1] >> sh) & 0xffffu;
-      const uint32_t e2 = (v[2].w[j >> 1] >> sh) & 0xffffu, e3 = (v[3].w[j >> 1] >> sh) & 0xffffu;
-      *reinterpret_cast<u32x2_v*>(d) = u32x2_v{e0 | (e1 << 16), e2 | (e3 << 16)};
-    }
-  } else {
-    const float s0 = sc ? sc[0] : 1.f, s1 = sc ? sc[1] : 1.f, s2 = sc ? sc[2] : 1.f,
-                s3 = sc ? sc[3] : 1.f;
-    *reinterpret_cast<float4_v*>(d) = float4_v{O::val(v[0], j) * s0, O::val(v[1], j) * s1,
-                                               O::val(v[2], j) * s2, O::val(v[3], j) * s3};
-  }
-}
-
-// The x tile of one work item: 4 tokens x 8 columns, loaded into registers.
-template <typename T, int W, int KB, int NTH>
-struct StageRegs {
-  static constexpr int NG = W / 8, NQ = KB / 4, NI = (NQ * NG + NTH - 1) / NTH;
-  typename Ops<T>::frag v[NI][4];
-};
-
-template <typename T, int W, int KB, int NTH>
-__device__ __forceinline__ void stage_load(StageRegs<T, W, KB, NTH>& st, const T* src,
-                                           int64_t stride_t, int L) {
-  using SR = StageRegs<T, W, KB, NTH>;
-#pragma unroll
-  for (int u = 0; u < SR::NI; ++u) {
-    const int it = u * NTH + int(threadIdx.x);
-    const int g8 = it % SR::NG;
-    const int s = 4 * ((it < SR::NQ * SR::NG ? it : 0) / SR::NG);
+  const T* dtp = static_cast<const T*>(p.dt);
+#pragma unroll 1
+  for (int i = 0; i < kCumHeads / 4; ++i) {
+    const int h = blockIdx.y * kCumHeads + wave + 4 * i;
+    if (h >= p.H) break;
+    const float Ah = p.A[h], bias = p.prep.bias_of(h);
+    float d[4], c[4];
+    float run = 0.f;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      // no guard: rows past the chunk end are clamped to its last row
-      const int row = s + t < L ? s + t : L - 1;
-      st.v[u][t] = Ops<T>::gld8u(src + int64_t(row) * stride_t + 8 * g8);
+      const int tok = 4 * lane + t;
+      const int row = tok < L ? tok : L - 1;
+      const float raw = to_f32(dtp[int64_t(cs0 + row) * p.dt_st + h]);
+      d[t] = tok < L ? p.prep.apply(raw, bias) : 0.f;
+      run += d[t] * Ah;
+      c[t] = run;
     }
-  }
-}
-
-// Write the loaded tile transposed into dst[W][RS] (token index contiguous), token s scaled
-// by scale[s] when given; when dst2 is given, a second copy scaled by scale2[s] goes there.
-template <typename T, int W, int KB, int RS, int NTH>
-__device__ __forceinline__ void stage_store(const StageRegs<T, W, KB, NTH>& st,
-                                            typename Ops<T>::lds_t* dst, const float* scale,
-                                            typename Ops<T>::lds_t* dst2 = nullptr,
-                                            const float* scale2 = nullptr) {
-  using SR = StageRegs<T, W, KB, NTH>;
+    const float incl = wave_inclusive_scan(run);
+    const float base = incl - run;
 #pragma unroll
-  for (int u = 0; u < SR::NI; ++u) {
-    const int it = u * NTH + int(threadIdx.x);
-    if (it >= SR::NQ * SR::NG) break;
-    const int g8 = it % SR::NG, s = 4 * (it / SR::NG);
-    float sc[4], sc2[4];
-    if (scale) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) sc[t] = scale[s + t];
+    for (int t = 0; t < 4; ++t) c[t] += base;
+    if (4 * lane < CS) {
+      float* dst = p.dcw + (int64_t(k) * p.H + h) * (2 * CS) + 4 * lane;
+      *reinterpret_cast<float4_v*>(dst) = float4_v{c[0], c[1], c[2], c[3]};
+      *reinterpret_cast<float4_v*>(dst + CS) = float4_v{d[0], d[1], d[2], d[3]};
     }
-    if (dst2) {
+    if (p.dA_cumsum_out) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) sc2[t] = scale2[s + t];
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      put4<T>(dst + (8 * g8 + j) * RS + s, st.v[u], j, scale ? sc : nullptr);
-      if (dst2) put4<T>(dst2 + (8 * g8 + j) * RS + s, st.v[u], j, sc2);
+      for (int t = 0; t < 4; ++t)
+        if (4 * lane + t < L) p.dA_cumsum_out[int64_t(h) * p.T + cs0 + 4 * lane + t] = c[t];
     }
   }
 }
 
 // ---------------------------------------------------------------------------------------
-// k_chunk_prep: per (chunk, group) C.B^T (lower-triangular 16x16 tiles, incl. the diagonal)
-// and B^T, both in the input dtype, shared by every head of the group
+// k_chunk_prep: per (chunk, group) B^T and the C.B^T blocks the y tiles need, both in the
+// input dtype and in MFMA-fragment order (one fragment = 64 lanes x 8 values, 1 KB in bf16),
+// so a wavefront fetches a fragment with one contiguous load.
+//   B^T fragment (n-tile nt, 32-token step ss): lane (kg, li) holds B[s = 32 ss + 8 kg + j]
+//     [n = 16 nt + li]; stored at ((chunk * G + g) * TN + nt) * NSTEP + ss.
+//   C.B^T fragment (row tile i, block b <= i/2): lane (kg, li) holds (C_l . B_s) for
+//     l = 16 i + li, s = 32 b + 8 kg + j; stored at (chunk * G + g) * NF + cb_frag_base(i) + b.
+// Rows past the chunk end are zero.  Work is split over kPrepSplit workgroups.
 // ---------------------------------------------------------------------------------------
-constexpr int kPrepSplit = 2;   // workgroups per (chunk, group) in k_chunk_prep
+constexpr int kPrepSplit = 4;
 
 template <typename T, int N, int CS>
 __global__ __launch_bounds__(256) void k_chunk_prep(PrefillParams p) {
@@ -238,8 +220,11 @@ __global__ __launch_bounds__(256) void k_chunk_prep(PrefillParams p) {
   constexpr int NW = 4;
   constexpr int NP = N < 32 ? 32 : N;    // dstate padded to the MFMA K of 32
   constexpr int RSB = NP + O::kPad;
-  constexpr int KN = NP / 32, NT = CS / 16;
+  constexpr int KN = NP / 32, NT = CS / 16, NSTEP = CS / 32, TN = N / 16;
+  constexpr int NF = cb_frag_base(NT);
+  constexpr int TLS = 36;                 // row stride of the per-wave 16 x 32 staging tile
   __shared__ __attribute__((aligned(16))) lds_t Bs[CS * RSB];
+  __shared__ __attribute__((aligned(16))) float tl[NW][16 * TLS];
 
   const int k = blockIdx.x, g = blockIdx.y, z = blockIdx.z, tid = threadIdx.x;
   int cs0, L, r;
@@ -260,37 +245,32 @@ __global__ __launch_bounds__(256) void k_chunk_prep(PrefillParams p) {
   }
   __syncthreads();
 
-  // B^T [N][CS] (this workgroup's half of the rows): lanes walk n fastest (conflict-free
-  // LDS column reads)
-  constexpr int NH = N / kPrepSplit;
-  T* bt = static_cast<T*>(p.btw) + (int64_t(k) * p.G + g) * N * CS;
-  for (int e = tid; e < NH * (CS / 8); e += 256) {
-    const int n = z * NH + e % NH, s8 = e / NH;
-    if constexpr (sizeof(T) == 2) {
-      uint32_t w[4];
+  // B^T fragments, this workgroup's share
+  T* bt = static_cast<T*>(p.btw) + (int64_t(k) * p.G + g) * (int64_t(N) * CS);
+  for (int e = z * 256 + tid; e < TN * NSTEP * 64; e += 256 * kPrepSplit) {
+    const int f = e >> 6, ln = e & 63;
+    const int nt = f / NSTEP, ss = f % NSTEP, li = ln & 15, kg = ln >> 4;
+    float v[8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        w[j] = uint32_t(Bs[(8 * s8 + 2 * j) * RSB + n]) | (uint32_t(Bs[(8 * s8 + 2 * j + 1) * RSB + n]) << 16);
-      *reinterpret_cast<u32x4_v*>(bt + int64_t(n) * CS + 8 * s8) = u32x4_v{w[0], w[1], w[2], w[3]};
-    } else {
-      float w[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) w[j] = Bs[(8 * s8 + j) * RSB + n];
-      *reinterpret_cast<float4_v*>(bt + int64_t(n) * CS + 8 * s8) = float4_v{w[0], w[1], w[2], w[3]};
-      *reinterpret_cast<float4_v*>(bt + int64_t(n) * CS + 8 * s8 + 4) = float4_v{w[4], w[5], w[6], w[7]};
-    }
+    for (int j = 0; j < 8; ++j) v[j] = to_f32(Bs[(32 * ss + 8 * kg + j) * RSB + 16 * nt + li]);
+    O::st8(bt + int64_t(e) * 8, O::from8(v));
   }
 
-  // C.B^T tiles, computed transposed (rows s, columns l) so a lane ends up with four
-  // consecutive s of one row l: CB[l][s0 + 4*(L/16) + r].
+  // C.B^T fragments: each 16x16 tile is computed transposed (rows s, columns l) so lane
+  // (kg, li) gets C_l . B_s for l = 16 i + li, s = 16 jt + 4 kg + rr; two tiles are regrouped
+  // through LDS into the 8-consecutive-s fragment of one 32-token block.
   const int wave = tid >> 6, lane = tid & 63, li = lane & 15, kg = lane >> 4;
   const T* csrc = static_cast<const T*>(p.Cm) + int64_t(cs0) * p.bc_st + int64_t(g) * N;
-  T* cb = static_cast<T*>(p.cbw) + (int64_t(k) * p.G + g) * CS * CS;
+  T* cb = static_cast<T*>(p.cbw) + (int64_t(k) * p.G + g) * (int64_t(NF) * 512);
   float* cb_dbg = p.cb_out ? p.cb_out + (int64_t(k) * p.G + g) * CS * CS : nullptr;
-  using TS = TileSet<NT, NW * kPrepSplit>;
+  float* tw = tl[wave];
+  // row tiles of this workgroup: w = z * NW + wave, then mirrored pairs balancing the
+  // causal work
+  constexpr int NWT = NW * kPrepSplit;
 #pragma unroll 1
-  for (int q = 0; q < TS::kPer; ++q) {
-    const int i = TS::tile(z * NW + wave, q);
+  for (int q = 0; q < (NT + NWT - 1) / NWT; ++q) {
+    const int w = z * NW + wave;
+    const int i = (q / 2) * 2 * NWT + ((q & 1) ? 2 * NWT - 1 - w : w);
     if (i >= NT) continue;
     const int lrow = 16 * i + li;
     frag cf[KN];
@@ -298,164 +278,142 @@ __global__ __launch_bounds__(256) void k_chunk_prep(PrefillParams p) {
     for (int kk = 0; kk < KN; ++kk)
       cf[kk] = O::gld8(csrc + int64_t(lrow) * p.bc_st + 32 * kk + 8 * kg,
                        lrow < L && 32 * kk + 8 * kg < N);
-    for (int j = 0; j <= i; ++j) {
-      f32x4_v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+    for (int b = 0; b <= i / 2; ++b) {
 #pragma unroll
-      for (int kk = 0; kk < KN; ++kk)
-        acc = O::mma(O::ld8(&Bs[(16 * j + li) * RSB + 32 * kk + 8 * kg]), cf[kk], acc);
-      T* dst = cb + int64_t(lrow) * CS + 16 * j + 4 * kg;
-      if constexpr (sizeof(T) == 2) {
-        *reinterpret_cast<u32x2_v*>(dst) = u32x2_v{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-      } else {
-        *reinterpret_cast<float4_v*>(dst) = float4_v{acc[0], acc[1], acc[2], acc[3]};
-      }
-      if (cb_dbg && lrow < L) {
+      for (int half = 0; half < 2; ++half) {
+        const int jt = 2 * b + half;
+        f32x4_v acc = {0.f, 0.f, 0.f, 0.f};
+        if (jt <= i) {
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          if (16 * j + 4 * kg + rr <= lrow) cb_dbg[int64_t(lrow) * CS + 16 * j + 4 * kg + rr] = acc[rr];
+          for (int kk = 0; kk < KN; ++kk)
+            acc = O::mma(O::ld8(&Bs[(16 * jt + li) * RSB + 32 * kk + 8 * kg]), cf[kk], acc);
+        }
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) tw[li * TLS + 16 * half + 4 * kg + rr] = acc[rr];
+        if (cb_dbg && lrow < L && jt <= i) {
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            if (16 * jt + 4 * kg + rr <= lrow) cb_dbg[int64_t(lrow) * CS + 16 * jt + 4 * kg + rr] = acc[rr];
+        }
       }
+      wave_lds_sync();
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = tw[li * TLS + 8 * kg + j];
+      O::st8(cb + (int64_t(cb_frag_base(i) + b) * 64 + lane) * 8, O::from8(v));
+      wave_lds_sync();
     }
   }
 }
 
 // ---------------------------------------------------------------------------------------
-// k_chunk_march: one workgroup per (head, sequence) walks the sequence's chunks in order
-// with the fp32 state held in registers.  For chunk k with incoming state H_in:
+// k_chunk_march: one workgroup (4 wavefronts) per (head, sequence, PW-column slice of the
+// head dim) walks the sequence's chunks in order with its fp32 state rows in registers.
+// For chunk k with incoming state H_in:
 //   y_l   = exp(c_l) C_l . H_in[p, :] + sum_{s<=l} CB_{l,s} exp(c_l - c_s) delta_s x_s + D x_l
 //   H_out = exp(c_last) H_in + sum_s delta_s exp(c_last - c_s) x_s B_s^T
-// and H_out is the checkpoint written at the chunk end (prefix caching, "why this design",
-// item 3).  The intra-chunk sums are split at 32-token blocks b with reference
-// r_b = 32b + 31: x is staged twice in LDS, raw (x^T) and as X~_s = exp(c_{r(s)} - c_s)
-// delta_s x_s (X~^T).
-//   * y, blocks entirely before the row's 16-row tile: raw C.B^T tiles against X~; the
-//     running sum is rescaled by exp(c_{r_b} - c_{r_{b-1}}) per block and joins the row
-//     with exp(c_l - c_{r_last});
-//   * y, the block holding the diagonal: exp(c_l - c_s) per element, causal mask, raw x;
+// and H_out is the checkpoint written at the chunk end.  The intra-chunk sums are split
+// at 32-token blocks b with reference r_b = 32b + 31: x is staged twice in LDS, raw (x^T)
+// and as X~_s = exp(c_{r(s)} - c_s) delta_s x_s (X~^T).
+//   * y, blocks entirely before the row's 32-token block: C.B^T fragments against X~, the
+//     running sum rescaled by exp(c_{r_b} - c_{r_{b-1}}) per block and joined to row l with
+//     exp(c_l - c_{r_last});
+//   * y, the block holding the diagonal: exp(c_l - c_s) delta_s per element, causal mask,
+//     raw x, and D on the diagonal (the skip connection D x_l);
 //   * H_out: X~^T against B^T with the same running rescale, which ends at the chunk's
-//     last token (exp(c_last - c_last) = 1).
+//     last token.
 // Every factor is an exp of a non-positive cumsum difference (delta >= 0, A <= 0).
-//
-// Work split (2*CS threads, NW = CS/32 waves): wave w owns the 16-row y tiles w and
-// NT-1-w (equal causal work) and the state columns n-tile w, w+NW, ... for every p-tile;
-// the state lives in the MFMA result layout of X~^T B^T.  The next chunk's x rows and
-// delta (the HBM stream) are requested as soon as the current ones sit in LDS, so HBM
-// keeps streaming while the MFMAs run; the L2-resident operands (C.B^T, B^T, C rows) are
-// requested at the top of each chunk.
+// y is computed transposed (rows p, columns l): a lane's result is 4 consecutive p of one
+// token, stored straight from the accumulator.
+// Work split: wave w owns the row tiles {w, 7-w} (+8 for the second half of a 256-token
+// chunk), which balances the causal work, and the state n-tiles [w*TNW, (w+1)*TNW).
 // ---------------------------------------------------------------------------------------
-template <typename T, int P, int N, int CS>
+template <typename T, int P, int PW, int N, int CS>
 struct MarchCfg {
-  static constexpr int NW = CS / 32, NTH = 64 * NW, NT = CS / 16;
+  static constexpr int NW = 4, NTH = 256, NT = CS / 16, NSTEP = CS / 32;
   static constexpr int NP = N < 32 ? 32 : N;
-  static constexpr int RSX = CS + Ops<T>::kPad, RSB = NP + Ops<T>::kPad, RSY = P + Ops<T>::kPad;
-  static constexpr int TP = P / 16, TN = N / 16, NTW = (TN + NW - 1) / NW, KN = NP / 32;
-  static constexpr int NSTEP = CS / 32;
-  static constexpr int F0 = (NW - 1) / 2 + 1, F1 = NW;   // C.B^T fragment slots per y tile
+  static constexpr int RSX = CS + Ops<T>::kPad, RSB = NP + Ops<T>::kPad;
+  static constexpr int TPW = PW / 16, TN = N / 16, TNW = (TN + NW - 1) / NW, KN = NP / 32;
+  static constexpr int NTQ = NT / NW;                 // row tiles per wave
+  static constexpr int PT = NTQ < 2 ? NTQ : 2;        // row tiles processed together
+  static constexpr int NPAIR = NTQ / PT;
+  static constexpr int NG = PW / 8, NITEM = NG * CS / 4, NI = (NITEM + NTH - 1) / NTH;
+  static constexpr int NF = cb_frag_base(NT);
+  static_assert(NT % NW == 0 && NTQ <= 4, "row tiles");
+  static_assert(PW % 16 == 0 && P % PW == 0 && PW <= 32, "head-dim slice");
 };
 
-// Operand fragments of one chunk held in registers by one wave.
-template <typename T, int P, int N, int CS>
-struct MarchFrags {
-  using M = MarchCfg<T, P, N, CS>;
-  using frag = typename Ops<T>::frag;
-  StageRegs<T, P, CS, M::NTH> x;
-  T dt;     // raw, converted where it is used
-  frag cb0[M::F0], cb1[M::F1];
-  frag bt[M::NSTEP][M::NTW];
-  frag cf[2][M::KN];
+// Per-thread registers of one chunk's staging: x rows of the thread's work items and the
+// cumsum / delta of their four tokens.
+template <typename T, int NI>
+struct StageIn {
+  typename Ops<T>::frag x[NI][4];
+  float4_v c[NI], d[NI];
+  float cref[NI];
 };
 
 struct ChunkLoc {
   int cs0, L;
 };
 
-template <typename T, int P, int N, int CS>
-__device__ __forceinline__ void march_load_x(MarchFrags<T, P, N, CS>& f, const PrefillParams& p,
-                                             ChunkLoc c, int h) {
-  const T* xsrc = static_cast<const T*>(p.x) + int64_t(c.cs0) * p.x_st + int64_t(h) * P;
-  stage_load(f.x, xsrc, p.x_st, c.L);
-  const int row = int(threadIdx.x) < c.L ? int(threadIdx.x) : c.L - 1;
-  f.dt = static_cast<const T*>(p.dt)[int64_t(c.cs0 + row) * p.dt_st + h];
-}
-
-template <typename T, int P, int N, int CS>
-__device__ __forceinline__ void march_load_cb(MarchFrags<T, P, N, CS>& f, const PrefillParams& p,
-                                              ChunkLoc c, int k, int g, const int* tiles) {
-  using M = MarchCfg<T, P, N, CS>;
-  const int li = threadIdx.x & 15, kg = (threadIdx.x & 63) >> 4;
-  const T* cbrows = static_cast<const T*>(p.cbw) + (int64_t(k) * p.G + g) * CS * CS;
+// Work item `it`: columns 8*g8 .. 8*g8+7 of the slice, tokens 4*sg .. 4*sg+3.
+template <typename T, int P, int PW, int N, int CS>
+__device__ __forceinline__ void march_load_stage(StageIn<T, MarchCfg<T, P, PW, N, CS>::NI>& st,
+                                                 const PrefillParams& p, ChunkLoc c, int k,
+                                                 int h, int p0) {
+  using M = MarchCfg<T, P, PW, N, CS>;
+  const T* xsrc = static_cast<const T*>(p.x) + int64_t(c.cs0) * p.x_st + int64_t(h) * P + p0;
+  const float* dc = p.dcw + (int64_t(k) * p.H + h) * (2 * CS);
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int i = tiles[q], bd = i / 2;
-    const T* cbr = cbrows + int64_t(16 * i + li) * CS;
-    constexpr int nf0 = M::F0, nf1 = M::F1;
+  for (int u = 0; u < M::NI; ++u) {
+    int it = u * M::NTH + int(threadIdx.x);
+    it = it < M::NITEM ? it : 0;
+    const int g8 = it % M::NG, s = 4 * (it / M::NG);
 #pragma unroll
-    for (int b = 0; b < nf1; ++b) {
-      if (q == 0 && b >= nf0) break;
-      const int nf = q == 0 ? nf0 : nf1;
-      const int blk = b == nf - 1 ? bd : b;   // last slot: the diagonal block
-      const typename Ops<T>::frag v =
-          Ops<T>::gld44(cbr + 32 * blk + 4 * kg, cbr + 32 * blk + 16 + 4 * kg);
-      if (q == 0) f.cb0[b] = v; else f.cb1[b] = v;
+    for (int t = 0; t < 4; ++t) {
+      // unguarded: rows past the chunk end repeat its last row (their weight is zero)
+      const int row = s + t < c.L ? s + t : c.L - 1;
+      st.x[u][t] = Ops<T>::gld8u(xsrc + int64_t(row) * p.x_st + 8 * g8);
     }
+    st.c[u] = *reinterpret_cast<const float4_v*>(dc + s);
+    st.d[u] = *reinterpret_cast<const float4_v*>(dc + CS + s);
+    st.cref[u] = dc[s | 31];
   }
 }
 
-template <typename T, int P, int N, int CS>
-__device__ __forceinline__ void march_load_bt(MarchFrags<T, P, N, CS>& f, const PrefillParams& p,
-                                              int k, int g) {
-  using M = MarchCfg<T, P, N, CS>;
-  const int wave = threadIdx.x >> 6, li = threadIdx.x & 15, kg = (threadIdx.x & 63) >> 4;
-  const T* bt = static_cast<const T*>(p.btw) + (int64_t(k) * p.G + g) * N * CS;
-#pragma unroll
-  for (int ss = 0; ss < M::NSTEP; ++ss)
-#pragma unroll
-    for (int q = 0; q < M::NTW; ++q) {
-      const int nt = wave + M::NW * q < M::TN ? wave + M::NW * q : M::TN - 1;
-      f.bt[ss][q] = Ops<T>::gld8u(bt + int64_t(nt * 16 + li) * CS + 32 * ss + 8 * kg);
-    }
-}
-
-template <typename T, int P, int N, int CS>
-__device__ __forceinline__ void march_load_c(MarchFrags<T, P, N, CS>& f, const PrefillParams& p,
-                                             ChunkLoc c, int g, const int* tiles) {
-  using M = MarchCfg<T, P, N, CS>;
-  const int li = threadIdx.x & 15, kg = (threadIdx.x & 63) >> 4;
-  const T* cbase = static_cast<const T*>(p.Cm) + int64_t(c.cs0) * p.bc_st + int64_t(g) * N;
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int lrow = 16 * tiles[q] + li < c.L ? 16 * tiles[q] + li : c.L - 1;
-#pragma unroll
-    for (int kk = 0; kk < M::KN; ++kk) {
-      const int col = 32 * kk + 8 * kg < N ? 32 * kk + 8 * kg : 0;
-      f.cf[q][kk] = Ops<T>::gld8u(cbase + int64_t(lrow) * p.bc_st + col);
-    }
-  }
-}
-
-template <typename T, int P, int N, int CS>
-__global__ __launch_bounds__(CS * 2) void k_chunk_march(PrefillParams p) {
+#ifndef SSD_MARCH_WAVES_PER_EU
+#define SSD_MARCH_WAVES_PER_EU 3
+#endif
+#ifndef SSD_MARCH_BT_RING
+#define SSD_MARCH_BT_RING 4
+#endif
+#ifndef SSD_MARCH_PAIR_UNROLL
+#define SSD_MARCH_PAIR_UNROLL 2
+#endif
+// Three workgroups per CU (one wavefront of each on every SIMD) hide each other's
+// latencies; that caps the registers at 512 / 3 per lane.
+template <typename T, int P, int PW, int N, int CS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_MARCH_WAVES_PER_EU)))
+void k_chunk_march(PrefillParams p) {
   using O = Ops<T>;
   using lds_t = typename O::lds_t;
   using frag = typename O::frag;
-  using M = MarchCfg<T, P, N, CS>;
-  constexpr int NW = M::NW, NTH = M::NTH, NT = M::NT, NP = M::NP;
-  constexpr int RSX = M::RSX, RSB = M::RSB, RSY = M::RSY;
-  constexpr int TP = M::TP, TN = M::TN, NTW = M::NTW, KN = M::KN, NSTEP = M::NSTEP;
-  constexpr int F0 = M::F0, F1 = M::F1;
-  static_assert(CS <= 256 && CS % 64 == 0, "chunk size");
-  __shared__ __attribute__((aligned(16))) lds_t xT[P * RSX];    // raw x^T
-  __shared__ __attribute__((aligned(16))) lds_t xv[P * RSX];    // X~^T
-  __shared__ __attribute__((aligned(16))) lds_t Hs[P * RSB];    // incoming state, bf16
-  __shared__ __attribute__((aligned(16))) lds_t ystage[NW * 16 * RSY];
-  __shared__ float s_c[CS];
-  __shared__ float s_d[CS];
-  __shared__ float s_v[CS];
-  __shared__ float s_scan[NW];
+  using M = MarchCfg<T, P, PW, N, CS>;
+  constexpr int NW = M::NW, NTH = M::NTH, NT = M::NT, NP = M::NP, NSTEP = M::NSTEP;
+  constexpr int RSX = M::RSX, RSB = M::RSB;
+  constexpr int TPW = M::TPW, TN = M::TN, TNW = M::TNW, KN = M::KN;
+  constexpr int PT = M::PT, NPAIR = M::NPAIR, NF = M::NF;
+  __shared__ __attribute__((aligned(16))) lds_t xT[PW * RSX];    // raw x^T (swizzled)
+  __shared__ __attribute__((aligned(16))) lds_t xv[PW * RSX];    // X~^T (swizzled)
+  __shared__ __attribute__((aligned(16))) lds_t Hs[PW * RSB];    // incoming state rows
+  __shared__ __attribute__((aligned(16))) float s_c[CS];
+  __shared__ __attribute__((aligned(16))) float s_d[CS];
 
-  const int h = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, li = lane & 15, kg = lane >> 4;
-  const int hpg = p.H / p.G, g = h / hpg;
-  const int tiles[2] = {wave, NT - 1 - wave};
+  const int h = blockIdx.x, r = blockIdx.y, p0 = blockIdx.z * PW, tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, li = lane & 15, kg = lane >> 4;
+  const int g = h / (p.H / p.G);
 
   // the sequence's chunks; all of them are checked before anything is read or written
   const int k0 = r == 0 ? 0 : p.last_chunk[r - 1] + 1;
@@ -481,212 +439,281 @@ __global__ __launch_bounds__(CS * 2) void k_chunk_march(PrefillParams p) {
       slot = -1;
     }
   }
-  float* pool_h = slot >= 0 ? p.pool + int64_t(slot) * p.slot_stride + int64_t(h) * P * N : nullptr;
+  float* pool_h = slot >= 0 ? p.pool + int64_t(slot) * p.slot_stride + (int64_t(h) * P + p0) * N
+                            : nullptr;
 
-  // the state: lane holds H[pt*16 + 4*kg + rr][nt*16 + li] for its n-tiles nt = wave + NW*q
-  f32x4_v hreg[NTW][TP];
+  // the state slice: lane holds H[p0 + pt*16 + 4*kg + rr][nt*16 + li], nt = wave*TNW + q
+  f32x4_v hreg[TNW][TPW];
   const bool init = pool_h && p.has_init && p.has_init[r];
 #pragma unroll
-  for (int q = 0; q < NTW; ++q)
+  for (int q = 0; q < TNW; ++q)
 #pragma unroll
-    for (int pt = 0; pt < TP; ++pt)
+    for (int pt = 0; pt < TPW; ++pt)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        const int nt = wave + NW * q;
-        hreg[q][pt][rr] = (init && nt < TN)
-                              ? pool_h[(pt * 16 + 4 * kg + rr) * N + nt * 16 + li]
-                              : 0.f;
+        const int nt = wave * TNW + q;
+        hreg[q][pt][rr] = (init && nt < TN) ? pool_h[(pt * 16 + 4 * kg + rr) * N + nt * 16 + li]
+                                            : 0.f;
       }
 
-  const float Ah = p.A[h];
   const float Dh = p.D ? p.D[h] : 0.f;
-  MarchFrags<T, P, N, CS> f;
-  ChunkLoc cur{p.cu_chunk[k0], p.cu_chunk[k0 + 1] - p.cu_chunk[k0]};
-  march_load_x(f, p, cur, h);
 
+  StageIn<T, M::NI> st;
+  ChunkLoc cur{ld_meta(p.cu_chunk, k0), ld_meta(p.cu_chunk, k0 + 1) - ld_meta(p.cu_chunk, k0)};
+  march_load_stage<T, P, PW, N, CS>(st, p, cur, k0, h, p0);
+
+  const int64_t grp = int64_t(g);
   for (int k = k0; k <= k1; ++k) {
     const int L = cur.L, cs0 = cur.cs0;
     const bool more = k < k1;
-    const ChunkLoc nxt = more ? ChunkLoc{p.cu_chunk[k + 1], p.cu_chunk[k + 2] - p.cu_chunk[k + 1]}
-                              : cur;
+    ChunkLoc nxt = cur;
+    if (more) {
+      const int e0 = ld_meta(p.cu_chunk, k + 1), e1 = ld_meta(p.cu_chunk, k + 2);
+      nxt = ChunkLoc{e0, e1 - e0};
+    }
     __syncthreads();   // the previous chunk is done with every LDS buffer
-    // L2-resident operands of this chunk; the scan and the staging below cover their latency
-    march_load_bt(f, p, k, g);
-    march_load_cb(f, p, cur, k, g, tiles);
 
-    // incoming state as bf16 for the inter-chunk MFMA
+    // B^T fragments of this wave's n-tiles (L2-resident) for the state update below: a
+    // ring of BTR steps, the first BTR - 1 requested here
+    const T* btk = static_cast<const T*>(p.btw) + (int64_t(k) * p.G + grp) * (int64_t(N) * CS);
+    constexpr int BTR = SSD_MARCH_BT_RING < NSTEP ? SSD_MARCH_BT_RING : NSTEP;
+    frag btf[BTR][TNW];
+    auto load_bt = [&](int ss) {
 #pragma unroll
-    for (int q = 0; q < NTW; ++q) {
-      const int nt = wave + NW * q;
-      if (nt >= TN) continue;
+      for (int q = 0; q < TNW; ++q) {
+        const int nt = wave * TNW + q < TN ? wave * TNW + q : TN - 1;
+        btf[ss % BTR][q] = O::gld8u(btk + ((int64_t(nt) * NSTEP + ss) * 64 + lane) * 8);
+      }
+    };
 #pragma unroll
-      for (int pt = 0; pt < TP; ++pt)
+    for (int ss = 0; ss < BTR - 1; ++ss) load_bt(ss);
+
+    // incoming state as MFMA operand rows
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) Hs[(pt * 16 + 4 * kg + rr) * RSB + nt * 16 + li] = O::cvt(hreg[q][pt][rr]);
+    for (int q = 0; q < TNW; ++q) {
+      const int nt = wave * TNW + q;
+      if (TN % NW != 0 && nt >= TN) continue;
+#pragma unroll
+      for (int pt = 0; pt < TPW; ++pt)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          Hs[(pt * 16 + 4 * kg + rr) * RSB + nt * 16 + li] = O::cvt(hreg[q][pt][rr]);
     }
     if constexpr (NP > N) {   // the padding columns of H must be zero for the K=32 MFMA
-      for (int e = tid; e < P * (NP - N); e += NTH)
+      for (int e = tid; e < PW * (NP - N); e += NTH)
         Hs[(e / (NP - N)) * RSB + N + e % (NP - N)] = O::cvt(0.f);
     }
 
-    // delta, cumsum, staging scale
-    const float d = tid < L ? p.prep(to_f32(f.dt), h) : 0.f;
-    const float c = block_inclusive_scan(d * Ah, s_scan);
-    if (tid < CS) {
-      s_c[tid] = c;
-      s_d[tid] = d;
+    // staging: raw x^T and X~^T, cumsum and delta
+#pragma unroll
+    for (int u = 0; u < M::NI; ++u) {
+      const int it = u * NTH + tid;
+      if (it >= M::NITEM) break;
+      const int g8 = it % M::NG, s = 4 * (it / M::NG);
+      const float cv[4] = {st.c[u].x, st.c[u].y, st.c[u].z, st.c[u].w};
+      const float dv[4] = {st.d[u].x, st.d[u].y, st.d[u].z, st.d[u].w};
+      float v[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) v[t] = dv[t] * fast_exp(st.cref[u] - cv[t]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int col = 8 * g8 + j;
+        O::put4raw(&xT[col * RSX + xsw(col, s)], st.x[u], j);
+        O::put4(&xv[col * RSX + xsw(col, s)], st.x[u], j, v);
+      }
+      if (g8 == 0) {
+        *reinterpret_cast<float4_v*>(&s_c[s]) = st.c[u];
+        *reinterpret_cast<float4_v*>(&s_d[s]) = st.d[u];
+      }
     }
     __syncthreads();
-    if (tid < CS) {
-      const int ref = (tid | 31) < CS ? (tid | 31) : CS - 1;
-      s_v[tid] = d * fast_exp(s_c[ref] - c);
-    }
-    if (tid < L && p.dA_cumsum_out) p.dA_cumsum_out[int64_t(h) * p.T + cs0 + tid] = c;
-    __syncthreads();
-    stage_store<T, P, CS, RSX, NTH>(f.x, xT, nullptr, xv, s_v);
-    __syncthreads();
-    const float c_last = s_c[L - 1];
-    if (more) march_load_x(f, p, nxt, h);
+    if (more) march_load_stage<T, P, PW, N, CS>(st, p, nxt, k + 1, h, p0);
 
     // the chunk's own state X~^T B^T with the running block rescale
-    f32x4_v sacc[NTW][TP];
+    f32x4_v sacc[TNW][TPW];
 #pragma unroll
-    for (int q = 0; q < NTW; ++q)
+    for (int q = 0; q < TNW; ++q)
 #pragma unroll
-      for (int pt = 0; pt < TP; ++pt) sacc[q][pt] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+      for (int pt = 0; pt < TPW; ++pt) sacc[q][pt] = f32x4_v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ss = 0; ss < NSTEP; ++ss) {
+      if (ss + BTR - 1 < NSTEP) load_bt(ss + BTR - 1);
       if (ss > 0) {
         const float al = fast_exp(s_c[32 * ss + 31] - s_c[32 * ss - 1]);
 #pragma unroll
-        for (int q = 0; q < NTW; ++q)
+        for (int q = 0; q < TNW; ++q)
 #pragma unroll
-          for (int pt = 0; pt < TP; ++pt) sacc[q][pt] *= al;
+          for (int pt = 0; pt < TPW; ++pt) sacc[q][pt] *= al;
       }
-      frag a[TP];
 #pragma unroll
-      for (int pt = 0; pt < TP; ++pt) a[pt] = O::ld8(&xv[(pt * 16 + li) * RSX + 32 * ss + 8 * kg]);
+      for (int pt = 0; pt < TPW; ++pt) {
+        const int pr = pt * 16 + li;
+        const frag a = O::ld8(&xv[pr * RSX + xsw(pr, 32 * ss + 8 * kg)]);
 #pragma unroll
-      for (int q = 0; q < NTW; ++q) {
-        if (TN % NW == 0 || wave + NW * q < TN) {
-#pragma unroll
-          for (int pt = 0; pt < TP; ++pt) sacc[q][pt] = O::mma(a[pt], f.bt[ss][q], sacc[q][pt]);
-        }
+        for (int q = 0; q < TNW; ++q)
+          if (TN % NW == 0 || wave * TNW + q < TN) sacc[q][pt] = O::mma(a, btf[ss % BTR][q], sacc[q][pt]);
       }
     }
     // H_out = exp(c_last) H_in + S_k: the checkpoint at the chunk end
-    const float dec = fast_exp(c_last);
-    const int64_t cbase = (int64_t(k) * p.H + h) * (P * N);
+    const float dec = fast_exp(s_c[CS - 1]);
 #pragma unroll
-    for (int q = 0; q < NTW; ++q) {
-      const int nt = wave + NW * q;
-      if (nt >= TN) continue;
+    for (int q = 0; q < TNW; ++q)
 #pragma unroll
-      for (int pt = 0; pt < TP; ++pt) {
-        hreg[q][pt] = dec * hreg[q][pt] + sacc[q][pt];
+      for (int pt = 0; pt < TPW; ++pt) hreg[q][pt] = dec * hreg[q][pt] + sacc[q][pt];
+    const int64_t sbase = (int64_t(k) * p.H + h) * (int64_t(P) * N) + int64_t(p0) * N;
+    if (p.states) {
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int e = (pt * 16 + 4 * kg + rr) * N + nt * 16 + li;
-          if (p.states) p.states[cbase + e] = hreg[q][pt][rr];
-          if (p.local_states_out) p.local_states_out[cbase + e] = sacc[q][pt][rr];
-        }
+      for (int q = 0; q < TNW; ++q) {
+        const int nt = wave * TNW + q;
+        if (TN % NW != 0 && nt >= TN) continue;
+#pragma unroll
+        for (int pt = 0; pt < TPW; ++pt)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            p.states[sbase + (pt * 16 + 4 * kg + rr) * N + nt * 16 + li] = hreg[q][pt][rr];
       }
     }
-    march_load_c(f, p, cur, g, tiles);
+    if (p.local_states_out) {
+#pragma unroll
+      for (int q = 0; q < TNW; ++q) {
+        const int nt = wave * TNW + q;
+        if (TN % NW != 0 && nt >= TN) continue;
+#pragma unroll
+        for (int pt = 0; pt < TPW; ++pt)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            p.local_states_out[sbase + (pt * 16 + 4 * kg + rr) * N + nt * 16 + li] = sacc[q][pt][rr];
+      }
+    }
 
-    // y, one 16-row tile at a time: inter-chunk term, intra-chunk terms, skip connection,
-    // then whole rows out through the wave's staging tile
-    T* ybase = static_cast<T*>(p.y) + int64_t(cs0) * p.y_st + int64_t(h) * P;
-    lds_t* yst = ystage + wave * 16 * RSY;
+    // y^T, PT row tiles at a time: tiles 8*pr + w and 8*pr + 7 - w
+    const T* cbk = static_cast<const T*>(p.cbw) + (int64_t(k) * p.G + grp) * (int64_t(NF) * 512);
+    const T* crow = static_cast<const T*>(p.Cm) + int64_t(cs0) * p.bc_st + grp * N;
+    T* ybase = static_cast<T*>(p.y) + int64_t(cs0) * p.y_st + int64_t(h) * P + p0;
+#pragma unroll SSD_MARCH_PAIR_UNROLL
+    for (int pr = 0; pr < NPAIR; ++pr) {
+      int ti[PT], bd[PT];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int i = tiles[q];
-      if (16 * i >= L) continue;
-      const int l0 = 16 * i, lrow = l0 + li, bd = i / 2;
-      // inter-chunk term: exp(c_l) C_l . H_in[p, :]
-      f32x4_v acc[TP];
-#pragma unroll
-      for (int pt = 0; pt < TP; ++pt) acc[pt] = f32x4_v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < KN; ++kk) {
-#pragma unroll
-        for (int pt = 0; pt < TP; ++pt)
-          acc[pt] = O::mma(f.cf[q][kk], O::ld8(&Hs[(pt * 16 + li) * RSB + 32 * kk + 8 * kg]), acc[pt]);
+      for (int t = 0; t < PT; ++t) {
+        ti[t] = __builtin_amdgcn_readfirstlane(8 * pr + (t ? 7 - wave : wave));
+        bd[t] = ti[t] / 2;
       }
+      // C rows of the tiles as B operands (column l, contracted n)
+      frag cf[PT][KN];
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const float e = fast_exp(s_c[l0 + 4 * kg + rr]);
+      for (int t = 0; t < PT; ++t) {
+        const int l = 16 * ti[t] + li < L ? 16 * ti[t] + li : L - 1;
 #pragma unroll
-        for (int pt = 0; pt < TP; ++pt) acc[pt][rr] *= e;
-      }
-      // blocks entirely before this tile, with the running rescale
-      if (bd > 0) {
-        f32x4_v acc2[TP];
-#pragma unroll
-        for (int pt = 0; pt < TP; ++pt) acc2[pt] = f32x4_v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int b = 0; b < F1 - 1; ++b) {
-          if (b >= bd || (q == 0 && b >= F0 - 1)) break;
-          if (b > 0) {
-            const float al = fast_exp(s_c[32 * b + 31] - s_c[32 * b - 1]);
-#pragma unroll
-            for (int pt = 0; pt < TP; ++pt) acc2[pt] *= al;
-          }
-          const frag& a = q == 0 ? f.cb0[b] : f.cb1[b];
-#pragma unroll
-          for (int pt = 0; pt < TP; ++pt) {
-            const lds_t* xr = &xv[(pt * 16 + li) * RSX + 32 * b + 4 * kg];
-            acc2[pt] = O::mma(a, O::ld44(xr, xr + 16), acc2[pt]);
-          }
-        }
-        const float cref = s_c[32 * bd - 1];
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const float fct = fast_exp(s_c[l0 + 4 * kg + rr] - cref);
-#pragma unroll
-          for (int pt = 0; pt < TP; ++pt) acc[pt][rr] += fct * acc2[pt][rr];
+        for (int kk = 0; kk < KN; ++kk) {
+          const int col = 32 * kk + 8 * kg < N ? 32 * kk + 8 * kg : 0;
+          cf[t][kk] = O::gld8u(crow + int64_t(l) * p.bc_st + col);
         }
       }
-      // the block holding the diagonal: exact decay per element, causal mask
-      {
-        const int s0 = 32 * bd;
-        const frag& cbd = q == 0 ? f.cb0[F0 - 1] : f.cb1[F1 - 1];
-        const float c_l = s_c[lrow];
+      // the diagonal blocks' C.B^T fragments
+      frag cbd[PT];
+#pragma unroll
+      for (int t = 0; t < PT; ++t)
+        cbd[t] = O::gld8u(cbk + ((int64_t(cb_frag_base(ti[t]) + bd[t])) * 64 + lane) * 8);
+
+      // inter-chunk term: exp(c_l) H_in[p, :] . C_l
+      f32x4_v acc[PT][TPW];
+#pragma unroll
+      for (int t = 0; t < PT; ++t)
+#pragma unroll
+        for (int pt = 0; pt < TPW; ++pt) acc[t][pt] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KN; ++kk)
+#pragma unroll
+        for (int pt = 0; pt < TPW; ++pt) {
+          const frag hf = O::ld8(&Hs[(pt * 16 + li) * RSB + 32 * kk + 8 * kg]);
+#pragma unroll
+          for (int t = 0; t < PT; ++t) acc[t][pt] = O::mma(hf, cf[t][kk], acc[t][pt]);
+        }
+#pragma unroll
+      for (int t = 0; t < PT; ++t) {
+        const float e = fast_exp(s_c[16 * ti[t] + li]);
+#pragma unroll
+        for (int pt = 0; pt < TPW; ++pt) acc[t][pt] *= e;
+      }
+
+      // blocks entirely before each tile's diagonal block, with the running rescale
+      const int bmax = bd[PT - 1] > bd[0] ? bd[PT - 1] : bd[0];
+      if (bmax > 0) {
+        f32x4_v acc2[PT][TPW];
+#pragma unroll
+        for (int t = 0; t < PT; ++t)
+#pragma unroll
+          for (int pt = 0; pt < TPW; ++pt) acc2[t][pt] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+        frag cbn[PT];
+#pragma unroll
+        for (int t = 0; t < PT; ++t) cbn[t] = O::gld8u(cbk + (int64_t(cb_frag_base(ti[t])) * 64 + lane) * 8);
+#pragma unroll
+        for (int b = 0; b < NT / 2 - 1; ++b) {
+          if (b >= bmax) break;
+          frag cbb[PT];
+#pragma unroll
+          for (int t = 0; t < PT; ++t) {
+            cbb[t] = cbn[t];
+            // the next block's fragment (clamped to the tile's own blocks)
+            const int bn = b + 1 < bd[t] ? b + 1 : (bd[t] > 0 ? bd[t] - 1 : 0);
+            cbn[t] = O::gld8u(cbk + (int64_t(cb_frag_base(ti[t]) + bn) * 64 + lane) * 8);
+          }
+          const float al = b > 0 ? fast_exp(s_c[32 * b + 31] - s_c[32 * b - 1]) : 1.f;
+#pragma unroll
+          for (int pt = 0; pt < TPW; ++pt) {
+            const int prow = pt * 16 + li;
+            const frag xf = O::ld8(&xv[prow * RSX + xsw(prow, 32 * b + 8 * kg)]);
+#pragma unroll
+            for (int t = 0; t < PT; ++t) {
+              if (b < bd[t]) acc2[t][pt] = O::mma(xf, cbb[t], acc2[t][pt] * al);
+            }
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < PT; ++t) {
+          if (bd[t] == 0) continue;
+          const float f = fast_exp(s_c[16 * ti[t] + li] - s_c[32 * bd[t] - 1]);
+#pragma unroll
+          for (int pt = 0; pt < TPW; ++pt) acc[t][pt] += f * acc2[t][pt];
+        }
+      }
+
+      // the block holding the diagonal: exact decay per element, causal mask, D on the
+      // diagonal
+#pragma unroll
+      for (int t = 0; t < PT; ++t) {
+        const int s0 = 32 * bd[t], l = 16 * ti[t] + li;
+        const float cl = s_c[l];
+        const float4_v c0 = *reinterpret_cast<const float4_v*>(&s_c[s0 + 8 * kg]);
+        const float4_v c1 = *reinterpret_cast<const float4_v*>(&s_c[s0 + 8 * kg + 4]);
+        const float4_v d0 = *reinterpret_cast<const float4_v*>(&s_d[s0 + 8 * kg]);
+        const float4_v d1 = *reinterpret_cast<const float4_v*>(&s_d[s0 + 8 * kg + 4]);
+        const float cs8[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+        const float ds8[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
         float m[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const int sj = s0 + (j < 4 ? 4 * kg + j : 16 + 4 * kg + (j - 4));
-          const float val = O::val(cbd, j) * fast_exp(c_l - s_c[sj]) * s_d[sj];
-          m[j] = sj <= lrow ? val : 0.f;
+          const int s = s0 + 8 * kg + j;
+          const float v = O::val(cbd[t], j) * fast_exp(cl - cs8[j]) * ds8[j] + (s == l ? Dh : 0.f);
+          m[j] = s <= l ? v : 0.f;
         }
         const frag mf = O::from8(m);
 #pragma unroll
-        for (int pt = 0; pt < TP; ++pt) {
-          const lds_t* xr = &xT[(pt * 16 + li) * RSX + s0 + 4 * kg];
-          acc[pt] = O::mma(mf, O::ld44(xr, xr + 16), acc[pt]);
+        for (int pt = 0; pt < TPW; ++pt) {
+          const int prow = pt * 16 + li;
+          acc[t][pt] = O::mma(O::ld8(&xT[prow * RSX + xsw(prow, s0 + 8 * kg)]), mf, acc[t][pt]);
         }
       }
-      // skip connection, then the tile leaves as whole rows
+      // y^T tile out: lane holds p = pt*16 + 4*kg + 0..3 of token l
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int l = l0 + 4 * kg + rr;
+      for (int t = 0; t < PT; ++t) {
+        const int l = 16 * ti[t] + li;
+        if (l < L) {
 #pragma unroll
-        for (int pt = 0; pt < TP; ++pt) {
-          const float yv = acc[pt][rr] + Dh * O::tof(xT[(pt * 16 + li) * RSX + l]);
-          yst[(4 * kg + rr) * RSY + pt * 16 + li] = O::cvt(yv);
+          for (int pt = 0; pt < TPW; ++pt)
+            O::st4(ybase + int64_t(l) * p.y_st + pt * 16 + 4 * kg, acc[t][pt]);
         }
       }
-      wave_lds_sync();
-      constexpr int EPC = 16 / sizeof(T);          // elements per 16 B
-      constexpr int CPR = P / EPC;                 // 16 B pieces per row
-      for (int e = lane; e < 16 * CPR; e += 64) {
-        const int row = e / CPR, piece = e % CPR;
-        if (l0 + row < L) {
-          *reinterpret_cast<u32x4_v*>(ybase + int64_t(l0 + row) * p.y_st + piece * EPC) =
-              *reinterpret_cast<const u32x4_v*>(&yst[row * RSY + piece * EPC]);
-        }
-      }
-      wave_lds_sync();
     }
 
     cur = nxt;
@@ -695,11 +722,11 @@ __global__ __launch_bounds__(CS * 2) void k_chunk_march(PrefillParams p) {
   // final state back to the pool slot (read at the start by this same workgroup)
   if (pool_h && p.write_final) {
 #pragma unroll
-    for (int q = 0; q < NTW; ++q) {
-      const int nt = wave + NW * q;
+    for (int q = 0; q < TNW; ++q) {
+      const int nt = wave * TNW + q;
       if (nt >= TN) continue;
 #pragma unroll
-      for (int pt = 0; pt < TP; ++pt)
+      for (int pt = 0; pt < TPW; ++pt)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr)
           pool_h[(pt * 16 + 4 * kg + rr) * N + nt * 16 + li] = hreg[q][pt][rr];
@@ -712,11 +739,15 @@ __global__ __launch_bounds__(CS * 2) void k_chunk_march(PrefillParams p) {
 // ---------------------------------------------------------------------------------------
 template <typename T, int P, int N, int CS>
 static hipError_t run_chunked(const PrefillParams& p, hipStream_t s, void* const* ev) {
+  constexpr int PW = P >= 32 ? 32 : P;
   record_event(ev, 0, s);
-  hipLaunchKernelGGL((k_chunk_prep<T, N, CS>), dim3(p.C, p.G, kPrepSplit), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((k_chunk_cumsum<T, CS>), dim3(p.C, (p.H + kCumHeads - 1) / kCumHeads),
+                     dim3(256), 0, s, p);
   record_event(ev, 1, s);
-  hipLaunchKernelGGL((k_chunk_march<T, P, N, CS>), dim3(p.H, p.S), dim3(CS * 2), 0, s, p);
+  hipLaunchKernelGGL((k_chunk_prep<T, N, CS>), dim3(p.C, p.G, kPrepSplit), dim3(256), 0, s, p);
   record_event(ev, 2, s);
+  hipLaunchKernelGGL((k_chunk_march<T, P, PW, N, CS>), dim3(p.H, p.S, P / PW), dim3(256), 0, s, p);
+  record_event(ev, 3, s);
   return hipGetLastError();
 }
 

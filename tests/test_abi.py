@@ -98,8 +98,12 @@ def _al(v):
 
 def test_workspace_size_layout():
     C, H, P, N, G, cs = 3, 8, 64, 128, 2, 256
-    # C.B^T [C,G,cs,cs] and B^T [C,G,N,cs] in the input dtype, shared by the heads of a group
-    prep = _al(C * G * cs * cs * 2) + _al(C * G * N * cs * 2)
+    # per (chunk, group) in the input dtype, shared by the heads of a group: the C.B^T
+    # fragments of the 16 row tiles (tile i needs i//2 + 1 fragments of 512 values) and
+    # B^T; per (chunk, head) fp32: the cumsum of delta*A and delta
+    nfrag = sum(i // 2 + 1 for i in range(cs // 16))
+    assert nfrag == 72
+    prep = _al(C * G * nfrag * 512 * 2) + _al(C * G * N * cs * 2) + _al(C * H * 2 * cs * 4)
     for over in ({}, dict(chunk_states_out=FAKE),
                  dict(chunk_states_out=FAKE, has_initial_state=FAKE, state_pool=FAKE,
                       state_indices=FAKE, num_slots=4, slot_stride=8 * 64 * 128)):
@@ -114,8 +118,8 @@ def test_kernel_count():
     n = ctypes.c_int32(-1)
     names = (ctypes.c_char_p * _abi.SSD_PREFILL_MAX_KERNELS)()
     assert lib().ssd_prefill_kernel_count(ctypes.byref(_good_prefill()), ctypes.byref(n), names) == 0
-    assert n.value == 2
-    assert [names[i] for i in range(2)] == [b"k_chunk_prep", b"k_chunk_march"]
+    assert n.value == 3
+    assert [names[i] for i in range(3)] == [b"k_chunk_cumsum", b"k_chunk_prep", b"k_chunk_march"]
     diag = _good_prefill(a_kind=_abi.SSD_A_DIAG, H=64, P=1, G=1, N=16, x_stride_t=64,
                          y_stride_t=64, dt_stride_t=64, bc_stride_t=16)
     assert lib().ssd_prefill_kernel_count(ctypes.byref(diag), ctypes.byref(n), names) == 0
