@@ -59,7 +59,7 @@ def prefill_work(inp, cuc, sidx):
     # per (chunk, 16 heads): read dt, write the cumsum of delta*A and delta (fp32)
     k_cum = dict(bytes=T * H * b + C * H * 2 * cs * 4, flops=0)
     # per (chunk, group): read B and C, write the C.B^T fragments and B^T
-    k_prep = dict(bytes=2 * T * G * N * b + C * G * (nfrag * 512 + N * cs) * b,
+    k_prep = dict(bytes=2 * T * G * N * b + C * G * (nfrag * 512 + 2 * N * cs) * b,
                   flops=sum(G * N * l * (l + 1) for l in lens))
     # per (head, sequence, half head dim): read x, C, the cumsum, the initial states; write y,
     # every chunk-end state and the final states (C.B^T and B^T come from the prep kernel
@@ -179,10 +179,12 @@ def bench_prefill(torch, name, steps, warmup, sets=4):
         d = {n: (t if i == 0 else t.clone()) for n, t in base.items()}
         d["y"] = torch.empty_like(d["x"])
         d["states"] = torch.empty(C, inp.H, inp.P, inp.N, dtype=torch.float32, device="cuda")
-        d["cu_seq"] = torch.empty(S + 1, dtype=torch.int32, device="cuda")
-        d["cu_chunk"] = torch.empty(C + 1, dtype=torch.int32, device="cuda")
-        d["seq_idx"] = torch.empty(C, dtype=torch.int32, device="cuda")
-        d["last"] = torch.empty(S, dtype=torch.int32, device="cuda")
+        # the four metadata arrays packed in one device buffer, filled by one copy per step
+        d["meta"] = torch.empty(S + 1 + C + 1 + C + S, dtype=torch.int32, device="cuda")
+        d["cu_seq"] = d["meta"][:S + 1]
+        d["cu_chunk"] = d["meta"][S + 1:S + C + 2]
+        d["seq_idx"] = d["meta"][S + C + 2:S + 2 * C + 2]
+        d["last"] = d["meta"][S + 2 * C + 2:]
         d["host"] = torch.empty(S + 1 + C + 1 + C + S, dtype=torch.int32).pin_memory()
         bufs.append(d)
     args = [api.prefill_args(d["x"], d["dt"], A, d["B"], d["C"], inp.chunk_size, d["cu_seq"],
@@ -207,11 +209,7 @@ def bench_prefill(torch, name, steps, warmup, sets=4):
         h = d["host"].numpy()
         h[:S + 1], h[S + 1:S + C + 2] = cu_np, c2
         h[S + C + 2:S + 2 * C + 2], h[S + 2 * C + 2:] = s2, l2
-        hd = d["host"].cuda(non_blocking=True)
-        d["cu_seq"].copy_(hd[:S + 1])
-        d["cu_chunk"].copy_(hd[S + 1:S + C + 2])
-        d["seq_idx"].copy_(hd[S + C + 2:S + 2 * C + 2])
-        d["last"].copy_(hd[S + 2 * C + 2:])
+        d["meta"].copy_(d["host"], non_blocking=True)
         a.profile_events = None if evs is None else ctypes.cast(evs, ctypes.c_void_p)
         check("ssd_prefill", lib().ssd_prefill(ctypes.byref(a), ws.data_ptr(), ws.numel(), sp))
 

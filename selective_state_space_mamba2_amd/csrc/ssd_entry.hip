@@ -78,6 +78,8 @@ ssd_status ssd_prefill(const ssd_prefill_args* a, void* workspace, size_t worksp
     p.cbw = ws + plan.off_cb;
     p.btw = ws + plan.off_bt;
     p.dcw = reinterpret_cast<float*>(ws + plan.off_dc);
+    p.cfw = ws + plan.off_cf;
+    p.seq_ord = reinterpret_cast<int*>(ws + plan.off_ord);
   }
 
   const hipStream_t s = static_cast<hipStream_t>(stream);

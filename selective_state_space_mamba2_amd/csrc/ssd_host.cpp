@@ -92,6 +92,10 @@ ssd_status plan_prefill(const ssd_prefill_args* a, PrefillPlan* plan) {
   off = align_up(off + size_t(C) * a->G * a->N * cs * esz, 256);
   plan->off_dc = off;
   off = align_up(off + size_t(C) * a->H * 2 * cs * sizeof(float), 256);
+  plan->off_cf = off;
+  off = align_up(off + size_t(C) * a->G * cs * size_t(a->N < 32 ? 32 : a->N) * esz, 256);
+  plan->off_ord = off;
+  off = align_up(off + size_t(a->num_seqs) * sizeof(int32_t), 256);
   plan->ws_bytes = off;
   return SSD_OK;
 }

@@ -33,6 +33,8 @@ struct PrefillParams {
   void* cbw;           // workspace, input dtype: C.B^T fragments per chunk and group
   void* btw;           // workspace, input dtype: B^T fragments per chunk and group
   float* dcw;          // workspace [C, H, 2, cs]: cumsum of delta*A, then delta
+  void* cfw;           // workspace, input dtype: C fragments per chunk and group
+  int* seq_ord;        // workspace [S]: sequences in march dispatch order
   int* flag;
   float* dA_cumsum_out;
   float* cb_out;

@@ -21,6 +21,8 @@ struct PrefillPlan {
                              // row tile, cb_frag_base(cs/16) fragments of 512 values
   size_t off_bt = 0;         // input dtype [C, G, N * cs]: B^T per chunk and group
   size_t off_dc = 0;         // fp32 [C, H, 2, cs]: cumsum of delta*A, then delta
+  size_t off_cf = 0;         // input dtype [C, G, cs * max(N, 32)]: C rows as fragments
+  size_t off_ord = 0;        // int32 [S]: sequence dispatch order of the march kernel
 };
 
 // C.B^T fragments of the 16-row tiles 0..i-1 of a chunk: tile i needs the 32-token blocks

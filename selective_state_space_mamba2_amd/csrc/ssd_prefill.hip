@@ -67,6 +67,8 @@ template <> struct Ops<bf16_t> {
   static __device__ __forceinline__ f32x4_v mma(const frag& a, const frag& b, f32x4_v c) {
     return mma_bf16(a, b, c);
   }
+  // four fp32 values -> 4 consecutive LDS elements
+  static __device__ __forceinline__ void st4lds(lds_t* q, f32x4_v v) { st4(q, v); }
   static __device__ __forceinline__ lds_t cvt(float v) { return f32_to_bf16(v); }
   static __device__ __forceinline__ float val(const frag& f, int j) {
     return bf16_to_f32(bf16_t(f.w[j >> 1] >> ((j & 1) * 16)));
@@ -113,6 +115,7 @@ template <> struct Ops<float> {
   static __device__ __forceinline__ f32x4_v mma(const frag& a, const frag& b, f32x4_v c) {
     return mma_f32(a, b, c);
   }
+  static __device__ __forceinline__ void st4lds(lds_t* q, f32x4_v v) { st4(q, v); }
   static __device__ __forceinline__ lds_t cvt(float v) { return v; }
   static __device__ __forceinline__ float val(const frag& f, int j) { return f.v[j]; }
   static __device__ __forceinline__ void put4(lds_t* d, const frag* v, int j, const float* sc) {
@@ -123,6 +126,44 @@ template <> struct Ops<float> {
     *reinterpret_cast<float4_v*>(d) = float4_v{v[0].v[j], v[1].v[j], v[2].v[j], v[3].v[j]};
   }
 };
+
+// Raw buffer resource over a wave-uniform base (gfx9 descriptor: 32-bit data format, no
+// swizzle): loads through it take a scalar offset plus one 32-bit vector offset, so the
+// per-load address math is a scalar add.  Offsets must stay below 2^31 bytes.
+struct BufRes {
+  __amdgpu_buffer_rsrc_t r;
+  __device__ __forceinline__ explicit BufRes(const void* base)
+      : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff,
+                                            0x00020000)) {}
+  __device__ __forceinline__ u32x4_v ld16(uint32_t voff, uint32_t soff) const {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  }
+};
+
+// 8 consecutive elements at byte offset voff + soff of a buffer
+template <typename T>
+__device__ __forceinline__ typename Ops<T>::frag buf_ld8(const BufRes& b, uint32_t voff, uint32_t soff) {
+  if constexpr (sizeof(T) == 2) {
+    const u32x4_v v = b.ld16(voff, soff);
+    return Frag8{{v.x, v.y, v.z, v.w}};
+  } else {
+    const u32x4_v v0 = b.ld16(voff, soff), v1 = b.ld16(voff + 16, soff);
+    return Frag8f{{__uint_as_float(v0.x), __uint_as_float(v0.y), __uint_as_float(v0.z),
+                   __uint_as_float(v0.w), __uint_as_float(v1.x), __uint_as_float(v1.y),
+                   __uint_as_float(v1.z), __uint_as_float(v1.w)}};
+  }
+}
+
+// Fragment f (64 lanes x 8 values, stored contiguously) of a buffer; lane_b = this lane's
+// byte offset inside a fragment.
+template <typename T>
+__device__ __forceinline__ typename Ops<T>::frag ld_frag(const BufRes& b, int f, uint32_t lane_b) {
+  return buf_ld8<T>(b, lane_b, uint32_t(f) * (512 * sizeof(T)));
+}
+
+__device__ __forceinline__ void st_f4(float* q, f32x4_v v) {
+  *reinterpret_cast<float4_v*>(q) = float4_v{v[0], v[1], v[2], v[3]};
+}
 
 // Chunk k's token range and sequence; false if the metadata is bad.
 __device__ __forceinline__ bool chunk_bounds(const PrefillParams& p, int k, int cs_max,
@@ -156,11 +197,36 @@ __device__ __forceinline__ int xsw(int p, int s) { return s ^ (((p >> 3) & 3) <<
 // ---------------------------------------------------------------------------------------
 constexpr int kCumHeads = 16;   // heads per workgroup (4 per wavefront)
 
+// The march kernel walks each sequence's chunks in order, so a long sequence is a serial
+// chain: its workgroups are dispatched first (longest first, ties by index) so the chain
+// starts at once and shorter sequences fill the remaining slots.  The order is computed by
+// one workgroup of k_chunk_cumsum (a rank count over at most kOrderMaxSeqs sequences;
+// larger batches keep the given order).
+constexpr int kOrderMaxSeqs = 1024;
+
+__device__ __forceinline__ void sequence_order(const PrefillParams& p, int* nch) {
+  const int S = p.S;
+  for (int r = threadIdx.x; r < S; r += blockDim.x)
+    nch[r] = p.last_chunk[r] - (r == 0 ? -1 : p.last_chunk[r - 1]);
+  __syncthreads();
+  for (int r = threadIdx.x; r < S; r += blockDim.x) {
+    const int n = nch[r];
+    int rank = 0;
+    for (int q = 0; q < S; ++q) {
+      const int m = nch[q];
+      rank += (m > n) || (m == n && q < r);
+    }
+    p.seq_ord[rank] = r;
+  }
+}
+
 template <typename T, int CS>
 __global__ __launch_bounds__(256) void k_chunk_cumsum(PrefillParams p) {
   static_assert(CS <= 256 && CS % 4 == 0, "chunk size");
+  __shared__ int nch[kOrderMaxSeqs];
   const int k = blockIdx.x, tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  if (k == 0 && blockIdx.y == 0 && p.S <= kOrderMaxSeqs) sequence_order(p, nch);
   int cs0, L, r;
   if (!chunk_bounds(p, k, CS, cs0, L, r)) {
     if (tid == 0 && blockIdx.y == 0) raise_flag(p.flag, SSD_DEVERR_CHUNK_RANGE);
@@ -208,6 +274,8 @@ __global__ __launch_bounds__(256) void k_chunk_cumsum(PrefillParams p) {
 //     [n = 16 nt + li]; stored at ((chunk * G + g) * TN + nt) * NSTEP + ss.
 //   C.B^T fragment (row tile i, block b <= i/2): lane (kg, li) holds (C_l . B_s) for
 //     l = 16 i + li, s = 32 b + 8 kg + j; stored at (chunk * G + g) * NF + cb_frag_base(i) + b.
+//   C fragment (row tile i, 32-wide dstate step kk): lane (kg, li) holds C[l = 16 i + li]
+//     [n = 32 kk + 8 kg + j] (zero past dstate); stored at ((chunk * G + g) * NT + i) * KN + kk.
 // Rows past the chunk end are zero.  Work is split over kPrepSplit workgroups.
 // ---------------------------------------------------------------------------------------
 constexpr int kPrepSplit = 4;
@@ -274,10 +342,13 @@ __global__ __launch_bounds__(256) void k_chunk_prep(PrefillParams p) {
     if (i >= NT) continue;
     const int lrow = 16 * i + li;
     frag cf[KN];
+    T* cfo = static_cast<T*>(p.cfw) + ((int64_t(k) * p.G + g) * NT + i) * (KN * 512);
 #pragma unroll
-    for (int kk = 0; kk < KN; ++kk)
+    for (int kk = 0; kk < KN; ++kk) {
       cf[kk] = O::gld8(csrc + int64_t(lrow) * p.bc_st + 32 * kk + 8 * kg,
                        lrow < L && 32 * kk + 8 * kg < N);
+      O::st8(cfo + (kk * 64 + lane) * 8, cf[kk]);
+    }
 #pragma unroll 1
     for (int b = 0; b <= i / 2; ++b) {
 #pragma unroll
@@ -363,7 +434,8 @@ __device__ __forceinline__ void march_load_stage(StageIn<T, MarchCfg<T, P, PW, N
                                                  const PrefillParams& p, ChunkLoc c, int k,
                                                  int h, int p0) {
   using M = MarchCfg<T, P, PW, N, CS>;
-  const T* xsrc = static_cast<const T*>(p.x) + int64_t(c.cs0) * p.x_st + int64_t(h) * P + p0;
+  const BufRes xr(static_cast<const T*>(p.x) + int64_t(c.cs0) * p.x_st + int64_t(h) * P + p0);
+  const uint32_t xrow_b = uint32_t(p.x_st * int64_t(sizeof(T)));
   const float* dc = p.dcw + (int64_t(k) * p.H + h) * (2 * CS);
 #pragma unroll
   for (int u = 0; u < M::NI; ++u) {
@@ -374,7 +446,7 @@ __device__ __forceinline__ void march_load_stage(StageIn<T, MarchCfg<T, P, PW, N
     for (int t = 0; t < 4; ++t) {
       // unguarded: rows past the chunk end repeat its last row (their weight is zero)
       const int row = s + t < c.L ? s + t : c.L - 1;
-      st.x[u][t] = Ops<T>::gld8u(xsrc + int64_t(row) * p.x_st + 8 * g8);
+      st.x[u][t] = buf_ld8<T>(xr, uint32_t(row) * xrow_b + uint32_t(g8) * 8 * sizeof(T), 0);
     }
     st.c[u] = *reinterpret_cast<const float4_v*>(dc + s);
     st.d[u] = *reinterpret_cast<const float4_v*>(dc + CS + s);
@@ -387,6 +459,9 @@ __device__ __forceinline__ void march_load_stage(StageIn<T, MarchCfg<T, P, PW, N
 #endif
 #ifndef SSD_MARCH_BT_RING
 #define SSD_MARCH_BT_RING 4
+#endif
+#ifndef SSD_MARCH_CB_RING
+#define SSD_MARCH_CB_RING 3
 #endif
 #ifndef SSD_MARCH_PAIR_UNROLL
 #define SSD_MARCH_PAIR_UNROLL 2
@@ -410,9 +485,19 @@ void k_chunk_march(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) float s_c[CS];
   __shared__ __attribute__((aligned(16))) float s_d[CS];
 
-  const int h = blockIdx.x, r = blockIdx.y, p0 = blockIdx.z * PW, tid = threadIdx.x;
+  // 1-D grid: the head-dim slice fastest, then the head, then the sequence in dispatch
+  // order (longest first when the order was computed)
+  constexpr int PS = P / PW;
+  const int wg = blockIdx.x, tid = threadIdx.x;
+  const int p0 = (wg % PS) * PW, h = (wg / PS) % p.H, ry = wg / (PS * p.H);
+  const int r = p.S <= kOrderMaxSeqs ? ld_meta(p.seq_ord, ry) : ry;
+  if (r < 0 || r >= p.S) {   // the order array comes from this launch's first kernel
+    if (tid == 0) raise_flag(p.flag, SSD_DEVERR_CHUNK_RANGE);
+    return;
+  }
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, li = lane & 15, kg = lane >> 4;
+  const uint32_t lane_b = uint32_t(lane) * 8 * sizeof(T);   // byte offset inside a fragment
   const int g = h / (p.H / p.G);
 
   // the sequence's chunks; all of them are checked before anything is read or written
@@ -442,19 +527,21 @@ void k_chunk_march(PrefillParams p) {
   float* pool_h = slot >= 0 ? p.pool + int64_t(slot) * p.slot_stride + (int64_t(h) * P + p0) * N
                             : nullptr;
 
-  // the state slice: lane holds H[p0 + pt*16 + 4*kg + rr][nt*16 + li], nt = wave*TNW + q
+  // the state slice, held transposed (the MFMA result layout of B^T X~): lane holds
+  // H[p0 + pt*16 + li][nt*16 + 4*kg + rr], nt = wave*TNW + q, i.e. 4 consecutive n of one row
   f32x4_v hreg[TNW][TPW];
   const bool init = pool_h && p.has_init && p.has_init[r];
 #pragma unroll
   for (int q = 0; q < TNW; ++q)
 #pragma unroll
-    for (int pt = 0; pt < TPW; ++pt)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int nt = wave * TNW + q;
-        hreg[q][pt][rr] = (init && nt < TN) ? pool_h[(pt * 16 + 4 * kg + rr) * N + nt * 16 + li]
-                                            : 0.f;
+    for (int pt = 0; pt < TPW; ++pt) {
+      const int nt = wave * TNW + q;
+      hreg[q][pt] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+      if (init && nt < TN) {
+        const float4_v v = *reinterpret_cast<const float4_v*>(pool_h + (pt * 16 + li) * N + nt * 16 + 4 * kg);
+        hreg[q][pt] = f32x4_v{v.x, v.y, v.z, v.w};
       }
+    }
 
   const float Dh = p.D ? p.D[h] : 0.f;
 
@@ -475,14 +562,14 @@ void k_chunk_march(PrefillParams p) {
 
     // B^T fragments of this wave's n-tiles (L2-resident) for the state update below: a
     // ring of BTR steps, the first BTR - 1 requested here
-    const T* btk = static_cast<const T*>(p.btw) + (int64_t(k) * p.G + grp) * (int64_t(N) * CS);
+    const BufRes btr(static_cast<const T*>(p.btw) + (int64_t(k) * p.G + grp) * (int64_t(N) * CS));
     constexpr int BTR = SSD_MARCH_BT_RING < NSTEP ? SSD_MARCH_BT_RING : NSTEP;
     frag btf[BTR][TNW];
     auto load_bt = [&](int ss) {
 #pragma unroll
       for (int q = 0; q < TNW; ++q) {
         const int nt = wave * TNW + q < TN ? wave * TNW + q : TN - 1;
-        btf[ss % BTR][q] = O::gld8u(btk + ((int64_t(nt) * NSTEP + ss) * 64 + lane) * 8);
+        btf[ss % BTR][q] = ld_frag<T>(btr, nt * NSTEP + ss, lane_b);
       }
     };
 #pragma unroll
@@ -494,10 +581,7 @@ void k_chunk_march(PrefillParams p) {
       const int nt = wave * TNW + q;
       if (TN % NW != 0 && nt >= TN) continue;
 #pragma unroll
-      for (int pt = 0; pt < TPW; ++pt)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          Hs[(pt * 16 + 4 * kg + rr) * RSB + nt * 16 + li] = O::cvt(hreg[q][pt][rr]);
+      for (int pt = 0; pt < TPW; ++pt) O::st4lds(&Hs[(pt * 16 + li) * RSB + nt * 16 + 4 * kg], hreg[q][pt]);
     }
     if constexpr (NP > N) {   // the padding columns of H must be zero for the K=32 MFMA
       for (int e = tid; e < PW * (NP - N); e += NTH)
@@ -527,7 +611,6 @@ void k_chunk_march(PrefillParams p) {
       }
     }
     __syncthreads();
-    if (more) march_load_stage<T, P, PW, N, CS>(st, p, nxt, k + 1, h, p0);
 
     // the chunk's own state X~^T B^T with the running block rescale
     f32x4_v sacc[TNW][TPW];
@@ -551,7 +634,7 @@ void k_chunk_march(PrefillParams p) {
         const frag a = O::ld8(&xv[pr * RSX + xsw(pr, 32 * ss + 8 * kg)]);
 #pragma unroll
         for (int q = 0; q < TNW; ++q)
-          if (TN % NW == 0 || wave * TNW + q < TN) sacc[q][pt] = O::mma(a, btf[ss % BTR][q], sacc[q][pt]);
+          if (TN % NW == 0 || wave * TNW + q < TN) sacc[q][pt] = O::mma(btf[ss % BTR][q], a, sacc[q][pt]);
       }
     }
     // H_out = exp(c_last) H_in + S_k: the checkpoint at the chunk end
@@ -568,9 +651,7 @@ void k_chunk_march(PrefillParams p) {
         if (TN % NW != 0 && nt >= TN) continue;
 #pragma unroll
         for (int pt = 0; pt < TPW; ++pt)
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr)
-            p.states[sbase + (pt * 16 + 4 * kg + rr) * N + nt * 16 + li] = hreg[q][pt][rr];
+          st_f4(p.states + sbase + (pt * 16 + li) * N + nt * 16 + 4 * kg, hreg[q][pt]);
       }
     }
     if (p.local_states_out) {
@@ -580,15 +661,13 @@ void k_chunk_march(PrefillParams p) {
         if (TN % NW != 0 && nt >= TN) continue;
 #pragma unroll
         for (int pt = 0; pt < TPW; ++pt)
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr)
-            p.local_states_out[sbase + (pt * 16 + 4 * kg + rr) * N + nt * 16 + li] = sacc[q][pt][rr];
+          st_f4(p.local_states_out + sbase + (pt * 16 + li) * N + nt * 16 + 4 * kg, sacc[q][pt]);
       }
     }
 
     // y^T, PT row tiles at a time: tiles 8*pr + w and 8*pr + 7 - w
-    const T* cbk = static_cast<const T*>(p.cbw) + (int64_t(k) * p.G + grp) * (int64_t(NF) * 512);
-    const T* crow = static_cast<const T*>(p.Cm) + int64_t(cs0) * p.bc_st + grp * N;
+    const BufRes cbr(static_cast<const T*>(p.cbw) + (int64_t(k) * p.G + grp) * (int64_t(NF) * 512));
+    const BufRes cfr(static_cast<const T*>(p.cfw) + (int64_t(k) * p.G + grp) * (int64_t(NT) * KN * 512));
     T* ybase = static_cast<T*>(p.y) + int64_t(cs0) * p.y_st + int64_t(h) * P + p0;
 #pragma unroll SSD_MARCH_PAIR_UNROLL
     for (int pr = 0; pr < NPAIR; ++pr) {
@@ -598,22 +677,27 @@ void k_chunk_march(PrefillParams p) {
         ti[t] = __builtin_amdgcn_readfirstlane(8 * pr + (t ? 7 - wave : wave));
         bd[t] = ti[t] / 2;
       }
+      // the next chunk's x rows and cumsum (the HBM stream), requested during the last pair
+      if (pr == NPAIR - 1 && more) march_load_stage<T, P, PW, N, CS>(st, p, nxt, k + 1, h, p0);
       // C rows of the tiles as B operands (column l, contracted n)
       frag cf[PT][KN];
 #pragma unroll
-      for (int t = 0; t < PT; ++t) {
-        const int l = 16 * ti[t] + li < L ? 16 * ti[t] + li : L - 1;
+      for (int t = 0; t < PT; ++t)
 #pragma unroll
-        for (int kk = 0; kk < KN; ++kk) {
-          const int col = 32 * kk + 8 * kg < N ? 32 * kk + 8 * kg : 0;
-          cf[t][kk] = O::gld8u(crow + int64_t(l) * p.bc_st + col);
-        }
-      }
-      // the diagonal blocks' C.B^T fragments
+        for (int kk = 0; kk < KN; ++kk)
+          cf[t][kk] = ld_frag<T>(cfr, ti[t] * KN + kk, lane_b);
+      // the diagonal blocks' C.B^T fragments, and the first CBR blocks before the diagonal
+      // (a ring refilled CBR blocks ahead; clamped requests re-read the diagonal block)
       frag cbd[PT];
 #pragma unroll
+      for (int t = 0; t < PT; ++t) cbd[t] = ld_frag<T>(cbr, cb_frag_base(ti[t]) + bd[t], lane_b);
+      constexpr int CBR = SSD_MARCH_CB_RING;
+      frag cbq[PT][CBR];
+#pragma unroll
       for (int t = 0; t < PT; ++t)
-        cbd[t] = O::gld8u(cbk + ((int64_t(cb_frag_base(ti[t]) + bd[t])) * 64 + lane) * 8);
+#pragma unroll
+        for (int j = 0; j < CBR; ++j)
+          cbq[t][j] = ld_frag<T>(cbr, cb_frag_base(ti[t]) + (j < bd[t] ? j : bd[t]), lane_b);
 
       // inter-chunk term: exp(c_l) H_in[p, :] . C_l
       f32x4_v acc[PT][TPW];
@@ -644,20 +728,9 @@ void k_chunk_march(PrefillParams p) {
         for (int t = 0; t < PT; ++t)
 #pragma unroll
           for (int pt = 0; pt < TPW; ++pt) acc2[t][pt] = f32x4_v{0.f, 0.f, 0.f, 0.f};
-        frag cbn[PT];
-#pragma unroll
-        for (int t = 0; t < PT; ++t) cbn[t] = O::gld8u(cbk + (int64_t(cb_frag_base(ti[t])) * 64 + lane) * 8);
 #pragma unroll
         for (int b = 0; b < NT / 2 - 1; ++b) {
           if (b >= bmax) break;
-          frag cbb[PT];
-#pragma unroll
-          for (int t = 0; t < PT; ++t) {
-            cbb[t] = cbn[t];
-            // the next block's fragment (clamped to the tile's own blocks)
-            const int bn = b + 1 < bd[t] ? b + 1 : (bd[t] > 0 ? bd[t] - 1 : 0);
-            cbn[t] = O::gld8u(cbk + (int64_t(cb_frag_base(ti[t]) + bn) * 64 + lane) * 8);
-          }
           const float al = b > 0 ? fast_exp(s_c[32 * b + 31] - s_c[32 * b - 1]) : 1.f;
 #pragma unroll
           for (int pt = 0; pt < TPW; ++pt) {
@@ -665,8 +738,13 @@ void k_chunk_march(PrefillParams p) {
             const frag xf = O::ld8(&xv[prow * RSX + xsw(prow, 32 * b + 8 * kg)]);
 #pragma unroll
             for (int t = 0; t < PT; ++t) {
-              if (b < bd[t]) acc2[t][pt] = O::mma(xf, cbb[t], acc2[t][pt] * al);
+              if (b < bd[t]) acc2[t][pt] = O::mma(xf, cbq[t][b % CBR], acc2[t][pt] * al);
             }
+          }
+#pragma unroll
+          for (int t = 0; t < PT; ++t) {
+            const int bn = b + CBR < bd[t] ? b + CBR : bd[t];
+            cbq[t][b % CBR] = ld_frag<T>(cbr, cb_frag_base(ti[t]) + bn, lane_b);
           }
         }
 #pragma unroll
@@ -726,10 +804,7 @@ void k_chunk_march(PrefillParams p) {
       const int nt = wave * TNW + q;
       if (nt >= TN) continue;
 #pragma unroll
-      for (int pt = 0; pt < TPW; ++pt)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          pool_h[(pt * 16 + 4 * kg + rr) * N + nt * 16 + li] = hreg[q][pt][rr];
+      for (int pt = 0; pt < TPW; ++pt) st_f4(pool_h + (pt * 16 + li) * N + nt * 16 + 4 * kg, hreg[q][pt]);
     }
   }
 }
@@ -746,7 +821,8 @@ static hipError_t run_chunked(const PrefillParams& p, hipStream_t s, void* const
   record_event(ev, 1, s);
   hipLaunchKernelGGL((k_chunk_prep<T, N, CS>), dim3(p.C, p.G, kPrepSplit), dim3(256), 0, s, p);
   record_event(ev, 2, s);
-  hipLaunchKernelGGL((k_chunk_march<T, P, PW, N, CS>), dim3(p.H, p.S, P / PW), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((k_chunk_march<T, P, PW, N, CS>), dim3(p.S * p.H * (P / PW)), dim3(256), 0,
+                     s, p);
   record_event(ev, 3, s);
   return hipGetLastError();
 }

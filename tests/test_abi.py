@@ -100,10 +100,13 @@ def test_workspace_size_layout():
     C, H, P, N, G, cs = 3, 8, 64, 128, 2, 256
     # per (chunk, group) in the input dtype, shared by the heads of a group: the C.B^T
     # fragments of the 16 row tiles (tile i needs i//2 + 1 fragments of 512 values) and
-    # B^T; per (chunk, head) fp32: the cumsum of delta*A and delta
+    # B^T; per (chunk, head) fp32: the cumsum of delta*A and delta; per (chunk, group): the
+    # C rows as fragments
     nfrag = sum(i // 2 + 1 for i in range(cs // 16))
     assert nfrag == 72
-    prep = _al(C * G * nfrag * 512 * 2) + _al(C * G * N * cs * 2) + _al(C * H * 2 * cs * 4)
+    S = 2
+    prep = (_al(C * G * nfrag * 512 * 2) + _al(C * G * N * cs * 2) + _al(C * H * 2 * cs * 4)
+            + _al(C * G * cs * N * 2) + _al(S * 4))
     for over in ({}, dict(chunk_states_out=FAKE),
                  dict(chunk_states_out=FAKE, has_initial_state=FAKE, state_pool=FAKE,
                       state_indices=FAKE, num_slots=4, slot_stride=8 * 64 * 128)):
