@@ -40,6 +40,18 @@ __global__ __launch_bounds__(256) void k_state_update(DecodeParams p) {
     return;
   }
 
+  // Gather the source state before any write; it is requested first so the 32 KB stream
+  // is in flight while the small per-token inputs are staged.
+  const int lane_q = tid % NQ, prow = tid / NQ;
+  const int64_t head_off = int64_t(h) * P * N;
+  const float4_v* src = reinterpret_cast<const float4_v*>(
+      p.pool + int64_t(idx_r[acc_tok - 1]) * p.slot_stride + head_off);
+  float4_v st[ITERS];
+#pragma unroll
+  for (int i = 0; i < ITERS; ++i) {
+    const int pr = i * RP + prow;
+    st[i] = pr < P ? src[pr * NQ + lane_q] : float4_v{0.f, 0.f, 0.f, 0.f};
+  }
   // Stage this row's token data for head h: x[ntok][P], B[ntok][N], C[ntok][N], delta.
   // B and C first: N is a multiple of 16, so their float4 reads stay 16-byte aligned.
   float* bs = lds;
@@ -64,17 +76,6 @@ __global__ __launch_bounds__(256) void k_state_update(DecodeParams p) {
   }
   if (tid < ntok) ds[tid] = p.prep(Elem<T>::load(dg + (int64_t(r) * ntok + tid) * H + h), h);
 
-  // Gather the source state before any write.
-  const int lane_q = tid % NQ, prow = tid / NQ;
-  const int64_t head_off = int64_t(h) * P * N;
-  const float4_v* src = reinterpret_cast<const float4_v*>(
-      p.pool + int64_t(idx_r[acc_tok - 1]) * p.slot_stride + head_off);
-  float4_v st[ITERS];
-#pragma unroll
-  for (int i = 0; i < ITERS; ++i) {
-    const int pr = i * RP + prow;
-    st[i] = pr < P ? src[pr * NQ + lane_q] : float4_v{0.f, 0.f, 0.f, 0.f};
-  }
   __syncthreads();
 
   const float Ah = p.A[h];

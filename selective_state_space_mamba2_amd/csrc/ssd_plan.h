@@ -29,6 +29,22 @@ struct PrefillPlan {
 // 0..i/2 (one fragment each).
 constexpr int cb_frag_base(int i) { return (i / 2) * (i / 2 + 1) + (i % 2) * (i / 2 + 1); }
 
+// Placement of the march kernel's work items on the 8 XCDs of the device.  Items (one per
+// sequence, head and head-dim slice, in sequence dispatch order) are cut into nblocks =
+// 8 * ceil(S*G / 8) contiguous blocks of bsize items; block j runs on XCD j % 8, which
+// receives workgroup ids w with w % 8 == j % 8.  The workgroups that read the same
+// chunk's C.B^T / B^T / C fragments (one sequence and group) thus share an L2.  The grid
+// has nblocks * bsize workgroups; ids past the last item exit at once.
+struct MarchGrid {
+  int items, nblocks, bsize;
+};
+constexpr int kXcds = 8;
+constexpr MarchGrid march_grid(int S, int G, int H, int ps) {
+  const int items = S * H * ps;
+  const int nblocks = kXcds * ((S * G + kXcds - 1) / kXcds);
+  return MarchGrid{items, nblocks, (items + nblocks - 1) / nblocks};
+}
+
 // One instantiated chunked-prefill shape.
 struct ChunkedShape {
   int dtype;   // ssd_dtype

@@ -485,11 +485,18 @@ void k_chunk_march(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) float s_c[CS];
   __shared__ __attribute__((aligned(16))) float s_d[CS];
 
-  // 1-D grid: the head-dim slice fastest, then the head, then the sequence in dispatch
-  // order (longest first when the order was computed)
+  // work item of this workgroup (see march_grid): items are ordered by sequence (dispatch
+  // order), group, head in group, head-dim slice
   constexpr int PS = P / PW;
-  const int wg = blockIdx.x, tid = threadIdx.x;
-  const int p0 = (wg % PS) * PW, h = (wg / PS) % p.H, ry = wg / (PS * p.H);
+  const int tid = threadIdx.x;
+  const MarchGrid mg = march_grid(p.S, p.G, p.H, PS);
+  const int xcd = blockIdx.x % kXcds, xslot = blockIdx.x / kXcds;
+  const int item = (xcd + kXcds * (xslot / mg.bsize)) * mg.bsize + xslot % mg.bsize;
+  if (item >= mg.items) return;
+  const int hpg = p.H / p.G;
+  const int p0 = (item % PS) * PW;
+  const int hh = (item / PS) % hpg, gi = (item / (PS * hpg)) % p.G, ry = item / (PS * p.H);
+  const int h = gi * hpg + hh;
   const int r = p.S <= kOrderMaxSeqs ? ld_meta(p.seq_ord, ry) : ry;
   if (r < 0 || r >= p.S) {   // the order array comes from this launch's first kernel
     if (tid == 0) raise_flag(p.flag, SSD_DEVERR_CHUNK_RANGE);
@@ -821,7 +828,8 @@ static hipError_t run_chunked(const PrefillParams& p, hipStream_t s, void* const
   record_event(ev, 1, s);
   hipLaunchKernelGGL((k_chunk_prep<T, N, CS>), dim3(p.C, p.G, kPrepSplit), dim3(256), 0, s, p);
   record_event(ev, 2, s);
-  hipLaunchKernelGGL((k_chunk_march<T, P, PW, N, CS>), dim3(p.S * p.H * (P / PW)), dim3(256), 0,
+  const MarchGrid mg = march_grid(p.S, p.G, p.H, P / PW);
+  hipLaunchKernelGGL((k_chunk_march<T, P, PW, N, CS>), dim3(mg.nblocks * mg.bsize), dim3(256), 0,
                      s, p);
   record_event(ev, 3, s);
   return hipGetLastError();
