@@ -161,6 +161,32 @@ __device__ __forceinline__ typename Ops<T>::frag ld_frag(const BufRes& b, int f,
   return buf_ld8<T>(b, lane_b, uint32_t(f) * (512 * sizeof(T)));
 }
 
+// One y^T tile of a lane: acc[pt] holds p = pt*16 + 4*kg + 0..3 of token row l.  With two
+// p-tiles in bf16, lanes kg and kg^1 (lane ^ 16) swap halves so each lane stores 8
+// consecutive p (16 bytes): even kg keeps p-tile 0, odd kg keeps p-tile 1.
+template <typename T, int TPW>
+__device__ __forceinline__ void store_yt(T* ybase, int64_t y_st, int l, int L, int kg,
+                                         const f32x4_v* acc) {
+  if constexpr (sizeof(T) == 2 && TPW == 2) {
+    const bool odd = kg & 1;
+    const uint32_t u0 = pack_bf16x2(acc[0][0], acc[0][1]), u1 = pack_bf16x2(acc[0][2], acc[0][3]);
+    const uint32_t w0 = pack_bf16x2(acc[1][0], acc[1][1]), w1 = pack_bf16x2(acc[1][2], acc[1][3]);
+    // send the p-tile the partner keeps
+    const uint32_t r0 = __builtin_amdgcn_ds_swizzle(int(odd ? u0 : w0), 0x1F | (16 << 10));
+    const uint32_t r1 = __builtin_amdgcn_ds_swizzle(int(odd ? u1 : w1), 0x1F | (16 << 10));
+    if (l < L) {
+      const u32x4_v v = odd ? u32x4_v{r0, r1, w0, w1} : u32x4_v{u0, u1, r0, r1};
+      const int col = odd ? 16 + 4 * (kg - 1) : 4 * kg;
+      *reinterpret_cast<u32x4_v*>(ybase + int64_t(l) * y_st + col) = v;
+    }
+  } else {
+    if (l < L) {
+#pragma unroll
+      for (int pt = 0; pt < TPW; ++pt) Ops<T>::st4(ybase + int64_t(l) * y_st + pt * 16 + 4 * kg, acc[pt]);
+    }
+  }
+}
+
 __device__ __forceinline__ void st_f4(float* q, f32x4_v v) {
   *reinterpret_cast<float4_v*>(q) = float4_v{v[0], v[1], v[2], v[3]};
 }
@@ -461,7 +487,13 @@ __device__ __forceinline__ void march_load_stage(StageIn<T, MarchCfg<T, P, PW, N
 #define SSD_MARCH_BT_RING 4
 #endif
 #ifndef SSD_MARCH_CB_RING
-#define SSD_MARCH_CB_RING 3
+#define SSD_MARCH_CB_RING 2
+#endif
+#ifndef SSD_MARCH_NEXT_BEFORE_STORE
+#define SSD_MARCH_NEXT_BEFORE_STORE 0
+#endif
+#ifndef SSD_MARCH_EARLY_PAIR0
+#define SSD_MARCH_EARLY_PAIR0 1
 #endif
 #ifndef SSD_MARCH_PAIR_UNROLL
 #define SSD_MARCH_PAIR_UNROLL 2
@@ -644,6 +676,42 @@ void k_chunk_march(PrefillParams p) {
           if (TN % NW == 0 || wave * TNW + q < TN) sacc[q][pt] = O::mma(btf[ss % BTR][q], a, sacc[q][pt]);
       }
     }
+    // y^T is computed PT row tiles at a time (tiles 8*pr + w and 8*pr + 7 - w).  Each pair's
+    // operand fragments are requested before the stores that precede its use: loads and
+    // stores share one in-order completion counter, so a load issued behind a store would
+    // also wait for the store.
+    const BufRes cbr(static_cast<const T*>(p.cbw) + (int64_t(k) * p.G + grp) * (int64_t(NF) * 512));
+    const BufRes cfr(static_cast<const T*>(p.cfw) + (int64_t(k) * p.G + grp) * (int64_t(NT) * KN * 512));
+    T* ybase = static_cast<T*>(p.y) + int64_t(cs0) * p.y_st + int64_t(h) * P + p0;
+    constexpr int CBR = SSD_MARCH_CB_RING;
+    frag cf[PT][KN];      // C rows of the tiles as B operands (column l, contracted n)
+    frag cbd[PT];         // the diagonal blocks' C.B^T fragments
+    frag cbq[PT][CBR];    // the first CBR blocks before the diagonal, then a ring refilled
+                          // CBR blocks ahead (clamped requests re-read the diagonal block)
+    auto pair_tiles = [&](int pr, int* ti, int* bd) {
+#pragma unroll
+      for (int t = 0; t < PT; ++t) {
+        ti[t] = __builtin_amdgcn_readfirstlane(8 * pr + (t ? 7 - wave : wave));
+        bd[t] = ti[t] / 2;
+      }
+    };
+    auto load_pair = [&](int pr) {
+      int ti[PT], bd[PT];
+      pair_tiles(pr, ti, bd);
+#pragma unroll
+      for (int t = 0; t < PT; ++t) {
+#pragma unroll
+        for (int kk = 0; kk < KN; ++kk) cf[t][kk] = ld_frag<T>(cfr, ti[t] * KN + kk, lane_b);
+        cbd[t] = ld_frag<T>(cbr, cb_frag_base(ti[t]) + bd[t], lane_b);
+#pragma unroll
+        for (int j = 0; j < CBR; ++j)
+          cbq[t][j] = ld_frag<T>(cbr, cb_frag_base(ti[t]) + (j < bd[t] ? j : bd[t]), lane_b);
+      }
+    };
+#if SSD_MARCH_EARLY_PAIR0
+    load_pair(0);
+#endif
+
     // H_out = exp(c_last) H_in + S_k: the checkpoint at the chunk end
     const float dec = fast_exp(s_c[CS - 1]);
 #pragma unroll
@@ -672,39 +740,13 @@ void k_chunk_march(PrefillParams p) {
       }
     }
 
-    // y^T, PT row tiles at a time: tiles 8*pr + w and 8*pr + 7 - w
-    const BufRes cbr(static_cast<const T*>(p.cbw) + (int64_t(k) * p.G + grp) * (int64_t(NF) * 512));
-    const BufRes cfr(static_cast<const T*>(p.cfw) + (int64_t(k) * p.G + grp) * (int64_t(NT) * KN * 512));
-    T* ybase = static_cast<T*>(p.y) + int64_t(cs0) * p.y_st + int64_t(h) * P + p0;
+#if !SSD_MARCH_EARLY_PAIR0
+    load_pair(0);
+#endif
 #pragma unroll SSD_MARCH_PAIR_UNROLL
     for (int pr = 0; pr < NPAIR; ++pr) {
       int ti[PT], bd[PT];
-#pragma unroll
-      for (int t = 0; t < PT; ++t) {
-        ti[t] = __builtin_amdgcn_readfirstlane(8 * pr + (t ? 7 - wave : wave));
-        bd[t] = ti[t] / 2;
-      }
-      // the next chunk's x rows and cumsum (the HBM stream), requested during the last pair
-      if (pr == NPAIR - 1 && more) march_load_stage<T, P, PW, N, CS>(st, p, nxt, k + 1, h, p0);
-      // C rows of the tiles as B operands (column l, contracted n)
-      frag cf[PT][KN];
-#pragma unroll
-      for (int t = 0; t < PT; ++t)
-#pragma unroll
-        for (int kk = 0; kk < KN; ++kk)
-          cf[t][kk] = ld_frag<T>(cfr, ti[t] * KN + kk, lane_b);
-      // the diagonal blocks' C.B^T fragments, and the first CBR blocks before the diagonal
-      // (a ring refilled CBR blocks ahead; clamped requests re-read the diagonal block)
-      frag cbd[PT];
-#pragma unroll
-      for (int t = 0; t < PT; ++t) cbd[t] = ld_frag<T>(cbr, cb_frag_base(ti[t]) + bd[t], lane_b);
-      constexpr int CBR = SSD_MARCH_CB_RING;
-      frag cbq[PT][CBR];
-#pragma unroll
-      for (int t = 0; t < PT; ++t)
-#pragma unroll
-        for (int j = 0; j < CBR; ++j)
-          cbq[t][j] = ld_frag<T>(cbr, cb_frag_base(ti[t]) + (j < bd[t] ? j : bd[t]), lane_b);
+      pair_tiles(pr, ti, bd);
 
       // inter-chunk term: exp(c_l) H_in[p, :] . C_l
       f32x4_v acc[PT][TPW];
@@ -726,6 +768,9 @@ void k_chunk_march(PrefillParams p) {
 #pragma unroll
         for (int pt = 0; pt < TPW; ++pt) acc[t][pt] *= e;
       }
+      // the next chunk's x rows and cumsum (the HBM stream), requested during the last pair
+      // once its C fragments are consumed
+      if (pr == NPAIR - 1 && more) march_load_stage<T, P, PW, N, CS>(st, p, nxt, k + 1, h, p0);
 
       // blocks entirely before each tile's diagonal block, with the running rescale
       const int bmax = bd[PT - 1] > bd[0] ? bd[PT - 1] : bd[0];
@@ -789,16 +834,18 @@ void k_chunk_march(PrefillParams p) {
           acc[t][pt] = O::mma(O::ld8(&xT[prow * RSX + xsw(prow, s0 + 8 * kg)]), mf, acc[t][pt]);
         }
       }
+
+#if SSD_MARCH_NEXT_BEFORE_STORE
+      // the next pair's fragments go out before this pair's stores
+      if (pr + 1 < NPAIR) load_pair(pr + 1);
+#endif
+
       // y^T tile out: lane holds p = pt*16 + 4*kg + 0..3 of token l
 #pragma unroll
-      for (int t = 0; t < PT; ++t) {
-        const int l = 16 * ti[t] + li;
-        if (l < L) {
-#pragma unroll
-          for (int pt = 0; pt < TPW; ++pt)
-            O::st4(ybase + int64_t(l) * p.y_st + pt * 16 + 4 * kg, acc[t][pt]);
-        }
-      }
+      for (int t = 0; t < PT; ++t) store_yt<T, TPW>(ybase, p.y_st, 16 * ti[t] + li, L, kg, acc[t]);
+#if !SSD_MARCH_NEXT_BEFORE_STORE
+      if (pr + 1 < NPAIR) load_pair(pr + 1);
+#endif
     }
 
     cur = nxt;
