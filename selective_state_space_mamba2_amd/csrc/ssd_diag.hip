@@ -13,24 +13,43 @@
 // bf16), delta is prepared once per (token, channel) while staging, and y leaves through
 // an LDS tile as coalesced rows.  Checkpoints are written at the chunk ends listed by the
 // chunk metadata.
+#include <type_traits>
+
 #include "ssd_params.h"
 
 namespace ssd {
 
-template <typename T>
+#ifndef SSD_DIAG_UNROLL
+#define SSD_DIAG_UNROLL 4
+#endif
+#ifndef SSD_DIAG_SPL
+#define SSD_DIAG_SPL 4
+#endif
+
+// SPL states per lane: a channel's 16 states sit on 16/SPL adjacent lanes and a
+// workgroup owns CH = 256 / (16/SPL) channels.
+template <typename T, int SPL>
+struct DiagCfg {
+  static constexpr int N = kDiagN, LPC = N / SPL, CH = 256 / LPC;
+};
+
+template <typename T, int SPL>
 __global__ __launch_bounds__(256) void k_diag_scan(PrefillParams p) {
   constexpr int N = kDiagN;    // 16 states per channel
-  constexpr int CH = 64;       // channels per workgroup
+  constexpr int LPC = DiagCfg<T, SPL>::LPC;   // lanes per channel
+  constexpr int CH = DiagCfg<T, SPL>::CH;     // channels per workgroup
   constexpr int TT = 32;       // tokens per LDS tile
+  constexpr int U = SSD_DIAG_UNROLL;   // tokens per step of the scan (divides TT)
+  static_assert(TT % U == 0, "unroll");
   __shared__ float s_d[TT][CH];
   __shared__ float s_x[TT][CH];
   __shared__ float s_y[TT][CH];
-  __shared__ float4_v s_b[TT][N / 4];
-  __shared__ float4_v s_c[TT][N / 4];
+  __shared__ __attribute__((aligned(16))) float s_b[TT][N];
+  __shared__ __attribute__((aligned(16))) float s_c[TT][N];
 
   const int tid = threadIdx.x;
   const int cb = blockIdx.x, r = blockIdx.y;
-  const int cl = tid >> 2, ng = tid & 3;
+  const int cl = tid / LPC, ng = tid % LPC;
   const int H = p.H;
   const int c = cb * CH + cl;
   const bool valid = c < H;
@@ -45,8 +64,10 @@ __global__ __launch_bounds__(256) void k_diag_scan(PrefillParams p) {
   }
   int next_end = p.cu_chunk[k + 1];
 
-  float A2[4];
-  float h[4] = {0.f, 0.f, 0.f, 0.f};
+  float A2[SPL];
+  float h[SPL];
+#pragma unroll
+  for (int i = 0; i < SPL; ++i) h[i] = 0.f;
   int slot = -1;
   if (p.pool && p.state_idx) {
     slot = p.state_idx[r];
@@ -57,15 +78,15 @@ __global__ __launch_bounds__(256) void k_diag_scan(PrefillParams p) {
   }
   if (valid) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) A2[i] = p.A[c * N + ng * 4 + i] * kLog2e;
+    for (int i = 0; i < SPL; ++i) A2[i] = p.A[c * N + ng * SPL + i] * kLog2e;
     if (slot >= 0 && p.has_init && p.has_init[r]) {
-      const float4_v v = *reinterpret_cast<const float4_v*>(
-          p.pool + int64_t(slot) * p.slot_stride + int64_t(c) * N + ng * 4);
-      h[0] = v.x; h[1] = v.y; h[2] = v.z; h[3] = v.w;
+      const float* src = p.pool + int64_t(slot) * p.slot_stride + int64_t(c) * N + ng * SPL;
+#pragma unroll
+      for (int i = 0; i < SPL; ++i) h[i] = src[i];
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) A2[i] = 0.f;
+    for (int i = 0; i < SPL; ++i) A2[i] = 0.f;
   }
   const float Dc = (valid && p.D) ? p.D[c] : 0.f;
 
@@ -75,57 +96,117 @@ __global__ __launch_bounds__(256) void k_diag_scan(PrefillParams p) {
   const T* cg = static_cast<const T*>(p.Cm);
   T* yg = static_cast<T*>(p.y);
 
-  for (int tb = t0; tb < t1; tb += TT) {
+  // A tile's inputs are fetched into registers one tile ahead (raw values; positions past
+  // the sequence end read as zero) and written to LDS at the top of the tile's turn.
+  constexpr int NE = TT * CH / 256;              // delta / x elements per thread
+  constexpr int NBC = TT * 2 * (N / 4);          // B / C float4 items per tile
+  T rd[NE], rx[NE];
+  float4_v rbc;
+  auto fetch = [&](int tb) {
     const int nt = min(TT, t1 - tb);
-    for (int e = tid; e < TT * CH; e += 256) {
-      const int tt = e / CH, cc = e % CH, ch = cb * CH + cc;
-      float dv = 0.f, xv = 0.f;
-      if (tt < nt && ch < H) {
-        const int64_t t = tb + tt;
-        dv = p.prep(Elem<T>::load(dg + t * p.dt_st + ch), ch);
-        xv = Elem<T>::load(xg + t * p.x_st + ch);
-      }
-      s_d[tt][cc] = dv;
-      s_x[tt][cc] = xv;
+#pragma unroll
+    for (int u = 0; u < NE; ++u) {
+      const int e = u * 256 + tid, tt = e / CH, ch = cb * CH + e % CH;
+      const bool in = tt < nt && ch < H;
+      const int64_t t = in ? tb + tt : t0;
+      const int chc = in ? ch : 0;
+      rd[u] = in ? dg[t * p.dt_st + chc] : T(0);
+      rx[u] = in ? xg[t * p.x_st + chc] : T(0);
     }
-    if (tid < TT * 2 * (N / 4)) {
+    rbc = float4_v{0.f, 0.f, 0.f, 0.f};
+    if (tid < NBC) {
       const int tt = tid / (2 * (N / 4)), q = tid % (2 * (N / 4));
       const int which = q / (N / 4), n4 = q % (N / 4);
-      float4_v v = {0.f, 0.f, 0.f, 0.f};
       if (tt < nt) {
         const T* src = (which ? cg : bg) + int64_t(tb + tt) * p.bc_st + n4 * 4;
-        v = float4_v{Elem<T>::load(src), Elem<T>::load(src + 1), Elem<T>::load(src + 2),
-                     Elem<T>::load(src + 3)};
+        rbc = float4_v{Elem<T>::load(src), Elem<T>::load(src + 1), Elem<T>::load(src + 2),
+                       Elem<T>::load(src + 3)};
       }
-      if (which) s_c[tt][n4] = v; else s_b[tt][n4] = v;
+    }
+  };
+  fetch(t0);
+  for (int tb = t0; tb < t1; tb += TT) {
+    const int nt = min(TT, t1 - tb);
+#pragma unroll
+    for (int u = 0; u < NE; ++u) {
+      const int e = u * 256 + tid, tt = e / CH, cc = e % CH, ch = cb * CH + cc;
+      const bool in = tt < nt && ch < H;
+      s_d[tt][cc] = in ? p.prep(to_f32(rd[u]), ch) : 0.f;
+      s_x[tt][cc] = to_f32(rx[u]);
+    }
+    if (tid < NBC) {
+      const int tt = tid / (2 * (N / 4)), q = tid % (2 * (N / 4));
+      const int which = q / (N / 4), n4 = q % (N / 4);
+      *reinterpret_cast<float4_v*>(which ? &s_c[tt][4 * n4] : &s_b[tt][4 * n4]) = rbc;
     }
     __syncthreads();
+    if (tb + TT < t1) fetch(tb + TT);
 
-    for (int tt = 0; tt < nt; ++tt) {
-      const float d = s_d[tt][cl];
-      const float xv = s_x[tt][cl];
-      const float dx = d * xv;
-      const float4_v bv = s_b[tt][ng];
-      const float4_v cv = s_c[tt][ng];
-      const float bb[4] = {bv.x, bv.y, bv.z, bv.w};
-      const float cc4[4] = {cv.x, cv.y, cv.z, cv.w};
-      float acc = 0.f;
+
+    // The tile is walked in segments that end at a checkpoint (a chunk end inside the tile)
+    // or at the tile end.  Inside a segment tokens go U at a time with no branch, so the
+    // exponentials and LDS reads of a group, which do not depend on h, are issued together
+    // and only the state updates run in sequence.  Positions past nt hold delta = 0 (decay 1,
+    // no input), which leaves h unchanged, so the last segment may round up to a multiple
+    // of U.
+    auto steps = [&](int tt, auto ucount) {
+      constexpr int V = decltype(ucount)::value;
+      float dv[V], xv[V], a[V][SPL], bb[V][SPL], cc4[V][SPL];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float a = __builtin_amdgcn_exp2f(d * A2[i]);
-        h[i] = a * h[i] + dx * bb[i];
-        acc += cc4[i] * h[i];
+      for (int u = 0; u < V; ++u) {
+        dv[u] = s_d[tt + u][cl];
+        xv[u] = s_x[tt + u][cl];
+#pragma unroll
+        for (int i = 0; i < SPL; ++i) {
+          bb[u][i] = s_b[tt + u][ng * SPL + i];
+          cc4[u][i] = s_c[tt + u][ng * SPL + i];
+          a[u][i] = __builtin_amdgcn_exp2f(dv[u] * A2[i]);
+        }
       }
-      acc += __shfl_xor(acc, 1, 64);
-      acc += __shfl_xor(acc, 2, 64);
-      if (ng == 0) s_y[tt][cl] = acc + Dc * xv;
-      if (tb + tt + 1 == next_end) {  // end of chunk k: checkpoint (uniform branch)
-        if (valid && p.states) {
-          *reinterpret_cast<float4_v*>(p.states + (int64_t(k) * H + c) * N + ng * 4) =
-              float4_v{h[0], h[1], h[2], h[3]};
+      float acc[V];
+#pragma unroll
+      for (int u = 0; u < V; ++u) {
+        const float dx = dv[u] * xv[u];
+        acc[u] = 0.f;
+#pragma unroll
+        for (int i = 0; i < SPL; ++i) {
+          h[i] = a[u][i] * h[i] + dx * bb[u][i];
+          acc[u] += cc4[u][i] * h[i];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < V; ++u) {
+#pragma unroll
+        for (int off = 1; off < LPC; off <<= 1) acc[u] += __shfl_xor(acc[u], off, 64);
+      }
+      if (ng == 0) {
+#pragma unroll
+        for (int u = 0; u < V; ++u) s_y[tt + u][cl] = acc[u] + Dc * xv[u];
+      }
+    };
+    int tt = 0;
+    while (tt < nt) {
+      const int cut = next_end - tb;   // tokens of this tile up to the next checkpoint
+      const bool ckpt = cut > tt && cut <= nt;
+      if (ckpt) {
+#pragma unroll 1
+        for (; tt + U <= cut; tt += U) steps(tt, std::integral_constant<int, U>{});
+#pragma unroll 1
+        for (; tt < cut; ++tt) steps(tt, std::integral_constant<int, 1>{});
+        if (valid && p.states) {   // end of chunk k: checkpoint
+          float* dst = p.states + (int64_t(k) * H + c) * N + ng * SPL;
+#pragma unroll
+          for (int i = 0; i < SPL; ++i) dst[i] = h[i];
         }
         ++k;
         next_end = k <= klast ? p.cu_chunk[k + 1] : -1;
+      } else {
+        // single tokens up to a multiple of U (after a checkpoint inside the tile), then
+        // groups: an aligned group never reaches past the tile's TT rows
+#pragma unroll 1
+        for (; tt < nt && tt % U != 0; ++tt) steps(tt, std::integral_constant<int, 1>{});
+#pragma unroll 1
+        for (; tt < nt; tt += U) steps(tt, std::integral_constant<int, U>{});
       }
     }
     __syncthreads();
@@ -137,17 +218,19 @@ __global__ __launch_bounds__(256) void k_diag_scan(PrefillParams p) {
   }
   if (k != klast + 1 && tid == 0 && cb == 0) raise_flag(p.flag, SSD_DEVERR_CHUNK_RANGE);
   if (valid && p.write_final && slot >= 0) {
-    *reinterpret_cast<float4_v*>(p.pool + int64_t(slot) * p.slot_stride + int64_t(c) * N +
-                                 ng * 4) = float4_v{h[0], h[1], h[2], h[3]};
+    float* dst = p.pool + int64_t(slot) * p.slot_stride + int64_t(c) * N + ng * SPL;
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) dst[i] = h[i];
   }
 }
 
 hipError_t launch_diag_prefill(int in_dtype, const PrefillParams& p, hipStream_t s,
                                void* const* events) {
-  const dim3 grid((p.H + 63) / 64, p.S);
+  constexpr int SPL = SSD_DIAG_SPL, CH = DiagCfg<float, SPL>::CH;
+  const dim3 grid((p.H + CH - 1) / CH, p.S);
   record_event(events, 0, s);
-  if (in_dtype == SSD_BF16) hipLaunchKernelGGL(k_diag_scan<bf16_t>, grid, dim3(256), 0, s, p);
-  else hipLaunchKernelGGL(k_diag_scan<float>, grid, dim3(256), 0, s, p);
+  if (in_dtype == SSD_BF16) hipLaunchKernelGGL((k_diag_scan<bf16_t, SPL>), grid, dim3(256), 0, s, p);
+  else hipLaunchKernelGGL((k_diag_scan<float, SPL>), grid, dim3(256), 0, s, p);
   record_event(events, 1, s);
   return hipGetLastError();
 }

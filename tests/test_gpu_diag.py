@@ -25,6 +25,17 @@ def test_small_diag_with_pool_and_checkpoints(dtype):
             np.testing.assert_array_equal(got["pool"][s], inp.pool[s])
 
 
+def test_diag_several_checkpoints_per_token_tile():
+    """chunk_size 24 with unaligned resume points: several chunk ends fall inside one
+    32-token tile of the scan, so groups of tokens restart at unaligned positions."""
+    inp = make_prefill(42, in_dtype="bf16", H=72, P=1, G=1, N=16, chunk_size=24,
+                       lengths=[97, 33, 150], num_computed=[0, 7, 50], a_kind="diag",
+                       init="pool", pool_slots=4)
+    got = run_prefill(inp)
+    assert got["flag"] == 0
+    check_prefill(inp, got, oracle_prefill(inp))
+
+
 def test_diag_softplus_and_long_memory():
     inp = make_prefill(41, in_dtype="f32", H=64, P=1, G=1, N=16, chunk_size=64,
                        lengths=[500], a_kind="diag", A_range=(1e-3, 1e-2))
