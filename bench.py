@@ -6,7 +6,7 @@
 One step is one pass of the prefill path over the Mamba2-2.7B-like layer batch (4 packed
 sequences x 2048 tokens, 80 heads, head_dim 64, dstate 128, chunk 256, bf16 in / fp32
 state, the state written at every chunk end): chunk metadata on the host, its copy to the
-device, and the three prefill kernels.  Inputs are resident in HBM before timing starts;
+device, and the two prefill kernels.  Inputs are resident in HBM before timing starts;
 four input/output buffer sets rotate so the 256 MB Infinity Cache cannot hold a step's
 working set.  The line printed also carries the decode state update (256 live requests of
 a 512-row padded batch, 1+3 tokens, [2048,48,64,128] fp32 pool), the Nemotron-H-like
@@ -56,10 +56,10 @@ def prefill_work(inp, cuc, sidx):
     lens = [int(cuc[k + 1] - cuc[k]) for k in range(C)]
     cs = inp.chunk_size
     nfrag = sum(i // 2 + 1 for i in range(cs // 16))
-    # per (chunk, 16 heads): read dt, write the cumsum of delta*A and delta (fp32)
-    k_cum = dict(bytes=T * H * b + C * H * 2 * cs * 4, flops=0)
-    # per (chunk, group): read B and C, write the C.B^T fragments and B^T
-    k_prep = dict(bytes=2 * T * G * N * b + C * G * (nfrag * 512 + 2 * N * cs) * b,
+    # per (chunk, group): read dt, B and C; write the cumsum of delta*A and delta (fp32), the
+    # C.B^T fragments, B^T and C in fragment order
+    k_prep = dict(bytes=T * H * b + C * H * 2 * cs * 4 + 2 * T * G * N * b
+                  + C * G * (nfrag * 512 + 2 * N * cs) * b,
                   flops=sum(G * N * l * (l + 1) for l in lens))
     # per (head, sequence, half head dim): read x, C, the cumsum, the initial states; write y,
     # every chunk-end state and the final states (C.B^T and B^T come from the prep kernel
@@ -70,8 +70,7 @@ def prefill_work(inp, cuc, sidx):
     path = dict(bytes=T * (2 * H * P * b + H * b + 2 * G * N * b) + (n_init + C + n_final) * st,
                 flops=sum(H * (4 * l * P * N + P * l * (l + 1)) + G * N * l * (l + 1)
                           for l in lens))
-    return {"k_chunk_cumsum": k_cum, "k_chunk_prep": k_prep, "k_chunk_march": k_march,
-            "path": path}
+    return {"k_chunk_prep": k_prep, "k_chunk_march": k_march, "path": path}
 
 
 def decode_work(inp):

@@ -199,9 +199,9 @@ typedef struct ssd_prefill_args {
   void* const* profile_events;
 } ssd_prefill_args;
 
-#define SSD_PREFILL_MAX_KERNELS 3
+#define SSD_PREFILL_MAX_KERNELS 2
 
-/* Number of kernels ssd_prefill launches for these arguments (3 for SSD_A_SCALAR, 1 for
+/* Number of kernels ssd_prefill launches for these arguments (2 for SSD_A_SCALAR, 1 for
  * SSD_A_DIAG, 0 for an empty batch) and, when `names` is not NULL, a static name for each
  * kernel in launch order (names must hold SSD_PREFILL_MAX_KERNELS entries). */
 ssd_status ssd_prefill_kernel_count(const ssd_prefill_args* args, int32_t* count,

@@ -57,7 +57,7 @@ class PrefillArgs(ctypes.Structure):
     ]
 
 
-SSD_PREFILL_MAX_KERNELS = 3
+SSD_PREFILL_MAX_KERNELS = 2
 
 
 class DecodeArgs(ctypes.Structure):

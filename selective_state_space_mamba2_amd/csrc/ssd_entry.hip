@@ -95,12 +95,12 @@ ssd_status ssd_prefill_kernel_count(const ssd_prefill_args* a, int32_t* count,
   ssd::PrefillPlan plan;
   const ssd_status st = ssd::plan_prefill(a, &plan);
   if (st != SSD_OK) return st;
-  static const char* const kChunked[] = {"k_chunk_cumsum", "k_chunk_prep", "k_chunk_march"};
+  static const char* const kChunked[] = {"k_chunk_prep", "k_chunk_march"};
   static const char* const kDiag[] = {"k_diag_scan"};
   *count = 0;
   if (a->num_seqs == 0) return SSD_OK;
   const char* const* list = plan.kind == ssd::PrefillKind::kChunked ? kChunked : kDiag;
-  *count = plan.kind == ssd::PrefillKind::kChunked ? 3 : 1;
+  *count = plan.kind == ssd::PrefillKind::kChunked ? 2 : 1;
   if (names)
     for (int i = 0; i < *count; ++i) names[i] = list[i];
   return SSD_OK;

@@ -7,11 +7,11 @@
 // c_t = sum_{r<=t} delta_r A (chunk-local), unrolling the recurrence gives
 //   h_end  = exp(c_last) h_in + sum_s delta_s exp(c_last - c_s) x_s B_s^T
 //   y_l    = exp(c_l) (h_in C_l) + sum_{s<=l} (C_l . B_s) exp(c_l - c_s) delta_s x_s + D x_l
-// which three kernels evaluate:
-//   k_chunk_cumsum per (chunk, 16 heads): delta and the chunk-local cumsum c of delta*A,
-//                  one wavefront scan per head
-//   k_chunk_prep   per (chunk, group): B^T and the lower-triangular C.B^T blocks in the
-//                  input dtype, written in MFMA-fragment order and shared by every head
+// which two kernels evaluate:
+//   k_chunk_prep   per (chunk, group): delta and the chunk-local cumsum c of delta*A of the
+//                  group's heads (one wavefront scan per head), and B^T and the
+//                  lower-triangular C.B^T blocks in the input dtype, written in
+//                  MFMA-fragment order and shared by every head of the group
 //   k_chunk_march  per (head, sequence, slice of the head dim): walks the sequence's chunks
 //                  with the fp32 state in registers, producing y, the state after every
 //                  chunk (the prefix-caching checkpoint, "why this design", item 3) and the
@@ -216,18 +216,14 @@ __device__ __forceinline__ void wave_lds_sync() {
 __device__ __forceinline__ int xsw(int p, int s) { return s ^ (((p >> 3) & 3) << 4); }
 
 // ---------------------------------------------------------------------------------------
-// k_chunk_cumsum: delta = clamp(softplus(dt + bias)) and the chunk-local inclusive cumsum
-// c of delta*A per (chunk, head), written [C][H][2][CS] (c then delta).  Positions at or past
-// the chunk end hold delta = 0 and c = c_last, the flat continuation the march relies on.
-// One wavefront per head: four tokens per lane, a lane-local prefix, a wave scan.
+// Chunk-local cumsum (dA cumsum) and the march's sequence order, both produced inside
+// k_chunk_prep.
 // ---------------------------------------------------------------------------------------
-constexpr int kCumHeads = 16;   // heads per workgroup (4 per wavefront)
-
 // The march kernel walks each sequence's chunks in order, so a long sequence is a serial
 // chain: its workgroups are dispatched first (longest first, ties by index) so the chain
 // starts at once and shorter sequences fill the remaining slots.  The order is computed by
-// one workgroup of k_chunk_cumsum (a rank count over at most kOrderMaxSeqs sequences;
-// larger batches keep the given order).
+// one workgroup of k_chunk_prep (a rank count over at most kOrderMaxSeqs sequences;
+// larger batches keep the given order).  `nch` is kOrderMaxSeqs ints of LDS.
 constexpr int kOrderMaxSeqs = 1024;
 
 __device__ __forceinline__ void sequence_order(const PrefillParams& p, int* nch) {
@@ -244,67 +240,73 @@ __device__ __forceinline__ void sequence_order(const PrefillParams& p, int* nch)
     }
     p.seq_ord[rank] = r;
   }
+  __syncthreads();
 }
 
-template <typename T, int CS>
-__global__ __launch_bounds__(256) void k_chunk_cumsum(PrefillParams p) {
-  static_assert(CS <= 256 && CS % 4 == 0, "chunk size");
-  __shared__ int nch[kOrderMaxSeqs];
-  const int k = blockIdx.x, tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  if (k == 0 && blockIdx.y == 0 && p.S <= kOrderMaxSeqs) sequence_order(p, nch);
-  int cs0, L, r;
-  if (!chunk_bounds(p, k, CS, cs0, L, r)) {
-    if (tid == 0 && blockIdx.y == 0) raise_flag(p.flag, SSD_DEVERR_CHUNK_RANGE);
-    return;
-  }
+// delta = clamp(softplus(dt + bias)) and the chunk-local inclusive cumsum c of delta*A of
+// one head, one wavefront: four tokens per lane, a lane-local prefix, a wave scan.  Written
+// to the workspace as [C][H][2][CS] (c then delta); positions at or past the chunk end hold
+// delta = 0 and c = c_last, the flat continuation the march relies on.
+template <typename T>
+__device__ __forceinline__ void load_dt4(const PrefillParams& p, int cs0, int L, int h, int lane,
+                                         float (&raw)[4]) {
   const T* dtp = static_cast<const T*>(p.dt);
-#pragma unroll 1
-  for (int i = 0; i < kCumHeads / 4; ++i) {
-    const int h = blockIdx.y * kCumHeads + wave + 4 * i;
-    if (h >= p.H) break;
-    const float Ah = p.A[h], bias = p.prep.bias_of(h);
-    float d[4], c[4];
-    float run = 0.f;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int tok = 4 * lane + t;
-      const int row = tok < L ? tok : L - 1;
-      const float raw = to_f32(dtp[int64_t(cs0 + row) * p.dt_st + h]);
-      d[t] = tok < L ? p.prep.apply(raw, bias) : 0.f;
-      run += d[t] * Ah;
-      c[t] = run;
-    }
-    const float incl = wave_inclusive_scan(run);
-    const float base = incl - run;
+  for (int t = 0; t < 4; ++t) {
+    const int tok = 4 * lane + t;
+    const int row = tok < L ? tok : L - 1;
+    raw[t] = to_f32(dtp[int64_t(cs0 + row) * p.dt_st + h]);
+  }
+}
+
+template <int CS>
+__device__ __forceinline__ void cumsum_head(const PrefillParams& p, int k, int cs0, int L, int h,
+                                            int lane, const float (&raw)[4]) {
+  static_assert(CS <= 256 && CS % 4 == 0, "chunk size");
+  const float Ah = p.A[h], bias = p.prep.bias_of(h);
+  float d[4], c[4];
+  float run = 0.f;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) c[t] += base;
-    if (4 * lane < CS) {
-      float* dst = p.dcw + (int64_t(k) * p.H + h) * (2 * CS) + 4 * lane;
-      *reinterpret_cast<float4_v*>(dst) = float4_v{c[0], c[1], c[2], c[3]};
-      *reinterpret_cast<float4_v*>(dst + CS) = float4_v{d[0], d[1], d[2], d[3]};
-    }
-    if (p.dA_cumsum_out) {
+  for (int t = 0; t < 4; ++t) {
+    d[t] = 4 * lane + t < L ? p.prep.apply(raw[t], bias) : 0.f;
+    run += d[t] * Ah;
+    c[t] = run;
+  }
+  const float incl = wave_inclusive_scan(run);
+  const float base = incl - run;
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        if (4 * lane + t < L) p.dA_cumsum_out[int64_t(h) * p.T + cs0 + 4 * lane + t] = c[t];
-    }
+  for (int t = 0; t < 4; ++t) c[t] += base;
+  if (4 * lane < CS) {
+    float* dst = p.dcw + (int64_t(k) * p.H + h) * (2 * CS) + 4 * lane;
+    *reinterpret_cast<float4_v*>(dst) = float4_v{c[0], c[1], c[2], c[3]};
+    *reinterpret_cast<float4_v*>(dst + CS) = float4_v{d[0], d[1], d[2], d[3]};
+  }
+  if (p.dA_cumsum_out) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      if (4 * lane + t < L) p.dA_cumsum_out[int64_t(h) * p.T + cs0 + 4 * lane + t] = c[t];
   }
 }
 
 // ---------------------------------------------------------------------------------------
-// k_chunk_prep: per (chunk, group) B^T and the C.B^T blocks the y tiles need, both in the
-// input dtype and in MFMA-fragment order (one fragment = 64 lanes x 8 values, 1 KB in bf16),
-// so a wavefront fetches a fragment with one contiguous load.
+// k_chunk_prep: per (chunk, group) the cumsum of delta*A of the group's heads (above), and
+// B^T and the C.B^T blocks the y tiles need, both in the input dtype and in MFMA-fragment
+// order (one fragment = 64 lanes x 8 values, 1 KB in bf16), so a wavefront fetches a
+// fragment with one contiguous load.
 //   B^T fragment (n-tile nt, 32-token step ss): lane (kg, li) holds B[s = 32 ss + 8 kg + j]
 //     [n = 16 nt + li]; stored at ((chunk * G + g) * TN + nt) * NSTEP + ss.
 //   C.B^T fragment (row tile i, block b <= i/2): lane (kg, li) holds (C_l . B_s) for
 //     l = 16 i + li, s = 32 b + 8 kg + j; stored at (chunk * G + g) * NF + cb_frag_base(i) + b.
 //   C fragment (row tile i, 32-wide dstate step kk): lane (kg, li) holds C[l = 16 i + li]
 //     [n = 32 kk + 8 kg + j] (zero past dstate); stored at ((chunk * G + g) * NT + i) * KN + kk.
-// Rows past the chunk end are zero.  Work is split over kPrepSplit workgroups.
+// Rows past the chunk end are zero.  Each (chunk, group) is split over gridDim.z
+// workgroups (prep_split): more of them when there are few chunks, one when there are many,
+// since every workgroup of a (chunk, group) stages the whole B chunk.
 // ---------------------------------------------------------------------------------------
-constexpr int kPrepSplit = 4;
+inline int prep_split(int chunks_x_groups) {
+  const int z = (512 + chunks_x_groups - 1) / chunks_x_groups;
+  return z < 1 ? 1 : (z > 8 ? 8 : z);
+}
 
 template <typename T, int N, int CS>
 __global__ __launch_bounds__(256) void k_chunk_prep(PrefillParams p) {
@@ -321,15 +323,47 @@ __global__ __launch_bounds__(256) void k_chunk_prep(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) float tl[NW][16 * TLS];
 
   const int k = blockIdx.x, g = blockIdx.y, z = blockIdx.z, tid = threadIdx.x;
+  const int zs = gridDim.z;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  if (k == 0 && g == 0 && z == 0 && p.S <= kOrderMaxSeqs) {
+    static_assert(sizeof(tl) >= kOrderMaxSeqs * sizeof(int), "order scratch");
+    sequence_order(p, reinterpret_cast<int*>(&tl[0][0]));
+  }
   int cs0, L, r;
   if (!chunk_bounds(p, k, CS, cs0, L, r)) {
     if (tid == 0 && g == 0 && z == 0) raise_flag(p.flag, SSD_DEVERR_CHUNK_RANGE);
     return;
   }
+  // the chunk's B rows: every request first, into registers
+  constexpr int NBI = CS * (NP / 8) / 256;
+  static_assert(CS * (NP / 8) % 256 == 0, "B staging");
   const T* bsrc = static_cast<const T*>(p.B) + int64_t(cs0) * p.bc_st + int64_t(g) * N;
-  for (int e = tid; e < CS * (NP / 8); e += 256) {
-    const int s = e / (NP / 8), c8 = e % (NP / 8);
-    const frag v = O::gld8(bsrc + int64_t(s) * p.bc_st + 8 * c8, s < L && 8 * c8 < N);
+  frag bv[NBI];
+#pragma unroll
+  for (int u = 0; u < NBI; ++u) {
+    const int e = u * 256 + tid, s = e / (NP / 8), c8 = e % (NP / 8);
+    bv[u] = O::gld8(bsrc + int64_t(s) * p.bc_st + 8 * c8, s < L && 8 * c8 < N);
+  }
+  // meanwhile the cumsum of this workgroup's share of the group's heads, one wavefront per
+  // head, each head's dt requested one head ahead
+  {
+    const int hpg = p.H / p.G, hz = (hpg + zs - 1) / zs;
+    const int h0 = g * hpg + z * hz, h1 = min(g * hpg + hpg, h0 + hz);
+    float raw[4], nxt[4];
+    int h = h0 + wave;
+    if (h < h1) load_dt4<T>(p, cs0, L, h, lane, nxt);
+#pragma unroll 1
+    for (; h < h1; h += 4) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) raw[t] = nxt[t];
+      if (h + 4 < h1) load_dt4<T>(p, cs0, L, h + 4, lane, nxt);
+      cumsum_head<CS>(p, k, cs0, L, h, lane, raw);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < NBI; ++u) {
+    const int e = u * 256 + tid, s = e / (NP / 8), c8 = e % (NP / 8);
+    const frag& v = bv[u];
     if constexpr (sizeof(T) == 2) {
       *reinterpret_cast<u32x4_v*>(&Bs[s * RSB + 8 * c8]) = u32x4_v{v.w[0], v.w[1], v.w[2], v.w[3]};
     } else {
@@ -341,7 +375,7 @@ __global__ __launch_bounds__(256) void k_chunk_prep(PrefillParams p) {
 
   // B^T fragments, this workgroup's share
   T* bt = static_cast<T*>(p.btw) + (int64_t(k) * p.G + g) * (int64_t(N) * CS);
-  for (int e = z * 256 + tid; e < TN * NSTEP * 64; e += 256 * kPrepSplit) {
+  for (int e = z * 256 + tid; e < TN * NSTEP * 64; e += 256 * zs) {
     const int f = e >> 6, ln = e & 63;
     const int nt = f / NSTEP, ss = f % NSTEP, li = ln & 15, kg = ln >> 4;
     float v[8];
@@ -353,14 +387,14 @@ __global__ __launch_bounds__(256) void k_chunk_prep(PrefillParams p) {
   // C.B^T fragments: each 16x16 tile is computed transposed (rows s, columns l) so lane
   // (kg, li) gets C_l . B_s for l = 16 i + li, s = 16 jt + 4 kg + rr; two tiles are regrouped
   // through LDS into the 8-consecutive-s fragment of one 32-token block.
-  const int wave = tid >> 6, lane = tid & 63, li = lane & 15, kg = lane >> 4;
+  const int li = lane & 15, kg = lane >> 4;
   const T* csrc = static_cast<const T*>(p.Cm) + int64_t(cs0) * p.bc_st + int64_t(g) * N;
   T* cb = static_cast<T*>(p.cbw) + (int64_t(k) * p.G + g) * (int64_t(NF) * 512);
   float* cb_dbg = p.cb_out ? p.cb_out + (int64_t(k) * p.G + g) * CS * CS : nullptr;
   float* tw = tl[wave];
   // row tiles of this workgroup: w = z * NW + wave, then mirrored pairs balancing the
   // causal work
-  constexpr int NWT = NW * kPrepSplit;
+  const int NWT = NW * zs;
 #pragma unroll 1
   for (int q = 0; q < (NT + NWT - 1) / NWT; ++q) {
     const int w = z * NW + wave;
@@ -870,15 +904,13 @@ template <typename T, int P, int N, int CS>
 static hipError_t run_chunked(const PrefillParams& p, hipStream_t s, void* const* ev) {
   constexpr int PW = P >= 32 ? 32 : P;
   record_event(ev, 0, s);
-  hipLaunchKernelGGL((k_chunk_cumsum<T, CS>), dim3(p.C, (p.H + kCumHeads - 1) / kCumHeads),
-                     dim3(256), 0, s, p);
+  hipLaunchKernelGGL((k_chunk_prep<T, N, CS>), dim3(p.C, p.G, prep_split(p.C * p.G)), dim3(256), 0,
+                     s, p);
   record_event(ev, 1, s);
-  hipLaunchKernelGGL((k_chunk_prep<T, N, CS>), dim3(p.C, p.G, kPrepSplit), dim3(256), 0, s, p);
-  record_event(ev, 2, s);
   const MarchGrid mg = march_grid(p.S, p.G, p.H, P / PW);
   hipLaunchKernelGGL((k_chunk_march<T, P, PW, N, CS>), dim3(mg.nblocks * mg.bsize), dim3(256), 0,
                      s, p);
-  record_event(ev, 3, s);
+  record_event(ev, 2, s);
   return hipGetLastError();
 }
 

@@ -121,8 +121,8 @@ def test_kernel_count():
     n = ctypes.c_int32(-1)
     names = (ctypes.c_char_p * _abi.SSD_PREFILL_MAX_KERNELS)()
     assert lib().ssd_prefill_kernel_count(ctypes.byref(_good_prefill()), ctypes.byref(n), names) == 0
-    assert n.value == 3
-    assert [names[i] for i in range(3)] == [b"k_chunk_cumsum", b"k_chunk_prep", b"k_chunk_march"]
+    assert n.value == 2
+    assert [names[i] for i in range(2)] == [b"k_chunk_prep", b"k_chunk_march"]
     diag = _good_prefill(a_kind=_abi.SSD_A_DIAG, H=64, P=1, G=1, N=16, x_stride_t=64,
                          y_stride_t=64, dt_stride_t=64, bc_stride_t=16)
     assert lib().ssd_prefill_kernel_count(ctypes.byref(diag), ctypes.byref(n), names) == 0
