@@ -62,16 +62,17 @@ def prefill_work(inp, cuc, sidx):
     k_prep = dict(bytes=T * H * b + C * H * 2 * cs * 4 + 2 * T * G * N * b
                   + C * G * (nfrag * 512 + 2 * N * cs) * b,
                   flops=sum(G * N * l * (l + 1) for l in lens))
-    # per (head, sequence, half head dim): read x, C, the cumsum, the initial states; write y,
-    # every chunk-end state and the final states (C.B^T and B^T come from the prep kernel
-    # through L2)
+    # the march / chain kernel: read x, C, the cumsum, the initial states; write y, every
+    # chunk-end state and the final states (C.B^T and B^T come from the prep kernel through
+    # L2, and a chain reads back its predecessor's state through L2 too)
     k_march = dict(bytes=T * (2 * H * P * b + G * N * b) + C * H * 2 * cs * 4
                    + (n_init + C + n_final) * st,
                    flops=sum(H * (4 * l * P * N + P * l * (l + 1)) for l in lens))
     path = dict(bytes=T * (2 * H * P * b + H * b + 2 * G * N * b) + (n_init + C + n_final) * st,
                 flops=sum(H * (4 * l * P * N + P * l * (l + 1)) + G * N * l * (l + 1)
                           for l in lens))
-    return {"k_chunk_prep": k_prep, "k_chunk_march": k_march, "path": path}
+    return {"k_chunk_prep": k_prep, "k_chunk_march": k_march, "k_chunk_chain": k_march,
+            "path": path}
 
 
 def decode_work(inp):

@@ -80,6 +80,11 @@ ssd_status ssd_prefill(const ssd_prefill_args* a, void* workspace, size_t worksp
     p.dcw = reinterpret_cast<float*>(ws + plan.off_dc);
     p.cfw = ws + plan.off_cf;
     p.seq_ord = reinterpret_cast<int*>(ws + plan.off_ord);
+    if (plan.chain) {
+      p.chain_flag = reinterpret_cast<int*>(ws + plan.off_flag);
+      p.chunk_ord = reinterpret_cast<int*>(ws + plan.off_cord);
+      p.hring = a->chunk_states_out ? nullptr : reinterpret_cast<float*>(ws + plan.off_ring);
+    }
   }
 
   const hipStream_t s = static_cast<hipStream_t>(stream);
@@ -96,10 +101,12 @@ ssd_status ssd_prefill_kernel_count(const ssd_prefill_args* a, int32_t* count,
   const ssd_status st = ssd::plan_prefill(a, &plan);
   if (st != SSD_OK) return st;
   static const char* const kChunked[] = {"k_chunk_prep", "k_chunk_march"};
+  static const char* const kChain[] = {"k_chunk_prep", "k_chunk_chain"};
   static const char* const kDiag[] = {"k_diag_scan"};
   *count = 0;
   if (a->num_seqs == 0) return SSD_OK;
-  const char* const* list = plan.kind == ssd::PrefillKind::kChunked ? kChunked : kDiag;
+  const char* const* list = plan.kind == ssd::PrefillKind::kChunked
+                                ? (plan.chain ? kChain : kChunked) : kDiag;
   *count = plan.kind == ssd::PrefillKind::kChunked ? 2 : 1;
   if (names)
     for (int i = 0; i < *count; ++i) names[i] = list[i];

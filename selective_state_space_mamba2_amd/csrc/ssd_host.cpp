@@ -96,6 +96,16 @@ ssd_status plan_prefill(const ssd_prefill_args* a, PrefillPlan* plan) {
   off = align_up(off + size_t(C) * a->G * cs * size_t(a->N < 32 ? 32 : a->N) * esz, 256);
   plan->off_ord = off;
   off = align_up(off + size_t(a->num_seqs) * sizeof(int32_t), 256);
+  plan->chain = chain_supported(a->in_dtype, a->P, a->N, a->chunk_size);
+  if (plan->chain) {
+    plan->off_flag = off;
+    off = align_up(off + size_t(C) * a->H * kChainWaves * sizeof(int32_t), 256);
+    plan->off_cord = off;
+    off = align_up(off + size_t(C) * sizeof(int32_t), 256);
+    plan->off_ring = off;
+    if (!a->chunk_states_out)
+      off = align_up(off + size_t(a->num_seqs) * a->H * 2 * size_t(state / a->H) * sizeof(float), 256);
+  }
   plan->ws_bytes = off;
   return SSD_OK;
 }

@@ -35,6 +35,9 @@ struct PrefillParams {
   float* dcw;          // workspace [C, H, 2, cs]: cumsum of delta*A, then delta
   void* cfw;           // workspace, input dtype: C fragments per chunk and group
   int* seq_ord;        // workspace [S]: sequences in march dispatch order
+  int* chain_flag;     // workspace [C, H, kChainWaves]: chain publication flags (NULL: march)
+  int* chunk_ord;      // workspace [C]: chunks in chain dispatch order
+  float* hring;        // workspace [S, H, 2, P, N] when states is NULL: published states
   int* flag;
   float* dA_cumsum_out;
   float* cb_out;

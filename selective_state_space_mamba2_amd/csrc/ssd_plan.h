@@ -23,7 +23,21 @@ struct PrefillPlan {
   size_t off_dc = 0;         // fp32 [C, H, 2, cs]: cumsum of delta*A, then delta
   size_t off_cf = 0;         // input dtype [C, G, cs * max(N, 32)]: C rows as fragments
   size_t off_ord = 0;        // int32 [S]: sequence dispatch order of the march kernel
+  bool chain = false;        // the chunk-chain kernel runs (else a march kernel)
+  size_t off_flag = 0;       // int32 [C, H, kChainWaves]: chain publication flags
+  size_t off_cord = 0;       // int32 [C]: chain dispatch order of the chunks
+  size_t off_ring = 0;       // fp32 [S, H, 2, P, N]: published states when no chunk-state
+                             // output is given (0 bytes otherwise)
 };
+
+// Shapes that run the chunk-chain kernel (bf16, head dim 64, dstate a multiple of 64,
+// chunks of at least 128 tokens); the others run the march kernel.
+constexpr bool chain_supported(int dtype, int P, int N, int CS) {
+  return dtype == SSD_BF16 && P == 64 && N % 64 == 0 && CS >= 128;
+}
+// Wavefronts per chunk-chain workgroup; each publishes its share of the state under a
+// flag of its own, so there are kChainWaves flags per (chunk, head).
+constexpr int kChainWaves = 4;
 
 // C.B^T fragments of the 16-row tiles 0..i-1 of a chunk: tile i needs the 32-token blocks
 // 0..i/2 (one fragment each).

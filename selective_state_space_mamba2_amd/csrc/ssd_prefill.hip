@@ -226,10 +226,19 @@ __device__ __forceinline__ int xsw(int p, int s) { return s ^ (((p >> 3) & 3) <<
 // larger batches keep the given order).  `nch` is kOrderMaxSeqs ints of LDS.
 constexpr int kOrderMaxSeqs = 1024;
 
-__device__ __forceinline__ void sequence_order(const PrefillParams& p, int* nch) {
+// Whether k_chunk_prep writes the chain kernel's chunk order (a count over all sequences
+// per chunk, so it is bounded); otherwise the chain kernel takes chunks in index order,
+// which also puts every predecessor first.
+__device__ __forceinline__ bool chain_ordered(const PrefillParams& p) {
+  return p.S <= kOrderMaxSeqs && int64_t(p.S) * p.C <= (int64_t(1) << 20);
+}
+
+__device__ __forceinline__ void sequence_order(const PrefillParams& p, int* nch, int* rank_of) {
   const int S = p.S;
-  for (int r = threadIdx.x; r < S; r += blockDim.x)
-    nch[r] = p.last_chunk[r] - (r == 0 ? -1 : p.last_chunk[r - 1]);
+  for (int r = threadIdx.x; r < S; r += blockDim.x) {
+    const int n = p.last_chunk[r] - (r == 0 ? -1 : p.last_chunk[r - 1]);
+    nch[r] = n < 0 ? 0 : (n > p.C ? p.C : n);
+  }
   __syncthreads();
   for (int r = threadIdx.x; r < S; r += blockDim.x) {
     const int n = nch[r];
@@ -239,8 +248,29 @@ __device__ __forceinline__ void sequence_order(const PrefillParams& p, int* nch)
       rank += (m > n) || (m == n && q < r);
     }
     p.seq_ord[rank] = r;
+    rank_of[r] = rank;
   }
   __syncthreads();
+}
+
+// The chain kernel's row order: chunk j of sequence r (ranked q longest first) goes to row
+// sum_r' min(nch_r', j) + q, i.e. by position inside the sequence, then by rank.  The
+// sequences with more than j chunks are exactly ranks 0 .. cnt_j - 1, so rows are dense
+// and every chunk's predecessor has a smaller row.  Rows no chunk claims (bad metadata)
+// hold -1.
+__device__ __forceinline__ void chain_chunk_order(const PrefillParams& p, const int* nch,
+                                                  const int* rank_of) {
+  for (int i = threadIdx.x; i < p.C; i += blockDim.x) p.chunk_ord[i] = -1;
+  __syncthreads();
+  for (int k = threadIdx.x; k < p.C; k += blockDim.x) {
+    const int r = p.seq_idx[k];
+    if (r < 0 || r >= p.S) continue;
+    const int j = k - (r == 0 ? 0 : p.last_chunk[r - 1] + 1);
+    if (j < 0 || j >= nch[r]) continue;
+    int row = rank_of[r];
+    for (int q = 0; q < p.S; ++q) row += min(nch[q], j);
+    if (row < p.C) p.chunk_ord[row] = k;
+  }
 }
 
 // delta = clamp(softplus(dt + bias)) and the chunk-local inclusive cumsum c of delta*A of
@@ -326,8 +356,17 @@ __global__ __launch_bounds__(256) void k_chunk_prep(PrefillParams p) {
   const int zs = gridDim.z;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   if (k == 0 && g == 0 && z == 0 && p.S <= kOrderMaxSeqs) {
-    static_assert(sizeof(tl) >= kOrderMaxSeqs * sizeof(int), "order scratch");
-    sequence_order(p, reinterpret_cast<int*>(&tl[0][0]));
+    static_assert(sizeof(tl) >= 2 * kOrderMaxSeqs * sizeof(int), "order scratch");
+    int* nch = reinterpret_cast<int*>(&tl[0][0]);
+    sequence_order(p, nch, nch + kOrderMaxSeqs);
+    if (p.chunk_ord && chain_ordered(p)) chain_chunk_order(p, nch, nch + kOrderMaxSeqs);
+    __syncthreads();
+  }
+  // the chain kernel's publication flags of this chunk start cleared
+  if (p.chain_flag && z == 0) {
+    const int n = (p.H / p.G) * kChainWaves;
+    for (int i = tid; i < n; i += 256)
+      p.chain_flag[(int64_t(k) * p.H + g * (p.H / p.G)) * kChainWaves + i] = 0;
   }
   int cs0, L, r;
   if (!chunk_bounds(p, k, CS, cs0, L, r)) {
@@ -898,18 +937,462 @@ void k_chunk_march(PrefillParams p) {
 }
 
 // ---------------------------------------------------------------------------------------
+// k_chunk_chain: the chunks of one (sequence, head) as a chain of workgroups, one per
+// (chunk, head), bf16 with P = 64.  The only serial dependency of the recurrence across
+// chunks is the state, H_k = exp(c_last) H_{k-1} + S_k.  Each workgroup computes its chunk's
+// own state S_k from its inputs alone, then takes H_{k-1} from its predecessor (the
+// chunk-end checkpoint, read back from memory), forms and publishes H_k, and only then
+// evaluates y with H_{k-1} as the incoming state.  The critical path per chunk is one
+// checkpoint round trip; the heavy work of all chunks runs concurrently.
+//
+// Per chunk (4 wavefronts; wave w owns the state columns n of its n-tiles [2w, 2w+2) and
+// the y row tiles {w, 7-w, 8+w, 15-w}), with only raw x^T staged in LDS and the per-token
+// weights applied to the other MFMA operand in registers:
+//   * S_k^T = (B^T o w) x with w_s = delta_s exp(c_last - c_s): one reference point, the
+//     chunk end, so no rescaling;
+//   * y, the blocks before the diagonal block: (C.B^T o v) x with
+//     v_s = delta_s exp(c_{r(s)} - c_s) (reference: the end of the token's 32-token block),
+//     the running sum rescaled block to block and joined to row l with exp(c_l - c_ref);
+//   * y, the diagonal block: exact exp(c_l - c_s) delta_s per element, causal mask, D on
+//     the diagonal; y^T leaves straight from the accumulators.
+// Every shared fragment (B^T, C.B^T, C) feeds all four 16-row p-tiles of the head.
+//
+// Hand-off: each wave publishes its columns of H_k under a flag of its own (the successor's
+// wave w reads exactly those columns), so the chain needs no workgroup barrier.  The
+// checkpoint stores and the successor's loads use the device-coherent cache policy (see
+// kCohDev); the publisher waits for its stores to complete, then sets the flag.
+//
+// Dispatch order: rows of the grid are chunks in the order of k_chunk_prep's chunk_ord (by
+// position inside the sequence, then sequences longest first), so a workgroup's
+// predecessor sits in an earlier row; inside a row, head h runs on XCD h / ceil(H / 8),
+// so the heads of one group share an L2 for the fragments.  Workgroups are dispatched in
+// id order, so a waiting workgroup's predecessor is already resident or done; the wait is
+// also bounded in time (about a second, then SSD_DEVERR_CHAIN_WAIT is raised and the
+// workgroup goes on), so no metadata error can stall the device.
+// ---------------------------------------------------------------------------------------
+
+// A bf16 fragment with value j multiplied by v[j].
+__device__ __forceinline__ Frag8 scale_frag(const Frag8& f, const float* v) {
+  Frag8 r;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float lo = __uint_as_float(f.w[w] << 16), hi = __uint_as_float(f.w[w] & 0xffff0000u);
+    r.w[w] = pack_bf16x2(lo * v[2 * w], hi * v[2 * w + 1]);
+  }
+  return r;
+}
+
+template <int N, int CS>
+struct ChainCfg {
+  static constexpr int P = 64, NW = kChainWaves, NTH = 64 * NW, NT = CS / 16, NSTEP = CS / 32;
+  static constexpr int TP = 4, TN = N / 16, TNW = TN / NW, KN = N / 32;
+  static constexpr int NTQ = NT / NW;                 // row tiles per wave
+  static constexpr int NG = P / 8, NITEM = NG * CS / 4, NI = NITEM / NTH;
+  static constexpr int NF = cb_frag_base(NT);
+  static_assert(TN % NW == 0 && N % 32 == 0 && NT % NW == 0 && NITEM % NTH == 0, "shape");
+};
+
+template <int NI>
+struct ChainStage {
+  Frag8 x[NI][4];
+  float4_v c[NI], d[NI];
+  float cref[NI];
+  float clast;
+};
+
+// The chunk's x rows, cumsum and delta.  Work item `it`: columns 8*g8 .. 8*g8+7, tokens
+// 4*sg .. 4*sg+3.
+template <int N, int CS>
+__device__ __forceinline__ void chain_load_stage(ChainStage<ChainCfg<N, CS>::NI>& st,
+                                                 const PrefillParams& p, ChunkLoc c, int k, int h) {
+  using M = ChainCfg<N, CS>;
+  const BufRes xr(static_cast<const bf16_t*>(p.x) + int64_t(c.cs0) * p.x_st + int64_t(h) * M::P);
+  const uint32_t xrow_b = uint32_t(p.x_st * int64_t(sizeof(bf16_t)));
+  const float* dc = p.dcw + (int64_t(k) * p.H + h) * (2 * CS);
+#pragma unroll
+  for (int u = 0; u < M::NI; ++u) {
+    const int it = u * M::NTH + int(threadIdx.x);
+    const int g8 = it % M::NG, s = 4 * (it / M::NG);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      // unguarded: rows past the chunk end repeat its last row (their weight is zero)
+      const int row = s + t < c.L ? s + t : c.L - 1;
+      st.x[u][t] = buf_ld8<bf16_t>(xr, uint32_t(row) * xrow_b + uint32_t(g8) * 16, 0);
+    }
+    st.c[u] = *reinterpret_cast<const float4_v*>(dc + s);
+    st.d[u] = *reinterpret_cast<const float4_v*>(dc + CS + s);
+    st.cref[u] = dc[s | 31];
+  }
+  st.clast = dc[CS - 1];
+}
+
+constexpr long long kChainWaitTicks = 100000000;   // ~1 s of the 100 MHz wall clock
+// Cache policy of the published-state accesses: device-scope coherent (sc1), the policy of
+// device-scope relaxed atomics.  A store with it is performed for every CU once it
+// completes, and a load with it observes such stores, so the hand-off needs no cache
+// flush or invalidate: the publisher waits for its stores to complete before the flag
+// store, the successor issues its loads after it has seen the flag.
+constexpr int kCohDev = 16;
+
+// LDS tiles of the chain kernel, unpadded rows (52 KB in all, three workgroups per CU):
+// x^T [p][s] with the 8-token (16-byte) groups XOR-ed with (p ^ p >> 3) & 7, so both the
+// staging writes (8 columns 8 apart per token group) and the fragment reads (16
+// consecutive rows) spread over all banks; the state rows [p][n] with the 8-column groups
+// XOR-ed with p & 7 (only p mod 16 matters, the p-tiles are 16 rows).
+__device__ __forceinline__ int chain_xs(int p, int s) { return s ^ ((((p >> 3) ^ p) & 7) << 3); }
+__device__ __forceinline__ int chain_hs(int pl, int n) { return n ^ ((pl & 7) << 3); }
+
+// The state buffer a chain publishes H_k through: the checkpoint output when there is one,
+// else a two-deep ring per (sequence, head) in the workspace (chunk j of a sequence uses
+// entry j & 1; entry reuse is safe because chunk j+2 publishes only after chunk j+1 has
+// read H_j).
+__device__ __forceinline__ float* chain_state(const PrefillParams& p, int k, int h, int r, int j) {
+  if (p.states) return p.states + (int64_t(k) * p.H + h) * int64_t(p.P) * p.N;
+  return p.hring + ((int64_t(r) * p.H + h) * 2 + (j & 1)) * int64_t(p.P) * p.N;
+}
+
+// Row tile q of wave w (tiles w and 2NW-1-w, then the same +2NW), and the most C.B^T
+// fragments any wave needs for its q-th tile (its 32-token blocks 0 .. tile/2).
+template <int NW>
+__device__ __forceinline__ int chain_tile(int q, int w) {
+  return 2 * NW * (q / 2) + ((q & 1) ? 2 * NW - 1 - w : w);
+}
+template <int NW>
+constexpr int chain_ncb(int q) {
+  return (2 * NW * (q / 2) + ((q & 1) ? 2 * NW - 1 : NW - 1)) / 2 + 1;
+}
+
+template <int N, int CS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void k_chunk_chain(PrefillParams p) {
+  using T = bf16_t;
+  using O = Ops<T>;
+  using frag = Frag8;
+  using M = ChainCfg<N, CS>;
+  constexpr int P = M::P, NW = M::NW, NT = M::NT, NSTEP = M::NSTEP;
+  constexpr int RSX = CS, RSB = N;
+  constexpr int TP = M::TP, TNW = M::TNW, KN = M::KN, NTQ = M::NTQ;
+  constexpr int NF = M::NF;
+  constexpr int NCB = chain_ncb<NW>(NTQ - 1);     // C.B^T fragment buffer of one tile
+  __shared__ __attribute__((aligned(16))) bf16_t xT[P * RSX];   // raw x^T (swizzled)
+  __shared__ __attribute__((aligned(16))) bf16_t Hs[P * RSB];   // incoming state rows
+  __shared__ __attribute__((aligned(16))) float s_c[CS];        // cumsum
+  __shared__ __attribute__((aligned(16))) float s_d[CS];        // delta
+  __shared__ __attribute__((aligned(16))) float s_v[CS];        // block-referenced weight
+  __shared__ __attribute__((aligned(16))) float s_w[CS];        // chunk-end weight
+
+  // (chunk, head) of this workgroup
+  const int tid = threadIdx.x;
+  const int hx = (p.H + kXcds - 1) / kXcds;                    // heads per XCD and row
+  const int row = blockIdx.x / (kXcds * hx), sl = blockIdx.x % (kXcds * hx);
+  const int h = (sl % kXcds) * hx + sl / kXcds;
+  if (h >= p.H || row >= p.C) return;
+  const int k = chain_ordered(p) ? ld_meta(p.chunk_ord, row) : row;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, li = lane & 15, kg = lane >> 4;
+  const uint32_t lane_b = uint32_t(lane) * 8 * sizeof(T);
+  // one flag per (chunk, head, wave): wave w publishes (and its successor wave w reads)
+  // the state columns n of its n-tiles, [w*TNW*16, (w+1)*TNW*16) of every row p
+  int* const done = p.chain_flag;
+  auto flag_of = [&](int kk) { return done + (int64_t(kk) * p.H + h) * NW + wave; };
+
+  // the chunk, its sequence and its place in the sequence, all checked before any access
+  bool ok = k >= 0 && k < p.C;
+  int r = 0, cs0 = 0, L = 1, k0 = 0, k1 = 0;
+  if (ok) {
+    r = p.seq_idx[k];
+    ok = r >= 0 && r < p.S;
+  }
+  if (ok) {
+    k0 = r == 0 ? 0 : p.last_chunk[r - 1] + 1;
+    k1 = p.last_chunk[r];
+    cs0 = p.cu_chunk[k];
+    const int cs1 = p.cu_chunk[k + 1];
+    L = cs1 - cs0;
+    const int t0 = p.cu_seqlens[r], t1 = p.cu_seqlens[r + 1];
+    ok = k0 <= k && k <= k1 && k1 < p.C && L >= 1 && L <= CS && cs0 >= t0 && cs1 <= t1 &&
+         t0 >= 0 && t1 <= p.T && (k != k0 || cs0 == t0) && (k != k1 || cs1 == t1);
+  }
+  if (!ok) {
+    // publish anyway so that no successor waits for this workgroup
+    if (tid == 0) raise_flag(p.flag, SSD_DEVERR_CHUNK_RANGE);
+    if (lane == 0 && k >= 0 && k < p.C)
+      __hip_atomic_store(flag_of(k), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  const bool first = k == k0, last = k == k1;
+  int slot = -1;
+  if (p.pool && p.state_idx && (first || last)) {
+    slot = p.state_idx[r];
+    if (slot < 0 || slot >= p.num_slots) {
+      if (tid == 0 && first) raise_flag(p.flag, SSD_DEVERR_SLOT_RANGE);
+      slot = -1;
+    }
+  }
+  float* pool_h = slot >= 0 ? p.pool + int64_t(slot) * p.slot_stride + int64_t(h) * P * N : nullptr;
+  const int g = h / (p.H / p.G);
+  const float Dh = p.D ? p.D[h] : 0.f;
+
+  // every input of the chunk's own state at once: x rows, cumsum and delta, and all of
+  // this wave's B^T fragments
+  ChainStage<M::NI> st;
+  chain_load_stage<N, CS>(st, p, ChunkLoc{cs0, L}, k, h);
+  const BufRes btr(static_cast<const T*>(p.btw) + (int64_t(k) * p.G + g) * (int64_t(N) * CS));
+  frag btf[NSTEP][TNW];
+#pragma unroll
+  for (int ss = 0; ss < NSTEP; ++ss)
+#pragma unroll
+    for (int q = 0; q < TNW; ++q) btf[ss][q] = ld_frag<T>(btr, (wave * TNW + q) * NSTEP + ss, lane_b);
+
+  // staging: raw x^T; cumsum, delta and the two token weights
+#pragma unroll
+  for (int u = 0; u < M::NI; ++u) {
+    const int it = u * M::NTH + tid;
+    const int g8 = it % M::NG, s = 4 * (it / M::NG);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int col = 8 * g8 + j;
+      O::put4raw(&xT[col * RSX + chain_xs(col, s)], st.x[u], j);
+    }
+    if (g8 == 0) {
+      const float cv[4] = {st.c[u].x, st.c[u].y, st.c[u].z, st.c[u].w};
+      const float dv[4] = {st.d[u].x, st.d[u].y, st.d[u].z, st.d[u].w};
+      float v[4], w[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        v[t] = dv[t] * fast_exp(st.cref[u] - cv[t]);
+        w[t] = dv[t] * fast_exp(st.clast - cv[t]);
+      }
+      *reinterpret_cast<float4_v*>(&s_c[s]) = st.c[u];
+      *reinterpret_cast<float4_v*>(&s_d[s]) = st.d[u];
+      *reinterpret_cast<float4_v*>(&s_v[s]) = float4_v{v[0], v[1], v[2], v[3]};
+      *reinterpret_cast<float4_v*>(&s_w[s]) = float4_v{w[0], w[1], w[2], w[3]};
+    }
+  }
+  __syncthreads();
+
+  // the chunk's own state S^T = (B^T o w) x (one reference: the chunk end)
+  f32x4_v sacc[TNW][TP];
+#pragma unroll
+  for (int q = 0; q < TNW; ++q)
+#pragma unroll
+    for (int pt = 0; pt < TP; ++pt) sacc[q][pt] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ss = 0; ss < NSTEP; ++ss) {
+    const float4_v w0 = *reinterpret_cast<const float4_v*>(&s_w[32 * ss + 8 * kg]);
+    const float4_v w1 = *reinterpret_cast<const float4_v*>(&s_w[32 * ss + 8 * kg + 4]);
+    const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    frag a[TNW];
+#pragma unroll
+    for (int q = 0; q < TNW; ++q) a[q] = scale_frag(btf[ss][q], wv);
+#pragma unroll
+    for (int pt = 0; pt < TP; ++pt) {
+      const int pr = pt * 16 + li;
+      const frag b = O::ld8(&xT[pr * RSX + chain_xs(pr, 32 * ss + 8 * kg)]);
+#pragma unroll
+      for (int q = 0; q < TNW; ++q) sacc[q][pt] = O::mma(a[q], b, sacc[q][pt]);
+    }
+  }
+  if (p.local_states_out) {
+    const int64_t sb = (int64_t(k) * p.H + h) * (int64_t(P) * N);
+#pragma unroll
+    for (int q = 0; q < TNW; ++q)
+#pragma unroll
+      for (int pt = 0; pt < TP; ++pt)
+        st_f4(p.local_states_out + sb + (pt * 16 + li) * N + (wave * TNW + q) * 16 + 4 * kg, sacc[q][pt]);
+  }
+
+  // y^T operands, two row tiles in flight: C fragments and the tile's C.B^T fragments
+  const BufRes cbr(static_cast<const T*>(p.cbw) + (int64_t(k) * p.G + g) * (int64_t(NF) * 512));
+  const BufRes cfr(static_cast<const T*>(p.cfw) + (int64_t(k) * p.G + g) * (int64_t(NT) * KN * 512));
+  frag cf[2][KN], cb[2][NCB];
+  auto load_tile = [&](int q4) {
+    const int i = __builtin_amdgcn_readfirstlane(chain_tile<NW>(q4, wave)), bd = i / 2;
+#pragma unroll
+    for (int kk = 0; kk < KN; ++kk) cf[q4 & 1][kk] = ld_frag<T>(cfr, i * KN + kk, lane_b);
+#pragma unroll
+    for (int j = 0; j < NCB; ++j)
+      if (j < chain_ncb<NW>(q4)) cb[q4 & 1][j] = ld_frag<T>(cbr, cb_frag_base(i) + (j < bd ? j : bd), lane_b);
+  };
+
+  // the incoming state of this wave's columns: the pool slot (or zero) for a sequence's
+  // first chunk, else what the predecessor's wave published
+  const float* hin = nullptr;
+  if (first) {
+    if (pool_h && p.has_init && p.has_init[r]) hin = pool_h;
+  } else {
+    if (lane == 0) {
+      const int* f = flag_of(k - 1);
+      if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+        const long long t_start = wall_clock64();
+        while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+          if (wall_clock64() - t_start > kChainWaitTicks) {
+            raise_flag(p.flag, SSD_DEVERR_CHAIN_WAIT);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+      }
+    }
+    asm volatile("" ::: "memory");
+    hin = chain_state(p, k - 1, h, r, k - 1 - k0);
+  }
+  f32x4_v hreg[TNW][TP];
+  if (hin) {
+    // device-coherent loads (the predecessor ran on another CU)
+    const BufRes hb(hin);
+#pragma unroll
+    for (int q = 0; q < TNW; ++q)
+#pragma unroll
+      for (int pt = 0; pt < TP; ++pt) {
+        const uint32_t off = uint32_t((pt * 16 + li) * N + (wave * TNW + q) * 16 + 4 * kg) * 4;
+        const u32x4_v v = __builtin_amdgcn_raw_buffer_load_b128(hb.r, off, 0, kCohDev);
+        hreg[q][pt] = f32x4_v{__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                              __uint_as_float(v.w)};
+      }
+  } else {
+#pragma unroll
+    for (int q = 0; q < TNW; ++q)
+#pragma unroll
+      for (int pt = 0; pt < TP; ++pt) hreg[q][pt] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+  }
+  load_tile(0);
+
+  // H_k = exp(c_last) H_{k-1} + S_k for this wave's columns: stored (checkpoint, pool at the
+  // sequence end), then, once the stores are complete, the wave's flag.  H_{k-1} goes to
+  // LDS as the MFMA operand of the inter-chunk term.
+#pragma unroll
+  for (int q = 0; q < TNW; ++q)
+#pragma unroll
+    for (int pt = 0; pt < TP; ++pt)
+      O::st4lds(&Hs[(pt * 16 + li) * RSB + chain_hs(li, (wave * TNW + q) * 16 + 4 * kg)], hreg[q][pt]);
+  {
+    const float dec = fast_exp(s_c[CS - 1]);
+    const BufRes hb(chain_state(p, k, h, r, k - k0));
+    const bool to_pool = last && pool_h && p.write_final;
+#pragma unroll
+    for (int q = 0; q < TNW; ++q)
+#pragma unroll
+      for (int pt = 0; pt < TP; ++pt) {
+        const f32x4_v v = dec * hreg[q][pt] + sacc[q][pt];
+        const int off = (pt * 16 + li) * N + (wave * TNW + q) * 16 + 4 * kg;
+        if (p.states || !last)
+          __builtin_amdgcn_raw_buffer_store_b128(
+              u32x4_v{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                      __float_as_uint(v[3])}, hb.r, uint32_t(off) * 4, 0, kCohDev);
+        if (to_pool) st_f4(pool_h + off, v);
+      }
+    if (!last) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (lane == 0) __hip_atomic_store(flag_of(k), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  if (NTQ > 1) load_tile(1);
+  __syncthreads();   // H_{k-1} rows complete in LDS
+
+  // y^T, one row tile at a time
+  T* ybase = static_cast<T*>(p.y) + int64_t(cs0) * p.y_st + int64_t(h) * P;
+#pragma unroll
+  for (int q4 = 0; q4 < NTQ; ++q4) {
+    const int i = __builtin_amdgcn_readfirstlane(chain_tile<NW>(q4, wave)), bd = i / 2;
+    const int l = 16 * i + li;
+    const frag* cfq = cf[q4 & 1];
+    const frag* cbt = cb[q4 & 1];
+    // inter-chunk term: exp(c_l) H_{k-1}[p, :] . C_l
+    f32x4_v acc[TP];
+#pragma unroll
+    for (int pt = 0; pt < TP; ++pt) acc[pt] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KN; ++kk)
+#pragma unroll
+      for (int pt = 0; pt < TP; ++pt)
+        acc[pt] = O::mma(O::ld8(&Hs[(pt * 16 + li) * RSB + chain_hs(li, 32 * kk + 8 * kg)]), cfq[kk], acc[pt]);
+    {
+      const float e = fast_exp(s_c[l]);
+#pragma unroll
+      for (int pt = 0; pt < TP; ++pt) acc[pt] *= e;
+    }
+    // blocks entirely before the diagonal block, with the running rescale
+    if (bd > 0) {
+      f32x4_v acc2[TP];
+#pragma unroll
+      for (int pt = 0; pt < TP; ++pt) acc2[pt] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int b = 0; b < chain_ncb<NW>(q4) - 1; ++b) {
+        if (b >= bd) break;
+        const float al = b > 0 ? fast_exp(s_c[32 * b + 31] - s_c[32 * b - 1]) : 1.f;
+        const float4_v v0 = *reinterpret_cast<const float4_v*>(&s_v[32 * b + 8 * kg]);
+        const float4_v v1 = *reinterpret_cast<const float4_v*>(&s_v[32 * b + 8 * kg + 4]);
+        const float vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+        const frag cbs = scale_frag(cbt[b], vv);
+#pragma unroll
+        for (int pt = 0; pt < TP; ++pt) {
+          const int prow = pt * 16 + li;
+          acc2[pt] = O::mma(O::ld8(&xT[prow * RSX + chain_xs(prow, 32 * b + 8 * kg)]), cbs, acc2[pt] * al);
+        }
+      }
+      const float f = fast_exp(s_c[l] - s_c[32 * bd - 1]);
+#pragma unroll
+      for (int pt = 0; pt < TP; ++pt) acc[pt] += f * acc2[pt];
+    }
+    // the block holding the diagonal: exact decay per element, causal mask, D on the
+    // diagonal (its C.B^T fragment is entry bd, or the last loaded one when bd is smaller)
+    {
+      const int s0 = 32 * bd;
+      const float cl = s_c[l];
+      const float4_v c0 = *reinterpret_cast<const float4_v*>(&s_c[s0 + 8 * kg]);
+      const float4_v c1 = *reinterpret_cast<const float4_v*>(&s_c[s0 + 8 * kg + 4]);
+      const float4_v d0 = *reinterpret_cast<const float4_v*>(&s_d[s0 + 8 * kg]);
+      const float4_v d1 = *reinterpret_cast<const float4_v*>(&s_d[s0 + 8 * kg + 4]);
+      const float cs8[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+      const float ds8[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+      frag cbd = cbt[0];
+#pragma unroll
+      for (int j = 1; j < chain_ncb<NW>(q4); ++j)
+        if (j == bd) cbd = cbt[j];
+      float m[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int s = s0 + 8 * kg + j;
+        const float v = O::val(cbd, j) * fast_exp(cl - cs8[j]) * ds8[j] + (s == l ? Dh : 0.f);
+        m[j] = s <= l ? v : 0.f;
+      }
+      const frag mf = O::from8(m);
+#pragma unroll
+      for (int pt = 0; pt < TP; ++pt) {
+        const int prow = pt * 16 + li;
+        acc[pt] = O::mma(O::ld8(&xT[prow * RSX + chain_xs(prow, s0 + 8 * kg)]), mf, acc[pt]);
+      }
+    }
+    if (q4 + 2 < NTQ) load_tile(q4 + 2);
+    store_yt<T, 2>(ybase, p.y_st, l, L, kg, acc);
+    store_yt<T, 2>(ybase + 32, p.y_st, l, L, kg, acc + 2);
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // launch table (same order as kChunkedShapes)
 // ---------------------------------------------------------------------------------------
+
+
 template <typename T, int P, int N, int CS>
 static hipError_t run_chunked(const PrefillParams& p, hipStream_t s, void* const* ev) {
   constexpr int PW = P >= 32 ? 32 : P;
+  constexpr bool kChain = chain_supported(sizeof(T) == 2 ? SSD_BF16 : SSD_F32, P, N, CS);
+  if (kChain && !p.chain_flag) return hipErrorInvalidValue;   // the plan gives it the buffers
   record_event(ev, 0, s);
   hipLaunchKernelGGL((k_chunk_prep<T, N, CS>), dim3(p.C, p.G, prep_split(p.C * p.G)), dim3(256), 0,
                      s, p);
   record_event(ev, 1, s);
-  const MarchGrid mg = march_grid(p.S, p.G, p.H, P / PW);
-  hipLaunchKernelGGL((k_chunk_march<T, P, PW, N, CS>), dim3(mg.nblocks * mg.bsize), dim3(256), 0,
-                     s, p);
+  if constexpr (kChain) {
+    const int hx = (p.H + kXcds - 1) / kXcds;
+    hipLaunchKernelGGL((k_chunk_chain<N, CS>), dim3(p.C * kXcds * hx), dim3(64 * kChainWaves), 0,
+                       s, p);
+  } else {
+    const MarchGrid mg = march_grid(p.S, p.G, p.H, P / PW);
+    hipLaunchKernelGGL((k_chunk_march<T, P, PW, N, CS>), dim3(mg.nblocks * mg.bsize), dim3(256), 0,
+                       s, p);
+  }
   record_event(ev, 2, s);
   return hipGetLastError();
 }

@@ -107,11 +107,22 @@ def test_workspace_size_layout():
     S = 2
     prep = (_al(C * G * nfrag * 512 * 2) + _al(C * G * N * cs * 2) + _al(C * H * 2 * cs * 4)
             + _al(C * G * cs * N * 2) + _al(S * 4))
-    for over in ({}, dict(chunk_states_out=FAKE),
-                 dict(chunk_states_out=FAKE, has_initial_state=FAKE, state_pool=FAKE,
-                      state_indices=FAKE, num_slots=4, slot_stride=8 * 64 * 128)):
+    # the chunk-chain kernel (bf16, head dim 64): per (chunk, head) an int32 flag for each of
+    # its 4 wavefronts, per chunk its dispatch row, and without a chunk-state output a
+    # two-deep fp32 state ring per (sequence, head)
+    chain = _al(C * H * 4 * 4) + _al(C * 4)
+    ring = _al(S * H * 2 * P * N * 4)
+    for over, extra in (({}, ring), (dict(chunk_states_out=FAKE), 0),
+                        (dict(chunk_states_out=FAKE, has_initial_state=FAKE, state_pool=FAKE,
+                              state_indices=FAKE, num_slots=4, slot_stride=8 * 64 * 128), 0)):
         st, n = _ws(_good_prefill(**over))
-        assert st == 0 and n == prep
+        assert st == 0 and n == prep + chain + extra
+    # fp32 inputs run the march kernel: no chain buffers
+    st, n = _ws(_good_prefill(in_dtype=_abi.SSD_F32, chunk_size=64))
+    nf64 = sum(i // 2 + 1 for i in range(64 // 16))
+    C64 = 3
+    assert st == 0 and n == (_al(C64 * G * nf64 * 512 * 4) + _al(C64 * G * N * 64 * 4)
+                             + _al(C64 * H * 2 * 64 * 4) + _al(C64 * G * 64 * N * 4) + _al(S * 4))
     st, n = _ws(_good_prefill(a_kind=_abi.SSD_A_DIAG, H=64, P=1, G=1, N=16, x_stride_t=64,
                               y_stride_t=64, dt_stride_t=64, bc_stride_t=16))
     assert st == 0 and n == 0
@@ -122,7 +133,10 @@ def test_kernel_count():
     names = (ctypes.c_char_p * _abi.SSD_PREFILL_MAX_KERNELS)()
     assert lib().ssd_prefill_kernel_count(ctypes.byref(_good_prefill()), ctypes.byref(n), names) == 0
     assert n.value == 2
-    assert [names[i] for i in range(2)] == [b"k_chunk_prep", b"k_chunk_march"]
+    assert [names[i] for i in range(2)] == [b"k_chunk_prep", b"k_chunk_chain"]
+    f32 = _good_prefill(in_dtype=_abi.SSD_F32, chunk_size=64)
+    assert lib().ssd_prefill_kernel_count(ctypes.byref(f32), ctypes.byref(n), names) == 0
+    assert n.value == 2 and [names[i] for i in range(2)] == [b"k_chunk_prep", b"k_chunk_march"]
     diag = _good_prefill(a_kind=_abi.SSD_A_DIAG, H=64, P=1, G=1, N=16, x_stride_t=64,
                          y_stride_t=64, dt_stride_t=64, bc_stride_t=16)
     assert lib().ssd_prefill_kernel_count(ctypes.byref(diag), ctypes.byref(n), names) == 0
