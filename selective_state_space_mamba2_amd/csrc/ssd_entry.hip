@@ -77,7 +77,7 @@ ssd_status ssd_prefill(const ssd_prefill_args* a, void* workspace, size_t worksp
   if (plan.kind == ssd::PrefillKind::kChunked) {
     p.cbw = ws + plan.off_cb;
     p.btw = ws + plan.off_bt;
-    p.dcw = reinterpret_cast<float*>(ws + plan.off_dc);
+    p.dcw = plan.chain ? nullptr : reinterpret_cast<float*>(ws + plan.off_dc);
     p.cfw = ws + plan.off_cf;
     p.seq_ord = reinterpret_cast<int*>(ws + plan.off_ord);
     if (plan.chain) {

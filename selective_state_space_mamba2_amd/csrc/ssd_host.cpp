@@ -90,13 +90,13 @@ ssd_status plan_prefill(const ssd_prefill_args* a, PrefillPlan* plan) {
   off = align_up(off + size_t(C) * a->G * size_t(cb_frag_base(int(cs / 16))) * 512 * esz, 256);
   plan->off_bt = off;
   off = align_up(off + size_t(C) * a->G * a->N * cs * esz, 256);
-  plan->off_dc = off;
-  off = align_up(off + size_t(C) * a->H * 2 * cs * sizeof(float), 256);
+  plan->chain = chain_supported(a->in_dtype, a->P, a->N, a->chunk_size);
+  plan->off_dc = off;   // the chain kernel forms delta and the cumsum itself
+  if (!plan->chain) off = align_up(off + size_t(C) * a->H * 2 * cs * sizeof(float), 256);
   plan->off_cf = off;
   off = align_up(off + size_t(C) * a->G * cs * size_t(a->N < 32 ? 32 : a->N) * esz, 256);
   plan->off_ord = off;
   off = align_up(off + size_t(a->num_seqs) * sizeof(int32_t), 256);
-  plan->chain = chain_supported(a->in_dtype, a->P, a->N, a->chunk_size);
   if (plan->chain) {
     plan->off_flag = off;
     off = align_up(off + size_t(C) * a->H * kChainWaves * sizeof(int32_t), 256);

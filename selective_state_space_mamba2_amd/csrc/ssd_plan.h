@@ -20,7 +20,8 @@ struct PrefillPlan {
   size_t off_cb = 0;         // input dtype, per (chunk, group): the C.B^T blocks of every
                              // row tile, cb_frag_base(cs/16) fragments of 512 values
   size_t off_bt = 0;         // input dtype [C, G, N * cs]: B^T per chunk and group
-  size_t off_dc = 0;         // fp32 [C, H, 2, cs]: cumsum of delta*A, then delta
+  size_t off_dc = 0;         // fp32 [C, H, 2, cs]: cumsum of delta*A, then delta (march
+                             // kernels only)
   size_t off_cf = 0;         // input dtype [C, G, cs * max(N, 32)]: C rows as fragments
   size_t off_ord = 0;        // int32 [S]: sequence dispatch order of the march kernel
   bool chain = false;        // the chunk-chain kernel runs (else a march kernel)

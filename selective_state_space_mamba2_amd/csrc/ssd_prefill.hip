@@ -384,8 +384,8 @@ __global__ __launch_bounds__(256) void k_chunk_prep(PrefillParams p) {
     bv[u] = O::gld8(bsrc + int64_t(s) * p.bc_st + 8 * c8, s < L && 8 * c8 < N);
   }
   // meanwhile the cumsum of this workgroup's share of the group's heads, one wavefront per
-  // head, each head's dt requested one head ahead
-  {
+  // head, each head's dt requested one head ahead (the chain kernel forms its own)
+  if (!p.chain_flag) {
     const int hpg = p.H / p.G, hz = (hpg + zs - 1) / zs;
     const int h0 = g * hpg + z * hz, h1 = min(g * hpg + hpg, h0 + hz);
     float raw[4], nxt[4];
@@ -992,23 +992,14 @@ struct ChainCfg {
   static_assert(TN % NW == 0 && N % 32 == 0 && NT % NW == 0 && NITEM % NTH == 0, "shape");
 };
 
-template <int NI>
-struct ChainStage {
-  Frag8 x[NI][4];
-  float4_v c[NI], d[NI];
-  float cref[NI];
-  float clast;
-};
-
-// The chunk's x rows, cumsum and delta.  Work item `it`: columns 8*g8 .. 8*g8+7, tokens
-// 4*sg .. 4*sg+3.
-template <int N, int CS>
-__device__ __forceinline__ void chain_load_stage(ChainStage<ChainCfg<N, CS>::NI>& st,
-                                                 const PrefillParams& p, ChunkLoc c, int k, int h) {
+// The chunk's x rows.  Work item `it`: columns 8*g8 .. 8*g8+7, tokens 4*sg .. 4*sg+3.
+template <int N, int CS, int NI>
+__device__ __forceinline__ void chain_load_x(Frag8 (&x)[NI][4], const PrefillParams& p, ChunkLoc c,
+                                             int h) {
   using M = ChainCfg<N, CS>;
+  static_assert(NI == M::NI, "staging items");
   const BufRes xr(static_cast<const bf16_t*>(p.x) + int64_t(c.cs0) * p.x_st + int64_t(h) * M::P);
   const uint32_t xrow_b = uint32_t(p.x_st * int64_t(sizeof(bf16_t)));
-  const float* dc = p.dcw + (int64_t(k) * p.H + h) * (2 * CS);
 #pragma unroll
   for (int u = 0; u < M::NI; ++u) {
     const int it = u * M::NTH + int(threadIdx.x);
@@ -1017,13 +1008,9 @@ __device__ __forceinline__ void chain_load_stage(ChainStage<ChainCfg<N, CS>::NI>
     for (int t = 0; t < 4; ++t) {
       // unguarded: rows past the chunk end repeat its last row (their weight is zero)
       const int row = s + t < c.L ? s + t : c.L - 1;
-      st.x[u][t] = buf_ld8<bf16_t>(xr, uint32_t(row) * xrow_b + uint32_t(g8) * 16, 0);
+      x[u][t] = buf_ld8<bf16_t>(xr, uint32_t(row) * xrow_b + uint32_t(g8) * 16, 0);
     }
-    st.c[u] = *reinterpret_cast<const float4_v*>(dc + s);
-    st.d[u] = *reinterpret_cast<const float4_v*>(dc + CS + s);
-    st.cref[u] = dc[s | 31];
   }
-  st.clast = dc[CS - 1];
 }
 
 constexpr long long kChainWaitTicks = 100000000;   // ~1 s of the 100 MHz wall clock
@@ -1080,6 +1067,7 @@ void k_chunk_chain(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) float s_d[CS];        // delta
   __shared__ __attribute__((aligned(16))) float s_v[CS];        // block-referenced weight
   __shared__ __attribute__((aligned(16))) float s_w[CS];        // chunk-end weight
+  __shared__ float s_tot[NW];                                    // per-wave delta*A sums
 
   // (chunk, head) of this workgroup
   const int tid = threadIdx.x;
@@ -1133,10 +1121,12 @@ void k_chunk_chain(PrefillParams p) {
   const int g = h / (p.H / p.G);
   const float Dh = p.D ? p.D[h] : 0.f;
 
-  // every input of the chunk's own state at once: x rows, cumsum and delta, and all of
-  // this wave's B^T fragments
-  ChainStage<M::NI> st;
-  chain_load_stage<N, CS>(st, p, ChunkLoc{cs0, L}, k, h);
+  // every input of the chunk's own state at once: x rows, this wave's dt values (token
+  // 64*wave + lane) and all of this wave's B^T fragments
+  Frag8 xs[M::NI][4];
+  chain_load_x<N, CS, M::NI>(xs, p, ChunkLoc{cs0, L}, h);
+  const int tok = 64 * wave + lane;
+  const float dt_raw = to_f32(static_cast<const T*>(p.dt)[int64_t(cs0 + (tok < L ? tok : L - 1)) * p.dt_st + h]);
   const BufRes btr(static_cast<const T*>(p.btw) + (int64_t(k) * p.G + g) * (int64_t(N) * CS));
   frag btf[NSTEP][TNW];
 #pragma unroll
@@ -1144,7 +1134,14 @@ void k_chunk_chain(PrefillParams p) {
 #pragma unroll
     for (int q = 0; q < TNW; ++q) btf[ss][q] = ld_frag<T>(btr, (wave * TNW + q) * NSTEP + ss, lane_b);
 
-  // staging: raw x^T; cumsum, delta and the two token weights
+  // delta = clamp(softplus(dt + bias)) and the chunk-local inclusive cumsum c of delta*A:
+  // a scan inside each wave, then the earlier waves' sums (tokens at or past the chunk end
+  // have delta = 0, so c stays flat there)
+  const float dl = tok < L ? p.prep.apply(dt_raw, p.prep.bias_of(h)) : 0.f;
+  const float incl = wave_inclusive_scan(dl * p.A[h]);
+  if (lane == 63) s_tot[wave] = incl;
+
+  // staging: raw x^T
 #pragma unroll
   for (int u = 0; u < M::NI; ++u) {
     const int it = u * M::NTH + tid;
@@ -1152,21 +1149,27 @@ void k_chunk_chain(PrefillParams p) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int col = 8 * g8 + j;
-      O::put4raw(&xT[col * RSX + chain_xs(col, s)], st.x[u], j);
+      O::put4raw(&xT[col * RSX + chain_xs(col, s)], xs[u], j);
     }
-    if (g8 == 0) {
-      const float cv[4] = {st.c[u].x, st.c[u].y, st.c[u].z, st.c[u].w};
-      const float dv[4] = {st.d[u].x, st.d[u].y, st.d[u].z, st.d[u].w};
-      float v[4], w[4];
+  }
+  __syncthreads();
+  // cumsum, delta and the two token weights: v_s against the end of the token's 32-token
+  // block, w_s against the chunk end
+  {
+    float base = 0.f, clast = 0.f;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        v[t] = dv[t] * fast_exp(st.cref[u] - cv[t]);
-        w[t] = dv[t] * fast_exp(st.clast - cv[t]);
-      }
-      *reinterpret_cast<float4_v*>(&s_c[s]) = st.c[u];
-      *reinterpret_cast<float4_v*>(&s_d[s]) = st.d[u];
-      *reinterpret_cast<float4_v*>(&s_v[s]) = float4_v{v[0], v[1], v[2], v[3]};
-      *reinterpret_cast<float4_v*>(&s_w[s]) = float4_v{w[0], w[1], w[2], w[3]};
+    for (int w = 0; w < NW; ++w) {
+      if (w < wave) base += s_tot[w];
+      clast += s_tot[w];
+    }
+    const float c = incl + base;
+    const float cref = __shfl(c, lane | 31, 64);
+    if (tok < CS) {
+      s_c[tok] = c;
+      s_d[tok] = dl;
+      s_v[tok] = dl * fast_exp(cref - c);
+      s_w[tok] = dl * fast_exp(clast - c);
+      if (p.dA_cumsum_out && tok < L) p.dA_cumsum_out[int64_t(h) * p.T + cs0 + tok] = c;
     }
   }
   __syncthreads();

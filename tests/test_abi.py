@@ -105,11 +105,11 @@ def test_workspace_size_layout():
     nfrag = sum(i // 2 + 1 for i in range(cs // 16))
     assert nfrag == 72
     S = 2
-    prep = (_al(C * G * nfrag * 512 * 2) + _al(C * G * N * cs * 2) + _al(C * H * 2 * cs * 4)
-            + _al(C * G * cs * N * 2) + _al(S * 4))
-    # the chunk-chain kernel (bf16, head dim 64): per (chunk, head) an int32 flag for each of
-    # its 4 wavefronts, per chunk its dispatch row, and without a chunk-state output a
-    # two-deep fp32 state ring per (sequence, head)
+    prep = (_al(C * G * nfrag * 512 * 2) + _al(C * G * N * cs * 2) + _al(C * G * cs * N * 2)
+            + _al(S * 4))
+    # the chunk-chain kernel (bf16, head dim 64) forms delta and the cumsum itself, and has
+    # per (chunk, head) an int32 flag for each of its 4 wavefronts, per chunk its dispatch
+    # row, and without a chunk-state output a two-deep fp32 state ring per (sequence, head)
     chain = _al(C * H * 4 * 4) + _al(C * 4)
     ring = _al(S * H * 2 * P * N * 4)
     for over, extra in (({}, ring), (dict(chunk_states_out=FAKE), 0),
