@@ -108,6 +108,28 @@ def test_without_chunk_state_output_uses_workspace():
     check_prefill(inp, got, oracle_prefill(inp))
 
 
+def test_long_chain_without_state_output():
+    """Seven chunks of one sequence with no chunk-state output: the chain kernel hands the
+    state down through its two-deep workspace ring, so entries are overwritten while the
+    sequence runs; a second sequence resumes mid-chunk."""
+    inp = _case(16, "bf16", 64, 128, 128, [7 * 128 - 5, 300], [0, 77])
+    got = run_prefill(inp, want_states=False)
+    assert got["flag"] == 0
+    check_prefill(inp, got, oracle_prefill(inp))
+
+
+def test_many_short_sequences_take_chunks_in_index_order():
+    """More sequences than the prep kernel orders (1100 > 1024): the chain kernel then
+    takes chunks in index order, which also dispatches every predecessor first."""
+    rng = np.random.default_rng(17)
+    lengths = [int(v) for v in rng.integers(1, 4, size=1100)]
+    lengths[5] = 300                                  # one multi-chunk sequence in the mix
+    inp = _case(17, "bf16", 64, 128, 128, lengths, [0] * 1100, H=4, G=1, slots=1200)
+    got = run_prefill(inp)
+    assert got["flag"] == 0
+    check_prefill(inp, got, oracle_prefill(inp, seqs=[0, 5, 6, 700, 1099]))
+
+
 @pytest.mark.parametrize("dtype,cs", [("bf16", 256), ("f32", 64)])
 def test_per_step_outputs(dtype, cs):
     """The within-chunk cumsum of delta*A, C.B^T per chunk and group, and each chunk's
