@@ -950,9 +950,11 @@ void k_chunk_march(PrefillParams p) {
 // weights applied to the other MFMA operand in registers:
 //   * S_k^T = (B^T o w) x with w_s = delta_s exp(c_last - c_s): one reference point, the
 //     chunk end, so no rescaling;
-//   * y, the blocks before the diagonal block: (C.B^T o v) x with
-//     v_s = delta_s exp(c_{r(s)} - c_s) (reference: the end of the token's 32-token block),
-//     the running sum rescaled block to block and joined to row l with exp(c_l - c_ref);
+//   * y, the blocks before the diagonal block: the C.B^T fragment, whose lane holds row l,
+//     scaled per token by v_s exp(c_l - c_{r(s)}) = delta_s exp(c_l - c_s), where
+//     v_s = delta_s exp(c_{r(s)} - c_s) is formed once per chunk (reference r(s): the end of
+//     the token's 32-token block) and exp(c_l - c_{r(s)}) once per lane and block; both
+//     factors are <= 1;
 //   * y, the diagonal block: exact exp(c_l - c_s) delta_s per element, causal mask, D on
 //     the diagonal; y^T leaves straight from the accumulators.
 // Every shared fragment (B^T, C.B^T, C) feeds all four 16-row p-tiles of the head.
@@ -1315,28 +1317,22 @@ void k_chunk_chain(PrefillParams p) {
 #pragma unroll
       for (int pt = 0; pt < TP; ++pt) acc[pt] *= e;
     }
-    // blocks entirely before the diagonal block, with the running rescale
-    if (bd > 0) {
-      f32x4_v acc2[TP];
+    // blocks entirely before the diagonal block: the C.B^T fragment (lane: row l) scaled
+    // per token by v_s exp(c_l - c_{32b+31}) = delta_s exp(c_l - c_s), two factors <= 1
 #pragma unroll
-      for (int pt = 0; pt < TP; ++pt) acc2[pt] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < chain_ncb<NW>(q4) - 1; ++b) {
+      if (b >= bd) break;
+      const float gb = fast_exp(s_c[l] - s_c[32 * b + 31]);
+      const float4_v v0 = *reinterpret_cast<const float4_v*>(&s_v[32 * b + 8 * kg]);
+      const float4_v v1 = *reinterpret_cast<const float4_v*>(&s_v[32 * b + 8 * kg + 4]);
+      const float vv[8] = {v0.x * gb, v0.y * gb, v0.z * gb, v0.w * gb,
+                           v1.x * gb, v1.y * gb, v1.z * gb, v1.w * gb};
+      const frag cbs = scale_frag(cbt[b], vv);
 #pragma unroll
-      for (int b = 0; b < chain_ncb<NW>(q4) - 1; ++b) {
-        if (b >= bd) break;
-        const float al = b > 0 ? fast_exp(s_c[32 * b + 31] - s_c[32 * b - 1]) : 1.f;
-        const float4_v v0 = *reinterpret_cast<const float4_v*>(&s_v[32 * b + 8 * kg]);
-        const float4_v v1 = *reinterpret_cast<const float4_v*>(&s_v[32 * b + 8 * kg + 4]);
-        const float vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-        const frag cbs = scale_frag(cbt[b], vv);
-#pragma unroll
-        for (int pt = 0; pt < TP; ++pt) {
-          const int prow = pt * 16 + li;
-          acc2[pt] = O::mma(O::ld8(&xT[prow * RSX + chain_xs(prow, 32 * b + 8 * kg)]), cbs, acc2[pt] * al);
-        }
+      for (int pt = 0; pt < TP; ++pt) {
+        const int prow = pt * 16 + li;
+        acc[pt] = O::mma(O::ld8(&xT[prow * RSX + chain_xs(prow, 32 * b + 8 * kg)]), cbs, acc[pt]);
       }
-      const float f = fast_exp(s_c[l] - s_c[32 * bd - 1]);
-#pragma unroll
-      for (int pt = 0; pt < TP; ++pt) acc[pt] += f * acc2[pt];
     }
     // the block holding the diagonal: exact decay per element, causal mask, D on the
     // diagonal (its C.B^T fragment is entry bd, or the last loaded one when bd is smaller)
