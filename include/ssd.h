@@ -55,9 +55,12 @@ typedef enum ssd_status {
                                       its sequence                                     */
 #define SSD_DEVERR_SLOT_RANGE 2    /* a state index is outside [0, num_slots)           */
 #define SSD_DEVERR_ACCEPTED 4      /* num_accepted_tokens outside [1, ntok]            */
-#define SSD_DEVERR_CHAIN_WAIT 8    /* a chunk waited about a second for its predecessor's
-                                      state (only inconsistent chunk metadata leaves a
-                                      predecessor unprocessed); its outputs are invalid */
+#define SSD_DEVERR_CHAIN_WAIT 8    /* a chunk could not take over its predecessor's state:
+                                      it waited about a second (only inconsistent chunk
+                                      metadata leaves a predecessor unprocessed), or the
+                                      state was left in the L2 of another XCD than the one
+                                      workgroup dispatch placed the chunk on; the outputs
+                                      of that sequence are invalid                       */
 
 typedef enum ssd_dtype { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
 

@@ -1016,12 +1016,24 @@ __device__ __forceinline__ void chain_load_x(Frag8 (&x)[NI][4], const PrefillPar
 }
 
 constexpr long long kChainWaitTicks = 100000000;   // ~1 s of the 100 MHz wall clock
-// Cache policy of the published-state accesses: device-scope coherent (sc1), the policy of
-// device-scope relaxed atomics.  A store with it is performed for every CU once it
-// completes, and a load with it observes such stores, so the hand-off needs no cache
-// flush or invalidate: the publisher waits for its stores to complete before the flag
-// store, the successor issues its loads after it has seen the flag.
+// Cache policies of the published-state accesses.  Device-scope coherent (sc1) is the
+// policy of device-scope relaxed atomics: a store with it is performed for every CU once it
+// completes, and a load with it observes such stores.  Within one XCD the L2 is shared, so
+// there a plain store (complete once it is in L2) and an L1-bypassing load (sc0) suffice
+// and keep the state in L2.  The publisher picks the L2 form only when it runs on the XCD
+// its workgroup id maps to (id mod 8, where a successor's id also maps), and records its
+// XCD and the form in the flag value; a successor on that same XCD reads through L2, any
+// other reads device-coherent, and a state left in another XCD's L2 is reported
+// (SSD_DEVERR_CHAIN_WAIT).  Neither side needs a cache flush or invalidate: the publisher
+// waits for its stores to complete before the flag store, the successor issues its loads
+// after it has seen the flag.
 constexpr int kCohDev = 16;
+constexpr int kCohWg = 1;
+constexpr int kFlagLocal = 16;   // flag value - 1 = XCD id | kFlagLocal when kept in L2
+
+__device__ __forceinline__ int xcd_id() {
+  return __builtin_amdgcn_s_getreg(20 | (0 << 6) | (3 << 11)) & 15;   // HW_REG_XCC_ID[3:0]
+}
 
 // LDS tiles of the chain kernel, unpadded rows (52 KB in all, three workgroups per CU):
 // x^T [p][s] with the 8-token (16-byte) groups XOR-ed with (p ^ p >> 3) & 7, so both the
@@ -1222,15 +1234,19 @@ void k_chunk_chain(PrefillParams p) {
 
   // the incoming state of this wave's columns: the pool slot (or zero) for a sequence's
   // first chunk, else what the predecessor's wave published
+  const int my_xcd = xcd_id();
   const float* hin = nullptr;
+  bool via_l2 = false;
   if (first) {
     if (pool_h && p.has_init && p.has_init[r]) hin = pool_h;
   } else {
+    int fv = 0;
     if (lane == 0) {
       const int* f = flag_of(k - 1);
-      if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+      fv = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (fv == 0) {
         const long long t_start = wall_clock64();
-        while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+        while ((fv = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0) {
           if (wall_clock64() - t_start > kChainWaitTicks) {
             raise_flag(p.flag, SSD_DEVERR_CHAIN_WAIT);
             break;
@@ -1240,21 +1256,38 @@ void k_chunk_chain(PrefillParams p) {
       }
     }
     asm volatile("" ::: "memory");
+    const int e = __builtin_amdgcn_readfirstlane(fv) - 1;
+    via_l2 = (e & 15) == my_xcd;
+    if (!via_l2 && (e & kFlagLocal) && lane == 0) raise_flag(p.flag, SSD_DEVERR_CHAIN_WAIT);
     hin = chain_state(p, k - 1, h, r, k - 1 - k0);
   }
   f32x4_v hreg[TNW][TP];
   if (hin) {
-    // device-coherent loads (the predecessor ran on another CU)
+    // the predecessor's state through this XCD's L2, else device-coherent (a pool slot:
+    // written before this launch, either form reads it)
     const BufRes hb(hin);
+    u32x4_v hv[TNW][TP];
+    if (via_l2) {
+#pragma unroll
+      for (int q = 0; q < TNW; ++q)
+#pragma unroll
+        for (int pt = 0; pt < TP; ++pt)
+          hv[q][pt] = __builtin_amdgcn_raw_buffer_load_b128(
+              hb.r, uint32_t((pt * 16 + li) * N + (wave * TNW + q) * 16 + 4 * kg) * 4, 0, kCohWg);
+    } else {
+#pragma unroll
+      for (int q = 0; q < TNW; ++q)
+#pragma unroll
+        for (int pt = 0; pt < TP; ++pt)
+          hv[q][pt] = __builtin_amdgcn_raw_buffer_load_b128(
+              hb.r, uint32_t((pt * 16 + li) * N + (wave * TNW + q) * 16 + 4 * kg) * 4, 0, kCohDev);
+    }
 #pragma unroll
     for (int q = 0; q < TNW; ++q)
 #pragma unroll
-      for (int pt = 0; pt < TP; ++pt) {
-        const uint32_t off = uint32_t((pt * 16 + li) * N + (wave * TNW + q) * 16 + 4 * kg) * 4;
-        const u32x4_v v = __builtin_amdgcn_raw_buffer_load_b128(hb.r, off, 0, kCohDev);
-        hreg[q][pt] = f32x4_v{__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
-                              __uint_as_float(v.w)};
-      }
+      for (int pt = 0; pt < TP; ++pt)
+        hreg[q][pt] = f32x4_v{__uint_as_float(hv[q][pt].x), __uint_as_float(hv[q][pt].y),
+                              __uint_as_float(hv[q][pt].z), __uint_as_float(hv[q][pt].w)};
   } else {
 #pragma unroll
     for (int q = 0; q < TNW; ++q)
@@ -1275,21 +1308,44 @@ void k_chunk_chain(PrefillParams p) {
     const float dec = fast_exp(s_c[CS - 1]);
     const BufRes hb(chain_state(p, k, h, r, k - k0));
     const bool to_pool = last && pool_h && p.write_final;
+    // kept in this XCD's L2 when the successor maps here too (the last chunk has none)
+    const bool keep_l2 = !last && my_xcd == int(blockIdx.x % kXcds);
+    f32x4_v hn[TNW][TP];
 #pragma unroll
     for (int q = 0; q < TNW; ++q)
 #pragma unroll
-      for (int pt = 0; pt < TP; ++pt) {
-        const f32x4_v v = dec * hreg[q][pt] + sacc[q][pt];
-        const int off = (pt * 16 + li) * N + (wave * TNW + q) * 16 + 4 * kg;
-        if (p.states || !last)
-          __builtin_amdgcn_raw_buffer_store_b128(
-              u32x4_v{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
-                      __float_as_uint(v[3])}, hb.r, uint32_t(off) * 4, 0, kCohDev);
-        if (to_pool) st_f4(pool_h + off, v);
-      }
+      for (int pt = 0; pt < TP; ++pt) hn[q][pt] = dec * hreg[q][pt] + sacc[q][pt];
+    auto hoff = [&](int q, int pt) {
+      return uint32_t((pt * 16 + li) * N + (wave * TNW + q) * 16 + 4 * kg) * 4;
+    };
+    auto hbits = [&](const f32x4_v& v) {
+      return u32x4_v{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                     __float_as_uint(v[3])};
+    };
+    if (keep_l2) {
+#pragma unroll
+      for (int q = 0; q < TNW; ++q)
+#pragma unroll
+        for (int pt = 0; pt < TP; ++pt)
+          __builtin_amdgcn_raw_buffer_store_b128(hbits(hn[q][pt]), hb.r, hoff(q, pt), 0, 0);
+    } else if (p.states || !last) {
+#pragma unroll
+      for (int q = 0; q < TNW; ++q)
+#pragma unroll
+        for (int pt = 0; pt < TP; ++pt)
+          __builtin_amdgcn_raw_buffer_store_b128(hbits(hn[q][pt]), hb.r, hoff(q, pt), 0, kCohDev);
+    }
+    if (to_pool) {
+#pragma unroll
+      for (int q = 0; q < TNW; ++q)
+#pragma unroll
+        for (int pt = 0; pt < TP; ++pt) st_f4(pool_h + hoff(q, pt) / 4, hn[q][pt]);
+    }
     if (!last) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      if (lane == 0) __hip_atomic_store(flag_of(k), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (lane == 0)
+        __hip_atomic_store(flag_of(k), 1 + (my_xcd | (keep_l2 ? kFlagLocal : 0)), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   if (NTQ > 1) load_tile(1);
