@@ -399,6 +399,23 @@ __global__ __launch_bounds__(256) void k_chunk_prep(PrefillParams p) {
       cumsum_head<CS>(p, k, cs0, L, h, lane, raw);
     }
   }
+  // the C rows of this wave's first row tile, requested before the B rows are staged
+  const int li = lane & 15, kg = lane >> 4;
+  const T* csrc = static_cast<const T*>(p.Cm) + int64_t(cs0) * p.bc_st + int64_t(g) * N;
+  const int NWT = NW * zs, NQ = (NT + NWT - 1) / NWT;
+  auto tile_of = [&](int q) {   // row tiles w = z * NW + wave, then mirrored pairs
+    const int w = z * NW + wave;
+    return (q / 2) * 2 * NWT + ((q & 1) ? 2 * NWT - 1 - w : w);
+  };
+  frag cf[KN];
+  auto load_c = [&](int q) {
+    const int lrow = 16 * tile_of(q) + li;
+#pragma unroll
+    for (int kk = 0; kk < KN; ++kk)
+      cf[kk] = O::gld8(csrc + int64_t(lrow) * p.bc_st + 32 * kk + 8 * kg,
+                       lrow < L && 32 * kk + 8 * kg < N);
+  };
+  load_c(0);
 #pragma unroll
   for (int u = 0; u < NBI; ++u) {
     const int e = u * 256 + tid, s = e / (NP / 8), c8 = e % (NP / 8);
@@ -426,28 +443,19 @@ __global__ __launch_bounds__(256) void k_chunk_prep(PrefillParams p) {
   // C.B^T fragments: each 16x16 tile is computed transposed (rows s, columns l) so lane
   // (kg, li) gets C_l . B_s for l = 16 i + li, s = 16 jt + 4 kg + rr; two tiles are regrouped
   // through LDS into the 8-consecutive-s fragment of one 32-token block.
-  const int li = lane & 15, kg = lane >> 4;
-  const T* csrc = static_cast<const T*>(p.Cm) + int64_t(cs0) * p.bc_st + int64_t(g) * N;
   T* cb = static_cast<T*>(p.cbw) + (int64_t(k) * p.G + g) * (int64_t(NF) * 512);
   float* cb_dbg = p.cb_out ? p.cb_out + (int64_t(k) * p.G + g) * CS * CS : nullptr;
   float* tw = tl[wave];
-  // row tiles of this workgroup: w = z * NW + wave, then mirrored pairs balancing the
-  // causal work
-  const int NWT = NW * zs;
+  // row tiles of this workgroup (tile_of), the causal work balanced by mirrored pairs
 #pragma unroll 1
-  for (int q = 0; q < (NT + NWT - 1) / NWT; ++q) {
-    const int w = z * NW + wave;
-    const int i = (q / 2) * 2 * NWT + ((q & 1) ? 2 * NWT - 1 - w : w);
-    if (i >= NT) continue;
+  for (int q = 0; q < NQ; ++q) {
+    const int i = tile_of(q);
+    if (i >= NT) break;   // later tiles of this wave are larger still
+    if (q > 0) load_c(q);
     const int lrow = 16 * i + li;
-    frag cf[KN];
     T* cfo = static_cast<T*>(p.cfw) + ((int64_t(k) * p.G + g) * NT + i) * (KN * 512);
 #pragma unroll
-    for (int kk = 0; kk < KN; ++kk) {
-      cf[kk] = O::gld8(csrc + int64_t(lrow) * p.bc_st + 32 * kk + 8 * kg,
-                       lrow < L && 32 * kk + 8 * kg < N);
-      O::st8(cfo + (kk * 64 + lane) * 8, cf[kk]);
-    }
+    for (int kk = 0; kk < KN; ++kk) O::st8(cfo + (kk * 64 + lane) * 8, cf[kk]);
 #pragma unroll 1
     for (int b = 0; b <= i / 2; ++b) {
 #pragma unroll
