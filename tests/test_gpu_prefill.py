@@ -130,6 +130,53 @@ def test_many_short_sequences_take_chunks_in_index_order():
     check_prefill(inp, got, oracle_prefill(inp, seqs=[0, 5, 6, 700, 1099]))
 
 
+@pytest.mark.parametrize("dtype,P,N,cs", [("bf16", 64, 128, 256), ("f32", 16, 16, 64)])
+def test_graph_capture_and_replay(dtype, P, N, cs):
+    """The prefill (chain or march kernels) captured in a HIP graph, replayed several times
+    with eager work in between, gives the eager call's y, chunk states and pool on every
+    replay (the workspace's flags and counters are reset by the kernels, not by a memset)."""
+    import torch
+    from gpu_helpers import dev_f32, dev_i32, dev_token, prefill_metadata
+    from selective_state_space_mamba2_amd import api
+    inp = _case(35, dtype, P, N, cs, [3 * cs + 17, cs - 5, 2 * cs], [0, 11, cs + 3])
+    cuc, sidx, last = prefill_metadata(inp)
+    x, dt, B, C = (dev_token(inp, n) for n in ("x", "dt", "B", "C"))
+    A, D = dev_f32(inp.A), dev_f32(inp.D)
+    md = [dev_i32(inp.cu_seqlens), dev_i32(cuc), dev_i32(sidx), dev_i32(last)]
+    pool0 = torch.from_numpy(inp.pool).cuda()
+    pool = pool0.clone()
+    y = torch.zeros_like(x)
+    states = torch.zeros(len(sidx), inp.H, P, N, device="cuda")
+    kw = dict(y=y, D=D, state_pool=pool, state_indices=dev_i32(inp.state_indices),
+              has_initial_state=dev_i32(inp.has_initial_state), write_final_to_pool=True,
+              chunk_states_out=states)
+    args = api.prefill_args(x, dt, A, B, C, cs, *md, **kw)
+    ws = torch.empty(max(api.ssd_prefill_workspace_size(args), 256), dtype=torch.uint8,
+                     device="cuda")
+    api.ssd_prefill(x, dt, A, B, C, cs, *md, workspace=ws, **kw)
+    torch.cuda.synchronize()
+    y_eager, st_eager, pool_eager = y.clone(), states.clone(), pool.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            api.ssd_prefill(x, dt, A, B, C, cs, *md, workspace=ws, stream=s, **kw)
+    torch.cuda.current_stream().wait_stream(s)
+    for _ in range(3):
+        pool.copy_(pool0)
+        y.zero_()
+        states.zero_()
+        ws.fill_(255)                          # stale flags and counters from elsewhere
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager)
+        assert torch.equal(states, st_eager)
+        assert torch.equal(pool, pool_eager)
+        _ = (x.float() * 2).sum().item()       # unrelated eager work between replays
+
+
 @pytest.mark.parametrize("dtype,cs", [("bf16", 256), ("f32", 64)])
 def test_per_step_outputs(dtype, cs):
     """The within-chunk cumsum of delta*A, C.B^T per chunk and group, and each chunk's
