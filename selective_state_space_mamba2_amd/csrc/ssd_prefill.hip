@@ -1146,9 +1146,9 @@ void k_chunk_chain(PrefillParams p) {
   // every input of the chunk's own state at once: x rows, this wave's dt values (token
   // 64*wave + lane) and all of this wave's B^T fragments
   Frag8 xs[M::NI][4];
-  chain_load_x<N, CS, M::NI>(xs, p, ChunkLoc{cs0, L}, h);
   const int tok = 64 * wave + lane;
   const float dt_raw = to_f32(static_cast<const T*>(p.dt)[int64_t(cs0 + (tok < L ? tok : L - 1)) * p.dt_st + h]);
+  chain_load_x<N, CS, M::NI>(xs, p, ChunkLoc{cs0, L}, h);
   const BufRes btr(static_cast<const T*>(p.btw) + (int64_t(k) * p.G + g) * (int64_t(N) * CS));
   frag btf[NSTEP][TNW];
 #pragma unroll
