@@ -31,10 +31,10 @@ struct PrefillPlan {
                              // output is given (0 bytes otherwise)
 };
 
-// Shapes that run the chunk-chain kernel (bf16, head dim 64, dstate a multiple of 64,
-// chunks of at least 128 tokens); the others run the march kernel.
+// Shapes that run the chunk-chain kernel (bf16, head dim 64, dstate and chunk size
+// multiples of 128); the others run the march kernel.
 constexpr bool chain_supported(int dtype, int P, int N, int CS) {
-  return dtype == SSD_BF16 && P == 64 && N % 64 == 0 && CS >= 128;
+  return dtype == SSD_BF16 && P == 64 && N % 128 == 0 && CS % 128 == 0;
 }
 // Wavefronts per chunk-chain workgroup; each publishes its share of the state under a
 // flag of its own, so there are kChainWaves flags per (chunk, head).

@@ -994,6 +994,7 @@ __device__ __forceinline__ Frag8 scale_frag(const Frag8& f, const float* v) {
 
 template <int N, int CS>
 struct ChainCfg {
+  static_assert(N % 128 == 0 && CS % 128 == 0, "the LDS swizzles need 128-element rows");
   static constexpr int P = 64, NW = kChainWaves, NTH = 64 * NW, NT = CS / 16, NSTEP = CS / 32;
   static constexpr int TP = 4, TN = N / 16, TNW = TN / NW, KN = N / 32;
   static constexpr int NTQ = NT / NW;                 // row tiles per wave
@@ -1044,12 +1045,13 @@ __device__ __forceinline__ int xcd_id() {
 }
 
 // LDS tiles of the chain kernel, unpadded rows (52 KB in all, three workgroups per CU):
-// x^T [p][s] with the 8-token (16-byte) groups XOR-ed with (p ^ p >> 3) & 7, so both the
+// x^T [p][s] with the 8-token (16-byte) groups XOR-ed with (p ^ p >> 3) & 15, so the
 // staging writes (8 columns 8 apart per token group) and the fragment reads (16
-// consecutive rows) spread over all banks; the state rows [p][n] with the 8-column groups
-// XOR-ed with p & 7 (only p mod 16 matters, the p-tiles are 16 rows).
-__device__ __forceinline__ int chain_xs(int p, int s) { return s ^ ((((p >> 3) ^ p) & 7) << 3); }
-__device__ __forceinline__ int chain_hs(int pl, int n) { return n ^ ((pl & 7) << 3); }
+// consecutive rows) both reach 16 different 16-byte bank groups; the state rows [p][n]
+// with the 8-column groups XOR-ed with p & 15 (only p mod 16 matters, the p-tiles are 16
+// rows).  Rows are a multiple of 128 elements long, so the XOR stays inside the row.
+__device__ __forceinline__ int chain_xs(int p, int s) { return s ^ ((((p >> 3) ^ p) & 15) << 3); }
+__device__ __forceinline__ int chain_hs(int pl, int n) { return n ^ ((pl & 15) << 3); }
 
 // The state buffer a chain publishes H_k through: the checkpoint output when there is one,
 // else a two-deep ring per (sequence, head) in the workspace (chunk j of a sequence uses
