@@ -242,13 +242,16 @@ ssd_status ssd_prefill(const ssd_prefill_args* args, void* workspace,
  *                        pool[state_indices[r, j]] = state
  * Slot indices of live rows must be distinct across rows (a row may read the slot it
  * writes).  All ntok outputs are produced: acceptance is decided after this step.
+ * With SSD_A_DIAG the same step runs the Mamba1 recurrence of the diagonal scan above
+ * (decay exp(delta[c] A[c, n]) per channel c and state n; H channels, P == 1, G == 1,
+ * N == 16), the single-token counterpart of the Mamba1 prefill.
  * ------------------------------------------------------------------------------------- */
 typedef struct ssd_decode_args {
   int32_t B_pad;        /* rows, including padding rows                                 */
   int32_t ntok;         /* tokens per row = 1 + speculative tokens, >= 1                */
   int32_t H, P, G, N;
   int32_t in_dtype;     /* ssd_dtype of x, dt, B, C and y                                */
-  int32_t a_kind;       /* SSD_A_SCALAR only                                            */
+  int32_t a_kind;       /* SSD_A_SCALAR, or SSD_A_DIAG (Mamba1: P == 1, G == 1, N == 16) */
 
   /* token tensors (device, contiguous) */
   const void* x;        /* [B_pad, ntok, H, P] */
@@ -257,7 +260,7 @@ typedef struct ssd_decode_args {
   const void* C;        /* [B_pad, ntok, G, N] */
   void* y;              /* [B_pad, ntok, H, P] out */
 
-  const float* A;       /* [H] */
+  const float* A;       /* [H], or [H, N] for SSD_A_DIAG */
   const float* D;       /* [H] or NULL */
   const float* dt_bias; /* [H] or NULL */
   int32_t dt_softplus;
@@ -274,8 +277,9 @@ typedef struct ssd_decode_args {
                                          the update kernel (timing hook)              */
 } ssd_decode_args;
 
-/* Errors: SSD_ERR_NULL_POINTER, SSD_ERR_BAD_SHAPE, SSD_ERR_UNSUPPORTED, SSD_ERR_HIP.
- * B_pad == 0 is a no-op. */
+/* Errors: SSD_ERR_NULL_POINTER, SSD_ERR_BAD_SHAPE (also an unknown a_kind, or SSD_A_DIAG
+ * with P != 1 or G != 1), SSD_ERR_UNSUPPORTED (N, ntok or P*N outside the instantiated
+ * range), SSD_ERR_HIP.  B_pad == 0 is a no-op. */
 ssd_status ssd_state_update(const ssd_decode_args* args, ssd_stream_t stream);
 
 #ifdef __cplusplus

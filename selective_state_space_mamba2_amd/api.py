@@ -172,7 +172,7 @@ def decode_args(x, dt, A, B, C, y, state_pool, state_indices, num_accepted_token
     a = DecodeArgs()
     a.B_pad, a.ntok, a.H, a.P, a.G, a.N = B_pad, ntok, H, P, G, N
     a.in_dtype = _dtype_code(x)
-    a.a_kind = _abi.SSD_A_SCALAR
+    a.a_kind = _abi.SSD_A_SCALAR if A.dim() == 1 else _abi.SSD_A_DIAG
     a.x, a.dt, a.B, a.C, a.y = x.data_ptr(), dt.data_ptr(), B.data_ptr(), C.data_ptr(), y.data_ptr()
     a.A, a.D, a.dt_bias = A.data_ptr(), _dptr(D), _dptr(dt_bias)
     a.dt_softplus = 1 if dt_softplus else 0

@@ -126,8 +126,99 @@ static hipError_t launch_n(const DecodeParams& p, hipStream_t s, void* const* ev
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------------------
+// Mamba1 decode (diagonal A, P == 1, G == 1, N == 16): the same step with a decay
+// exp(delta[c] A[c, n]) per channel c and state n.  One thread per channel keeps the
+// channel's 16 fp32 states in registers (64 contiguous bytes of the slot, so a wavefront
+// reads and writes 4 KB in one stream); B and C of the row's tokens are shared by every
+// channel and staged in LDS.
+// ---------------------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void k_state_update_diag(DecodeParams p) {
+  constexpr int N = kDiagN;
+  __shared__ __attribute__((aligned(16))) float s_bc[kDecodeMaxTokens][2][N];
+  const int r = blockIdx.y, tid = threadIdx.x;
+  const int c = blockIdx.x * 256 + tid;
+  const int ntok = p.ntok, H = p.H;
+  const int* idx_r = p.idx + int64_t(r) * ntok;
+  if (idx_r[0] == p.null_id) return;  // padding row: nothing read, nothing written
+
+  const int acc_tok = p.num_acc ? p.num_acc[r] : 1;
+  bool bad = acc_tok < 1 || acc_tok > ntok;
+  if (!bad) {
+    for (int j = 0; j < ntok; ++j) {
+      const int s = idx_r[j];
+      bad |= (s < 0 || s >= p.num_slots);
+    }
+  }
+  if (bad) {
+    if (tid == 0 && blockIdx.x == 0)
+      raise_flag(p.flag, (acc_tok < 1 || acc_tok > ntok) ? SSD_DEVERR_ACCEPTED
+                                                         : SSD_DEVERR_SLOT_RANGE);
+    return;
+  }
+  // the source state first (read before any write), then the row's B and C
+  const bool live = c < H;
+  const int cc = live ? c : H - 1;
+  float h[N], A2[N];
+  {
+    const float4_v* src = reinterpret_cast<const float4_v*>(
+        p.pool + int64_t(idx_r[acc_tok - 1]) * p.slot_stride + int64_t(cc) * N);
+    const float4_v* ap = reinterpret_cast<const float4_v*>(p.A + int64_t(cc) * N);
+#pragma unroll
+    for (int q = 0; q < N / 4; ++q) {
+      const float4_v v = src[q], a = ap[q];
+      h[4 * q] = v.x; h[4 * q + 1] = v.y; h[4 * q + 2] = v.z; h[4 * q + 3] = v.w;
+      A2[4 * q] = a.x * kLog2e; A2[4 * q + 1] = a.y * kLog2e;
+      A2[4 * q + 2] = a.z * kLog2e; A2[4 * q + 3] = a.w * kLog2e;
+    }
+  }
+  const T* bg = static_cast<const T*>(p.B);
+  const T* cg = static_cast<const T*>(p.Cm);
+  for (int e = tid; e < ntok * 2 * N; e += 256) {
+    const int j = e / (2 * N), w = (e / N) & 1, n = e % N;
+    s_bc[j][w][n] = Elem<T>::load((w ? cg : bg) + (int64_t(r) * ntok + j) * N + n);
+  }
+  __syncthreads();
+  if (!live) return;
+
+  const T* xg = static_cast<const T*>(p.x);
+  const T* dg = static_cast<const T*>(p.dt);
+  T* yg = static_cast<T*>(p.y);
+  const float Dc = p.D ? p.D[c] : 0.f;
+  for (int j = 0; j < ntok; ++j) {
+    const int64_t tj = (int64_t(r) * ntok + j) * H + c;
+    const float delta = p.prep(Elem<T>::load(dg + tj), c);
+    const float xv = Elem<T>::load(xg + tj);
+    const float dx = delta * xv;
+    float acc = 0.f;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      h[n] = __builtin_amdgcn_exp2f(delta * A2[n]) * h[n] + dx * s_bc[j][0][n];
+      acc += s_bc[j][1][n] * h[n];
+    }
+    Elem<T>::store(yg + tj, acc + Dc * xv);
+    float4_v* dst = reinterpret_cast<float4_v*>(
+        p.pool + int64_t(idx_r[j]) * p.slot_stride + int64_t(c) * N);
+#pragma unroll
+    for (int q = 0; q < N / 4; ++q)
+      __builtin_nontemporal_store(float4_v{h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]},
+                                  dst + q);
+  }
+}
+
+template <typename T>
+static hipError_t launch_diag_update(const DecodeParams& p, hipStream_t s, void* const* ev) {
+  const dim3 grid((p.H + 255) / 256, p.B_pad);
+  record_event(ev, 0, s);
+  hipLaunchKernelGGL((k_state_update_diag<T>), grid, dim3(256), 0, s, p);
+  record_event(ev, 1, s);
+  return hipGetLastError();
+}
+
 template <typename T>
 static hipError_t launch_t(const DecodeParams& p, hipStream_t s, void* const* ev) {
+  if (p.diag) return launch_diag_update<T>(p, s, ev);
   switch (p.N) {
     case 16: return launch_n<T, 16>(p, s, ev);
     case 32: return launch_n<T, 32>(p, s, ev);

@@ -121,6 +121,7 @@ ssd_status ssd_state_update(const ssd_decode_args* a, ssd_stream_t stream) {
   if (!aligned(a->state_pool, 16) || a->slot_stride % 4) return SSD_ERR_UNSUPPORTED;
   ssd::DecodeParams p{};
   p.B_pad = a->B_pad; p.ntok = a->ntok; p.H = a->H; p.P = a->P; p.G = a->G; p.N = a->N;
+  p.diag = a->a_kind == SSD_A_DIAG ? 1 : 0;
   p.x = a->x; p.dt = a->dt; p.B = a->B; p.Cm = a->C; p.y = a->y;
   p.A = a->A; p.D = a->D;
   p.prep = ssd::DtPrep{a->dt_bias, a->dt_softplus ? 1 : 0, a->dt_min, a->dt_max};

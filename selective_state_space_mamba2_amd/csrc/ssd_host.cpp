@@ -116,10 +116,15 @@ ssd_status check_decode(const ssd_decode_args* a) {
   if (a->ntok < 1 || a->H < 1 || a->P < 1 || a->G < 1 || a->N < 1) return SSD_ERR_BAD_SHAPE;
   if (a->H % a->G != 0) return SSD_ERR_BAD_SHAPE;
   if (!valid_dtype(a->in_dtype)) return SSD_ERR_BAD_SHAPE;
-  if (a->a_kind != SSD_A_SCALAR) return SSD_ERR_UNSUPPORTED;
+  if (a->a_kind != SSD_A_SCALAR && a->a_kind != SSD_A_DIAG) return SSD_ERR_BAD_SHAPE;
   if (a->ntok > kDecodeMaxTokens) return SSD_ERR_UNSUPPORTED;
-  if (!decode_supports_n(a->N) || int64_t(a->P) * a->N > kDecodeMaxStateElems)
+  if (a->a_kind == SSD_A_DIAG) {
+    // Mamba1: one channel per head position, one B/C group, dstate 16
+    if (a->P != 1 || a->G != 1) return SSD_ERR_BAD_SHAPE;
+    if (a->N != kDiagN) return SSD_ERR_UNSUPPORTED;
+  } else if (!decode_supports_n(a->N) || int64_t(a->P) * a->N > kDecodeMaxStateElems) {
     return SSD_ERR_UNSUPPORTED;
+  }
   if (std::isnan(a->dt_min) || std::isnan(a->dt_max) || a->dt_min > a->dt_max)
     return SSD_ERR_BAD_SHAPE;
   if (a->B_pad == 0) return SSD_OK;

@@ -46,6 +46,7 @@ struct PrefillParams {
 
 struct DecodeParams {
   int B_pad, ntok, H, P, G, N;
+  int diag;            // SSD_A_DIAG: A is [H, N] (Mamba1, P == 1, G == 1)
   const void* x;
   const void* dt;
   const void* B;

@@ -122,7 +122,7 @@ class DecodeInputs:
     G: int
     N: int
     null_block_id: int
-    A: np.ndarray                    # fp32 values [H]
+    A: np.ndarray                    # fp32 values [H], or [H, N] for a diagonal A (P == 1)
     D: np.ndarray                    # fp32 values [H]
     dt: np.ndarray                   # [B_pad, ntok, H]
     x: np.ndarray                    # [B_pad, ntok, H, P]
@@ -206,10 +206,11 @@ def make_prefill(seed: int, *, in_dtype: str, H: int, P: int, G: int, N: int,
 
 def make_decode(seed: int, *, in_dtype: str = "bf16", B_pad: int, n_live: int, ntok: int,
                 H: int, P: int, G: int, N: int, pool_slots: int,
-                null_block_id: int = 0) -> DecodeInputs:
+                null_block_id: int = 0, a_kind: str = "scalar") -> DecodeInputs:
     """Draw one padded decode batch: rows [0, n_live) are live, the tail rows are padding
     whose state_indices are all ``null_block_id``.  Live rows get distinct slot indices
-    drawn from [1, pool_slots) (slot 0 is reserved), num_accepted ~ U{1..ntok}."""
+    drawn from [1, pool_slots) (slot 0 is reserved), num_accepted ~ U{1..ntok}.
+    ``a_kind`` "diag" draws A per (channel, state), [H, N] (the Mamba1 layout, P == 1)."""
     rng = np.random.default_rng(seed)
     if n_live * ntok > pool_slots - 1:
         raise ValueError("pool too small for distinct indices")
@@ -217,7 +218,8 @@ def make_decode(seed: int, *, in_dtype: str = "bf16", B_pad: int, n_live: int, n
     idx[:n_live] = (rng.permutation(pool_slots - 1)[:n_live * ntok] + 1).reshape(n_live, ntok)
     num_acc = np.ones(B_pad, dtype=np.int32)
     num_acc[:n_live] = rng.integers(1, ntok + 1, size=n_live)
-    A = (-np.exp(rng.uniform(np.log(1.0), np.log(16.0), size=H))).astype(np.float32).astype(np.float64)
+    a_shape = (H,) if a_kind == "scalar" else (H, N)
+    A = (-np.exp(rng.uniform(np.log(1.0), np.log(16.0), size=a_shape))).astype(np.float32).astype(np.float64)
     D = rng.standard_normal(H).astype(np.float32).astype(np.float64)
     dt = _softplus(rng.standard_normal((B_pad, ntok, H)) - 2.0)
     x = rng.standard_normal((B_pad, ntok, H, P))
@@ -277,6 +279,11 @@ WORKLOADS = {
     # Decode: pool [2048,48,64,128], 256 live rows of a 512-row graph batch, 1+3 tokens.
     "decode_spec": dict(kind="decode", seed=3, in_dtype="bf16", B_pad=512, n_live=256,
                         ntok=4, H=48, P=64, G=4, N=128, pool_slots=2048, null_block_id=0),
+    # Mamba1-style decode: pool [1024,5120,1,16], 256 live rows of a 512-row batch, 1+3
+    # tokens, diagonal A.
+    "mamba1_decode_spec": dict(kind="decode", seed=5, in_dtype="bf16", B_pad=512, n_live=256,
+                               ntok=4, H=5120, P=1, G=1, N=16, pool_slots=1025,
+                               null_block_id=0, a_kind="diag"),
     # Mamba1-style diagonal scan: d_inner=5120, dstate=16, 8 x 16384 tokens, cs=2048.
     "mamba1_long_diag": dict(kind="prefill", seed=4, in_dtype="bf16", H=5120, P=1, G=1,
                              N=16, chunk_size=2048, lengths=[16384] * 8, a_kind="diag"),

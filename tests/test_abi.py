@@ -228,7 +228,9 @@ def _good_decode(**over):
     (dict(H=47), _abi.SSD_ERR_BAD_SHAPE),
     (dict(N=48), _abi.SSD_ERR_UNSUPPORTED),
     (dict(P=256), _abi.SSD_ERR_UNSUPPORTED),               # P*N above the per-head limit
-    (dict(a_kind=_abi.SSD_A_DIAG), _abi.SSD_ERR_UNSUPPORTED),
+    (dict(a_kind=_abi.SSD_A_DIAG), _abi.SSD_ERR_BAD_SHAPE),      # diag needs P == G == 1
+    (dict(a_kind=_abi.SSD_A_DIAG, P=1, G=1, N=32, slot_stride=48 * 32), _abi.SSD_ERR_UNSUPPORTED),
+    (dict(a_kind=7), _abi.SSD_ERR_BAD_SHAPE),
     (dict(in_dtype=3), _abi.SSD_ERR_BAD_SHAPE),
     (dict(state_pool=None), _abi.SSD_ERR_NULL_POINTER),
     (dict(state_indices=None), _abi.SSD_ERR_NULL_POINTER),

@@ -129,3 +129,34 @@ def test_graph_capture_and_replay():
         assert torch.equal(y, y_eager)
         assert torch.equal(pool, pool_eager)
         _ = (x.float() * 2).sum().item()   # unrelated eager work between replays
+
+
+# ----------------------------------------------------------------------------------------
+# Mamba1 decode: diagonal A [H, N], P == 1, G == 1, N == 16
+
+@pytest.mark.parametrize("dtype,ntok", [("bf16", 4), ("f32", 2), ("bf16", 1)])
+def test_mamba1_diag_small_batches(dtype, ntok):
+    """300 channels (a partial block of 256), padding rows, every restore column."""
+    inp = make_decode(40 + ntok, in_dtype=dtype, B_pad=12, n_live=7, ntok=ntok, H=300, P=1,
+                      G=1, N=16, pool_slots=64, a_kind="diag")
+    got = run_decode(inp)
+    assert got["flag"] == 0
+    _check(inp, got)
+
+
+def test_mamba1_diag_softplus_bias_limit_and_no_num_accepted():
+    inp = make_decode(45, in_dtype="f32", B_pad=6, n_live=5, ntok=3, H=96, P=1, G=1, N=16,
+                      pool_slots=32, a_kind="diag", null_block_id=-1)
+    bias = np.linspace(-1.0, 1.0, inp.H)
+    kw = dict(dt_bias=bias, softplus=True, dt_limit=(0.01, 0.5))
+    got = run_decode(inp, use_acc=False, **kw)
+    assert got["flag"] == 0
+    _check(inp, got, use_acc=False, **kw)
+
+
+def test_full_mamba1_decode_workload():
+    inp = workload("mamba1_decode_spec")
+    got = run_decode(inp)
+    assert got["flag"] == 0
+    live = np.flatnonzero(inp.state_indices[:, 0] != inp.null_block_id)
+    _check(inp, got, rows=[int(live[0]), int(live[len(live) // 2]), int(live[-1])])

@@ -253,6 +253,29 @@ def test_decode_is_prefill_continued_from_the_accepted_checkpoint():
                                        rtol=1e-14, atol=1e-14)
 
 
+def test_mamba1_decode_is_the_diagonal_prefill_continued():
+    """Diagonal A [H, N] with P == 1 (the Mamba1 decode): each live row's step equals the
+    diagonal-A prefill (pinned above by brute force and lfilter) resumed from the accepted
+    checkpoint, token by token."""
+    pool, idx, acc, x, dt, _, Bm, Cm, D = _decode_case(14, H=3, P=1, N=5)
+    A = -np.exp(np.random.default_rng(15).uniform(-1, 2, size=(3, 5)))
+    y, writes = scan_decode(pool, idx, acc, x, dt, A, Bm, Cm, D, null_block_id=0)
+    assert set(y) == {0, 1, 2, 3}
+    for r in range(4):
+        ref = scan_prefill(x[r], dt[r], A, Bm[r], Cm[r], D, [0, x.shape[1]], 1,
+                           initial_states=[pool[idx[r, acc[r] - 1]]])
+        np.testing.assert_allclose(y[r], ref["y"], rtol=1e-14, atol=1e-14)
+        for j in range(x.shape[1]):
+            np.testing.assert_allclose(writes[int(idx[r, j])], ref["boundary_states"][j],
+                                       rtol=1e-14, atol=1e-14)
+    # and one state element by hand: h = exp(delta A[c, n]) h + delta x B[n]
+    r, c, n = 0, 2, 3
+    h = pool[idx[r, acc[r] - 1]][c, 0, n]
+    for j in range(x.shape[1]):
+        h = math.exp(dt[r, j, c] * A[c, n]) * h + dt[r, j, c] * x[r, j, c, 0] * Bm[r, j, 0, n]
+        assert abs(writes[int(idx[r, j])][c, 0, n] - h) <= 1e-12 * max(1.0, abs(h))
+
+
 def test_decode_reads_the_source_before_writing_it():
     """num_accepted = ntok makes the source the last column, which is also written: the
     step must start from the old contents."""
