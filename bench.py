@@ -308,12 +308,12 @@ def cpu_baseline_prefill(inp, n_seqs=2):
 # ----------------------------------------------------------------------------------------
 # decode
 # ----------------------------------------------------------------------------------------
-def bench_decode(torch, steps, warmup, with_cpu=True):
+def bench_decode(torch, steps, warmup, with_cpu=True, name="decode_spec"):
     import ctypes
     from selective_state_space_mamba2_amd import api
     from selective_state_space_mamba2_amd._abi import check, lib
     from selective_state_space_mamba2_amd.inputs import workload
-    inp = workload("decode_spec")
+    inp = workload(name)
     x, dt, B, C = (_dev_token(torch, inp, n) for n in ("x", "dt", "B", "C"))
     y = torch.empty_like(x)
     pool = torch.from_numpy(inp.pool).cuda()
@@ -341,13 +341,14 @@ def bench_decode(torch, steps, warmup, with_cpu=True):
     ms = start.elapsed_time(end) / steps
     kms = _kernel_times(ev_sets, 1)[0]
     w = decode_work(inp)
-    out = {"workload": "decode_spec", "metric": "state-updates/s",
+    kname = "k_state_update_diag" if inp.A.ndim == 2 else "k_state_update"
+    out = {"workload": name, "metric": "state-updates/s",
            "value": round(w["updates"] / (ms * 1e-3), 1), "unit": "state-updates/s",
            "ms_per_step": round(ms, 5),
            "roofline": _roofline("hbm", w["bytes"] / (kms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s",
-                                 _counter_traffic("k_state_update", "decode_spec",
+                                 _counter_traffic(kname, name,
                                                   _source_digest("ssd_decode.hip", "ssd_device.h")),
-                                 "k_state_update"),
+                                 kname),
            "kernel_ms": round(kms, 5), "alg_bytes": w["bytes"]}
     if with_cpu:
         from oracle import scan_decode
@@ -489,6 +490,11 @@ def main():
         torch.cuda.empty_cache()
         _log("mamba1_long_diag")
         line["diag"] = bench_diag(torch, max(3, args.steps // 5), max(1, args.warmup // 5))
+        torch.cuda.empty_cache()
+        _log("mamba1_decode_spec")
+        line["decode_mamba1"] = bench_decode(torch, args.steps, args.warmup,
+                                             with_cpu=not args.no_cpu_baseline,
+                                             name="mamba1_decode_spec")
     print(json.dumps(line), flush=True)
 
 

@@ -128,17 +128,19 @@ static hipError_t launch_n(const DecodeParams& p, hipStream_t s, void* const* ev
 
 // ---------------------------------------------------------------------------------------
 // Mamba1 decode (diagonal A, P == 1, G == 1, N == 16): the same step with a decay
-// exp(delta[c] A[c, n]) per channel c and state n.  One thread per channel keeps the
-// channel's 16 fp32 states in registers (64 contiguous bytes of the slot, so a wavefront
-// reads and writes 4 KB in one stream); B and C of the row's tokens are shared by every
+// exp(delta[c] A[c, n]) per channel c and state n.  Four adjacent lanes own one channel,
+// four states each, so every state load and store of a wavefront is 1 KB contiguous in
+// the slot; y is a 4-lane reduction.  B and C of the row's tokens are shared by every
 // channel and staged in LDS.
 // ---------------------------------------------------------------------------------------
+constexpr int kDiagDecodeChannels = 64;   // channels per 256-thread workgroup
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_state_update_diag(DecodeParams p) {
-  constexpr int N = kDiagN;
+  constexpr int N = kDiagN, SPL = 4;
   __shared__ __attribute__((aligned(16))) float s_bc[kDecodeMaxTokens][2][N];
   const int r = blockIdx.y, tid = threadIdx.x;
-  const int c = blockIdx.x * 256 + tid;
+  const int c = blockIdx.x * kDiagDecodeChannels + tid / SPL, q = tid % SPL;
   const int ntok = p.ntok, H = p.H;
   const int* idx_r = p.idx + int64_t(r) * ntok;
   if (idx_r[0] == p.null_id) return;  // padding row: nothing read, nothing written
@@ -160,19 +162,10 @@ __global__ __launch_bounds__(256) void k_state_update_diag(DecodeParams p) {
   // the source state first (read before any write), then the row's B and C
   const bool live = c < H;
   const int cc = live ? c : H - 1;
-  float h[N], A2[N];
-  {
-    const float4_v* src = reinterpret_cast<const float4_v*>(
-        p.pool + int64_t(idx_r[acc_tok - 1]) * p.slot_stride + int64_t(cc) * N);
-    const float4_v* ap = reinterpret_cast<const float4_v*>(p.A + int64_t(cc) * N);
-#pragma unroll
-    for (int q = 0; q < N / 4; ++q) {
-      const float4_v v = src[q], a = ap[q];
-      h[4 * q] = v.x; h[4 * q + 1] = v.y; h[4 * q + 2] = v.z; h[4 * q + 3] = v.w;
-      A2[4 * q] = a.x * kLog2e; A2[4 * q + 1] = a.y * kLog2e;
-      A2[4 * q + 2] = a.z * kLog2e; A2[4 * q + 3] = a.w * kLog2e;
-    }
-  }
+  float4_v h = *reinterpret_cast<const float4_v*>(
+      p.pool + int64_t(idx_r[acc_tok - 1]) * p.slot_stride + int64_t(cc) * N + SPL * q);
+  const float4_v a = *reinterpret_cast<const float4_v*>(p.A + int64_t(cc) * N + SPL * q);
+  const float A2[SPL] = {a.x * kLog2e, a.y * kLog2e, a.z * kLog2e, a.w * kLog2e};
   const T* bg = static_cast<const T*>(p.B);
   const T* cg = static_cast<const T*>(p.Cm);
   for (int e = tid; e < ntok * 2 * N; e += 256) {
@@ -180,7 +173,7 @@ __global__ __launch_bounds__(256) void k_state_update_diag(DecodeParams p) {
     s_bc[j][w][n] = Elem<T>::load((w ? cg : bg) + (int64_t(r) * ntok + j) * N + n);
   }
   __syncthreads();
-  if (!live) return;
+  if (!live) return;   // whole 4-lane groups leave together
 
   const T* xg = static_cast<const T*>(p.x);
   const T* dg = static_cast<const T*>(p.dt);
@@ -191,25 +184,25 @@ __global__ __launch_bounds__(256) void k_state_update_diag(DecodeParams p) {
     const float delta = p.prep(Elem<T>::load(dg + tj), c);
     const float xv = Elem<T>::load(xg + tj);
     const float dx = delta * xv;
-    float acc = 0.f;
-#pragma unroll
-    for (int n = 0; n < N; ++n) {
-      h[n] = __builtin_amdgcn_exp2f(delta * A2[n]) * h[n] + dx * s_bc[j][0][n];
-      acc += s_bc[j][1][n] * h[n];
-    }
-    Elem<T>::store(yg + tj, acc + Dc * xv);
-    float4_v* dst = reinterpret_cast<float4_v*>(
-        p.pool + int64_t(idx_r[j]) * p.slot_stride + int64_t(c) * N);
-#pragma unroll
-    for (int q = 0; q < N / 4; ++q)
-      __builtin_nontemporal_store(float4_v{h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]},
-                                  dst + q);
+    const float4_v bv = *reinterpret_cast<const float4_v*>(&s_bc[j][0][SPL * q]);
+    const float4_v cv = *reinterpret_cast<const float4_v*>(&s_bc[j][1][SPL * q]);
+    h.x = __builtin_amdgcn_exp2f(delta * A2[0]) * h.x + dx * bv.x;
+    h.y = __builtin_amdgcn_exp2f(delta * A2[1]) * h.y + dx * bv.y;
+    h.z = __builtin_amdgcn_exp2f(delta * A2[2]) * h.z + dx * bv.z;
+    h.w = __builtin_amdgcn_exp2f(delta * A2[3]) * h.w + dx * bv.w;
+    float acc = cv.x * h.x + cv.y * h.y + cv.z * h.z + cv.w * h.w;
+    acc += __shfl_xor(acc, 1, 64);
+    acc += __shfl_xor(acc, 2, 64);
+    if (q == 0) Elem<T>::store(yg + tj, acc + Dc * xv);
+    __builtin_nontemporal_store(
+        h, reinterpret_cast<float4_v*>(p.pool + int64_t(idx_r[j]) * p.slot_stride +
+                                       int64_t(c) * N + SPL * q));
   }
 }
 
 template <typename T>
 static hipError_t launch_diag_update(const DecodeParams& p, hipStream_t s, void* const* ev) {
-  const dim3 grid((p.H + 255) / 256, p.B_pad);
+  const dim3 grid((p.H + kDiagDecodeChannels - 1) / kDiagDecodeChannels, p.B_pad);
   record_event(ev, 0, s);
   hipLaunchKernelGGL((k_state_update_diag<T>), grid, dim3(256), 0, s, p);
   record_event(ev, 1, s);
