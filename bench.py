@@ -78,9 +78,9 @@ def prefill_work(inp, cuc, sidx):
             "k_chunk_prep/chain": k_prep_chain, "path": path}
 
 
-def decode_work(inp):
+def decode_work(inp, state_bytes=4):
     b = 2 if inp.in_dtype == "bf16" else 4
-    st = inp.H * inp.P * inp.N * 4
+    st = inp.H * inp.P * inp.N * state_bytes
     tok = inp.ntok * (2 * inp.H * inp.P * b + inp.H * b + 2 * inp.G * inp.N * b)
     return dict(bytes=inp.n_live * ((1 + inp.ntok) * st + tok), updates=inp.n_live * inp.ntok)
 
@@ -308,7 +308,7 @@ def cpu_baseline_prefill(inp, n_seqs=2):
 # ----------------------------------------------------------------------------------------
 # decode
 # ----------------------------------------------------------------------------------------
-def bench_decode(torch, steps, warmup, with_cpu=True, name="decode_spec"):
+def bench_decode(torch, steps, warmup, with_cpu=True, name="decode_spec", pool_bf16=False):
     import ctypes
     from selective_state_space_mamba2_amd import api
     from selective_state_space_mamba2_amd._abi import check, lib
@@ -317,6 +317,8 @@ def bench_decode(torch, steps, warmup, with_cpu=True, name="decode_spec"):
     x, dt, B, C = (_dev_token(torch, inp, n) for n in ("x", "dt", "B", "C"))
     y = torch.empty_like(x)
     pool = torch.from_numpy(inp.pool).cuda()
+    if pool_bf16:
+        pool = pool.to(torch.bfloat16)
     idx = torch.from_numpy(inp.state_indices).cuda()
     acc = torch.from_numpy(inp.num_accepted).cuda()
     A = torch.tensor(inp.A, dtype=torch.float32).cuda()
@@ -340,13 +342,14 @@ def bench_decode(torch, steps, warmup, with_cpu=True, name="decode_spec"):
         torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
     kms = _kernel_times(ev_sets, 1)[0]
-    w = decode_work(inp)
+    w = decode_work(inp, 2 if pool_bf16 else 4)
     kname = "k_state_update_diag" if inp.A.ndim == 2 else "k_state_update"
-    out = {"workload": name, "metric": "state-updates/s",
+    out = {"workload": name + (" (bf16 state pool)" if pool_bf16 else ""),
+           "metric": "state-updates/s",
            "value": round(w["updates"] / (ms * 1e-3), 1), "unit": "state-updates/s",
            "ms_per_step": round(ms, 5),
            "roofline": _roofline("hbm", w["bytes"] / (kms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s",
-                                 _counter_traffic(kname, name,
+                                 None if pool_bf16 else _counter_traffic(kname, name,
                                                   _source_digest("ssd_decode.hip", "ssd_device.h")),
                                  kname),
            "kernel_ms": round(kms, 5), "alg_bytes": w["bytes"]}
@@ -495,6 +498,10 @@ def main():
         line["decode_mamba1"] = bench_decode(torch, args.steps, args.warmup,
                                              with_cpu=not args.no_cpu_baseline,
                                              name="mamba1_decode_spec")
+        torch.cuda.empty_cache()
+        _log("decode_spec, bf16 state pool")
+        line["decode_bf16_pool"] = bench_decode(torch, args.steps, args.warmup, with_cpu=False,
+                                                pool_bf16=True)
     print(json.dumps(line), flush=True)
 
 

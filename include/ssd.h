@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 1
+#define SSD_ABI_VERSION 2
 
 typedef enum ssd_status {
   SSD_OK = 0,
@@ -177,9 +177,9 @@ typedef struct ssd_prefill_args {
   const int32_t* last_chunk_indices; /* [S]   */
 
   /* state pool (device, fp32, [num_slots, H, P, N] with slot_stride elements between
-   * slots, slot_stride >= H*P*N).  May be NULL when no sequence has an initial state and
-   * write_final_to_pool == 0. */
-  float* state_pool;
+   * slots, slot_stride >= H*P*N), in state_dtype.  May be NULL when no sequence has an
+   * initial state and write_final_to_pool == 0. */
+  void* state_pool;
   int64_t slot_stride;
   int32_t num_slots;
   const int32_t* state_indices;      /* [S] slot per sequence (device); NULL only without a pool */
@@ -203,6 +203,13 @@ typedef struct ssd_prefill_args {
    * the last one; entries past the kernels this call launches are not touched.  The number
    * of kernels launched is reported by ssd_prefill_kernel_count. */
   void* const* profile_events;
+
+  /* ssd_dtype of state_pool: SSD_F32 (0, so a zero-initialised struct keeps fp32) or
+   * SSD_BF16 (a bf16 pool, the reduced-precision SSM state dtype of "vLLM Mamba2 SSD kernel
+   * warm-up", mamba_mixer2.py section): states are read from and written to the pool in
+   * that dtype (round to nearest even) and carried in fp32 everywhere else; chunk_states_out
+   * stays fp32. */
+  int32_t state_dtype;
 } ssd_prefill_args;
 
 #define SSD_PREFILL_MAX_KERNELS 2
@@ -266,7 +273,7 @@ typedef struct ssd_decode_args {
   int32_t dt_softplus;
   float dt_min, dt_max;
 
-  float* state_pool;    /* [num_slots, H, P, N] fp32, slot_stride >= H*P*N */
+  void* state_pool;     /* [num_slots, H, P, N] in state_dtype, slot_stride >= H*P*N */
   int64_t slot_stride;
   int32_t num_slots;
   const int32_t* state_indices;       /* [B_pad, ntok] (device) */
@@ -275,6 +282,8 @@ typedef struct ssd_decode_args {
   int32_t* device_error_flag;         /* NULL or an int32 receiving SSD_DEVERR_* bits */
   void* const* profile_events;        /* NULL or 2 hipEvent_t recorded before and after
                                          the update kernel (timing hook)              */
+  int32_t state_dtype;                /* ssd_dtype of state_pool: SSD_F32 (0) or SSD_BF16;
+                                         the state is carried in fp32 inside the step  */
 } ssd_decode_args;
 
 /* Errors: SSD_ERR_NULL_POINTER, SSD_ERR_BAD_SHAPE (also an unknown a_kind, or SSD_A_DIAG

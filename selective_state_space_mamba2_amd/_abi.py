@@ -54,7 +54,7 @@ class PrefillArgs(ctypes.Structure):
         ("state_indices", _vp), ("has_initial_state", _vp), ("write_final_to_pool", _i32),
         ("chunk_states_out", _vp), ("device_error_flag", _vp),
         ("dA_cumsum_out", _vp), ("cb_out", _vp), ("chunk_local_states_out", _vp),
-        ("profile_events", _vp),
+        ("profile_events", _vp), ("state_dtype", _i32),
     ]
 
 
@@ -71,6 +71,7 @@ class DecodeArgs(ctypes.Structure):
         ("state_pool", _vp), ("slot_stride", _i64), ("num_slots", _i32),
         ("state_indices", _vp), ("num_accepted_tokens", _vp),
         ("null_block_id", _i32), ("device_error_flag", _vp), ("profile_events", _vp),
+        ("state_dtype", _i32),
     ]
 
 

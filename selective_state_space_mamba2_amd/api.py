@@ -123,6 +123,7 @@ def prefill_args(x, dt, A, B, C, chunk_size: int, cu_seqlens, cu_chunk_seqlens, 
         a.state_pool = state_pool.data_ptr()
         a.slot_stride = state_pool.stride(0)
         a.num_slots = state_pool.shape[0]
+        a.state_dtype = _dtype_code(state_pool)
     a.state_indices = _dptr(state_indices)
     a.has_initial_state = _dptr(has_initial_state)
     a.write_final_to_pool = 1 if write_final_to_pool else 0
@@ -180,6 +181,7 @@ def decode_args(x, dt, A, B, C, y, state_pool, state_indices, num_accepted_token
     a.state_pool = state_pool.data_ptr()
     a.slot_stride = state_pool.stride(0)
     a.num_slots = state_pool.shape[0]
+    a.state_dtype = _dtype_code(state_pool)
     a.state_indices = state_indices.data_ptr()
     a.num_accepted_tokens = _dptr(num_accepted_tokens)
     a.null_block_id = int(null_block_id)

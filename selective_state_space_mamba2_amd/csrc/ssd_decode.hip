@@ -15,7 +15,7 @@
 
 namespace ssd {
 
-template <typename T, int N, int ITERS>
+template <typename T, typename S, int N, int ITERS>
 __global__ __launch_bounds__(256) void k_state_update(DecodeParams p) {
   constexpr int NQ = N / 4;          // float4 per state row
   constexpr int RP = 256 / NQ;       // state rows covered per iteration
@@ -44,13 +44,12 @@ __global__ __launch_bounds__(256) void k_state_update(DecodeParams p) {
   // is in flight while the small per-token inputs are staged.
   const int lane_q = tid % NQ, prow = tid / NQ;
   const int64_t head_off = int64_t(h) * P * N;
-  const float4_v* src = reinterpret_cast<const float4_v*>(
-      p.pool + int64_t(idx_r[acc_tok - 1]) * p.slot_stride + head_off);
+  const int64_t src = int64_t(idx_r[acc_tok - 1]) * p.slot_stride + head_off;
   float4_v st[ITERS];
 #pragma unroll
   for (int i = 0; i < ITERS; ++i) {
     const int pr = i * RP + prow;
-    st[i] = pr < P ? src[pr * NQ + lane_q] : float4_v{0.f, 0.f, 0.f, 0.f};
+    st[i] = pr < P ? PoolIO<S>::ld4(p.pool, src + pr * N + 4 * lane_q) : float4_v{0.f, 0.f, 0.f, 0.f};
   }
   // Stage this row's token data for head h: x[ntok][P], B[ntok][N], C[ntok][N], delta.
   // B and C first: N is a multiple of 16, so their float4 reads stay 16-byte aligned.
@@ -85,8 +84,7 @@ __global__ __launch_bounds__(256) void k_state_update(DecodeParams p) {
     const float decay = fast_exp(delta * Ah);
     const float4_v bv = *reinterpret_cast<const float4_v*>(bs + j * N + 4 * lane_q);
     const float4_v cv = *reinterpret_cast<const float4_v*>(cs + j * N + 4 * lane_q);
-    float4_v* dst = reinterpret_cast<float4_v*>(
-        p.pool + int64_t(idx_r[j]) * p.slot_stride + head_off);
+    const int64_t dst = int64_t(idx_r[j]) * p.slot_stride + head_off;
 #pragma unroll
     for (int i = 0; i < ITERS; ++i) {
       const int pr = i * RP + prow;
@@ -98,7 +96,7 @@ __global__ __launch_bounds__(256) void k_state_update(DecodeParams p) {
       for (int off = NQ / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
       if (pr < P) {
         if (lane_q == 0) ys[j * P + pr] = part + Dh * xp;
-        __builtin_nontemporal_store(st[i], dst + pr * NQ + lane_q);
+        PoolIO<S>::st4_nt(p.pool, dst + pr * N + 4 * lane_q, st[i]);
       }
     }
   }
@@ -110,18 +108,18 @@ __global__ __launch_bounds__(256) void k_state_update(DecodeParams p) {
   }
 }
 
-template <typename T, int N>
+template <typename T, typename S, int N>
 static hipError_t launch_n(const DecodeParams& p, hipStream_t s, void* const* ev) {
   const int rows_per_iter = 256 / (N / 4);
   const int iters = (p.P + rows_per_iter - 1) / rows_per_iter;
   const dim3 grid(p.H, p.B_pad);
   const size_t lds = decode_lds_bytes(p.ntok, p.P, N);
   record_event(ev, 0, s);
-  if (iters <= 1) hipLaunchKernelGGL((k_state_update<T, N, 1>), grid, dim3(256), lds, s, p);
-  else if (iters <= 2) hipLaunchKernelGGL((k_state_update<T, N, 2>), grid, dim3(256), lds, s, p);
-  else if (iters <= 4) hipLaunchKernelGGL((k_state_update<T, N, 4>), grid, dim3(256), lds, s, p);
-  else if (iters <= 8) hipLaunchKernelGGL((k_state_update<T, N, 8>), grid, dim3(256), lds, s, p);
-  else hipLaunchKernelGGL((k_state_update<T, N, 16>), grid, dim3(256), lds, s, p);
+  if (iters <= 1) hipLaunchKernelGGL((k_state_update<T, S, N, 1>), grid, dim3(256), lds, s, p);
+  else if (iters <= 2) hipLaunchKernelGGL((k_state_update<T, S, N, 2>), grid, dim3(256), lds, s, p);
+  else if (iters <= 4) hipLaunchKernelGGL((k_state_update<T, S, N, 4>), grid, dim3(256), lds, s, p);
+  else if (iters <= 8) hipLaunchKernelGGL((k_state_update<T, S, N, 8>), grid, dim3(256), lds, s, p);
+  else hipLaunchKernelGGL((k_state_update<T, S, N, 16>), grid, dim3(256), lds, s, p);
   record_event(ev, 1, s);
   return hipGetLastError();
 }
@@ -135,7 +133,7 @@ static hipError_t launch_n(const DecodeParams& p, hipStream_t s, void* const* ev
 // ---------------------------------------------------------------------------------------
 constexpr int kDiagDecodeChannels = 64;   // channels per 256-thread workgroup
 
-template <typename T>
+template <typename T, typename S>
 __global__ __launch_bounds__(256) void k_state_update_diag(DecodeParams p) {
   constexpr int N = kDiagN, SPL = 4;
   __shared__ __attribute__((aligned(16))) float s_bc[kDecodeMaxTokens][2][N];
@@ -162,8 +160,7 @@ __global__ __launch_bounds__(256) void k_state_update_diag(DecodeParams p) {
   // the source state first (read before any write), then the row's B and C
   const bool live = c < H;
   const int cc = live ? c : H - 1;
-  float4_v h = *reinterpret_cast<const float4_v*>(
-      p.pool + int64_t(idx_r[acc_tok - 1]) * p.slot_stride + int64_t(cc) * N + SPL * q);
+  float4_v h = PoolIO<S>::ld4(p.pool, int64_t(idx_r[acc_tok - 1]) * p.slot_stride + int64_t(cc) * N + SPL * q);
   const float4_v a = *reinterpret_cast<const float4_v*>(p.A + int64_t(cc) * N + SPL * q);
   const float A2[SPL] = {a.x * kLog2e, a.y * kLog2e, a.z * kLog2e, a.w * kLog2e};
   const T* bg = static_cast<const T*>(p.B);
@@ -194,36 +191,36 @@ __global__ __launch_bounds__(256) void k_state_update_diag(DecodeParams p) {
     acc += __shfl_xor(acc, 1, 64);
     acc += __shfl_xor(acc, 2, 64);
     if (q == 0) Elem<T>::store(yg + tj, acc + Dc * xv);
-    __builtin_nontemporal_store(
-        h, reinterpret_cast<float4_v*>(p.pool + int64_t(idx_r[j]) * p.slot_stride +
-                                       int64_t(c) * N + SPL * q));
+    PoolIO<S>::st4_nt(p.pool, int64_t(idx_r[j]) * p.slot_stride + int64_t(c) * N + SPL * q, h);
   }
 }
 
-template <typename T>
+template <typename T, typename S>
 static hipError_t launch_diag_update(const DecodeParams& p, hipStream_t s, void* const* ev) {
   const dim3 grid((p.H + kDiagDecodeChannels - 1) / kDiagDecodeChannels, p.B_pad);
   record_event(ev, 0, s);
-  hipLaunchKernelGGL((k_state_update_diag<T>), grid, dim3(256), 0, s, p);
+  hipLaunchKernelGGL((k_state_update_diag<T, S>), grid, dim3(256), 0, s, p);
   record_event(ev, 1, s);
   return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, typename S>
 static hipError_t launch_t(const DecodeParams& p, hipStream_t s, void* const* ev) {
-  if (p.diag) return launch_diag_update<T>(p, s, ev);
+  if (p.diag) return launch_diag_update<T, S>(p, s, ev);
   switch (p.N) {
-    case 16: return launch_n<T, 16>(p, s, ev);
-    case 32: return launch_n<T, 32>(p, s, ev);
-    case 64: return launch_n<T, 64>(p, s, ev);
-    case 128: return launch_n<T, 128>(p, s, ev);
-    default: return launch_n<T, 256>(p, s, ev);
+    case 16: return launch_n<T, S, 16>(p, s, ev);
+    case 32: return launch_n<T, S, 32>(p, s, ev);
+    case 64: return launch_n<T, S, 64>(p, s, ev);
+    case 128: return launch_n<T, S, 128>(p, s, ev);
+    default: return launch_n<T, S, 256>(p, s, ev);
   }
 }
 
 hipError_t launch_state_update(int in_dtype, const DecodeParams& p, hipStream_t s,
                                void* const* events) {
-  return in_dtype == SSD_BF16 ? launch_t<bf16_t>(p, s, events) : launch_t<float>(p, s, events);
+  if (in_dtype == SSD_BF16)
+    return p.pool_bf16 ? launch_t<bf16_t, bf16_t>(p, s, events) : launch_t<bf16_t, float>(p, s, events);
+  return p.pool_bf16 ? launch_t<float, bf16_t>(p, s, events) : launch_t<float, float>(p, s, events);
 }
 
 }  // namespace ssd

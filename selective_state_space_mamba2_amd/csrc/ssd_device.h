@@ -57,6 +57,45 @@ template <> struct Elem<bf16_t> {
   static __device__ __forceinline__ void store(bf16_t* p, float v) { *p = f32_to_bf16(v); }
 };
 
+// Four consecutive pool states: fp32 in memory, or bf16 (round to nearest even on store).
+template <typename S> struct PoolIO;
+template <> struct PoolIO<float> {
+  static __device__ __forceinline__ float4_v ld4(const void* base, int64_t e) {
+    return *reinterpret_cast<const float4_v*>(static_cast<const float*>(base) + e);
+  }
+  static __device__ __forceinline__ void st4(void* base, int64_t e, float4_v v) {
+    *reinterpret_cast<float4_v*>(static_cast<float*>(base) + e) = v;
+  }
+  static __device__ __forceinline__ void st4_nt(void* base, int64_t e, float4_v v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<float4_v*>(static_cast<float*>(base) + e));
+  }
+};
+template <> struct PoolIO<bf16_t> {
+  static __device__ __forceinline__ float4_v ld4(const void* base, int64_t e) {
+    const u32x2_v v = *reinterpret_cast<const u32x2_v*>(static_cast<const bf16_t*>(base) + e);
+    return float4_v{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                    __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u)};
+  }
+  static __device__ __forceinline__ void st4(void* base, int64_t e, float4_v v) {
+    *reinterpret_cast<u32x2_v*>(static_cast<bf16_t*>(base) + e) =
+        u32x2_v{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
+  }
+  static __device__ __forceinline__ void st4_nt(void* base, int64_t e, float4_v v) {
+    __builtin_nontemporal_store(u32x2_v{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)},
+                                reinterpret_cast<u32x2_v*>(static_cast<bf16_t*>(base) + e));
+  }
+};
+__device__ __forceinline__ float4_v as_float4(f32x4_v v) { return float4_v{v[0], v[1], v[2], v[3]}; }
+// The same with the pool dtype chosen at run time (kernels that touch the pool only at a
+// sequence's first and last chunk).
+__device__ __forceinline__ float4_v pool_ld4(const void* base, int bf16, int64_t e) {
+  return bf16 ? PoolIO<bf16_t>::ld4(base, e) : PoolIO<float>::ld4(base, e);
+}
+__device__ __forceinline__ void pool_st4(void* base, int bf16, int64_t e, float4_v v) {
+  if (bf16) PoolIO<bf16_t>::st4(base, e, v);
+  else PoolIO<float>::st4(base, e, v);
+}
+
 // delta from raw dt: + bias, optional softplus, clamp.
 struct DtPrep {
   const float* bias;

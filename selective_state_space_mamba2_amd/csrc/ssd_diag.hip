@@ -30,6 +30,7 @@ namespace ssd {
 // workgroup owns CH = 256 / (16/SPL) channels.
 template <typename T, int SPL>
 struct DiagCfg {
+  static_assert(SPL % 4 == 0, "states move to and from the pool four at a time");
   static constexpr int N = kDiagN, LPC = N / SPL, CH = 256 / LPC;
 };
 
@@ -80,9 +81,12 @@ __global__ __launch_bounds__(256) void k_diag_scan(PrefillParams p) {
 #pragma unroll
     for (int i = 0; i < SPL; ++i) A2[i] = p.A[c * N + ng * SPL + i] * kLog2e;
     if (slot >= 0 && p.has_init && p.has_init[r]) {
-      const float* src = p.pool + int64_t(slot) * p.slot_stride + int64_t(c) * N + ng * SPL;
+      const int64_t e = int64_t(slot) * p.slot_stride + int64_t(c) * N + ng * SPL;
 #pragma unroll
-      for (int i = 0; i < SPL; ++i) h[i] = src[i];
+      for (int i = 0; i < SPL; i += 4) {
+        const float4_v v = pool_ld4(p.pool, p.pool_bf16, e + i);
+        h[i] = v.x; h[i + 1] = v.y; h[i + 2] = v.z; h[i + 3] = v.w;
+      }
     }
   } else {
 #pragma unroll
@@ -218,9 +222,10 @@ __global__ __launch_bounds__(256) void k_diag_scan(PrefillParams p) {
   }
   if (k != klast + 1 && tid == 0 && cb == 0) raise_flag(p.flag, SSD_DEVERR_CHUNK_RANGE);
   if (valid && p.write_final && slot >= 0) {
-    float* dst = p.pool + int64_t(slot) * p.slot_stride + int64_t(c) * N + ng * SPL;
+    const int64_t e = int64_t(slot) * p.slot_stride + int64_t(c) * N + ng * SPL;
 #pragma unroll
-    for (int i = 0; i < SPL; ++i) dst[i] = h[i];
+    for (int i = 0; i < SPL; i += 4)
+      pool_st4(p.pool, p.pool_bf16, e + i, float4_v{h[i], h[i + 1], h[i + 2], h[i + 3]});
   }
 }
 

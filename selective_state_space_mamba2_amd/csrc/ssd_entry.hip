@@ -66,6 +66,7 @@ ssd_status ssd_prefill(const ssd_prefill_args* a, void* workspace, size_t worksp
   p.cu_seqlens = a->cu_seqlens; p.cu_chunk = a->cu_chunk_seqlens;
   p.seq_idx = a->seq_idx; p.last_chunk = a->last_chunk_indices;
   p.pool = a->state_pool; p.slot_stride = a->slot_stride; p.num_slots = a->num_slots;
+  p.pool_bf16 = a->state_dtype == SSD_BF16 ? 1 : 0;
   p.state_idx = a->state_indices; p.has_init = a->has_initial_state;
   p.write_final = (a->write_final_to_pool && a->state_pool) ? 1 : 0;
   p.flag = a->device_error_flag;
@@ -126,6 +127,7 @@ ssd_status ssd_state_update(const ssd_decode_args* a, ssd_stream_t stream) {
   p.A = a->A; p.D = a->D;
   p.prep = ssd::DtPrep{a->dt_bias, a->dt_softplus ? 1 : 0, a->dt_min, a->dt_max};
   p.pool = a->state_pool; p.slot_stride = a->slot_stride; p.num_slots = a->num_slots;
+  p.pool_bf16 = a->state_dtype == SSD_BF16 ? 1 : 0;
   p.idx = a->state_indices; p.num_acc = a->num_accepted_tokens;
   p.null_id = a->null_block_id; p.flag = a->device_error_flag;
   const hipError_t e = ssd::launch_state_update(a->in_dtype, p, static_cast<hipStream_t>(stream),

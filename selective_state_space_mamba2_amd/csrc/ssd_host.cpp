@@ -57,6 +57,7 @@ ssd_status plan_prefill(const ssd_prefill_args* a, PrefillPlan* plan) {
   }
   if (std::isnan(a->dt_min) || std::isnan(a->dt_max) || a->dt_min > a->dt_max)
     return SSD_ERR_BAD_SHAPE;
+  if (!valid_dtype(a->state_dtype)) return SSD_ERR_BAD_SHAPE;
 
   const int64_t C = a->num_chunks;
   if (a->a_kind == SSD_A_DIAG) {
@@ -117,6 +118,7 @@ ssd_status check_decode(const ssd_decode_args* a) {
   if (a->H % a->G != 0) return SSD_ERR_BAD_SHAPE;
   if (!valid_dtype(a->in_dtype)) return SSD_ERR_BAD_SHAPE;
   if (a->a_kind != SSD_A_SCALAR && a->a_kind != SSD_A_DIAG) return SSD_ERR_BAD_SHAPE;
+  if (!valid_dtype(a->state_dtype)) return SSD_ERR_BAD_SHAPE;
   if (a->ntok > kDecodeMaxTokens) return SSD_ERR_UNSUPPORTED;
   if (a->a_kind == SSD_A_DIAG) {
     // Mamba1: one channel per head position, one B/C group, dstate 16

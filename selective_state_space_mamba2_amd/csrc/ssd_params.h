@@ -25,7 +25,8 @@ struct PrefillParams {
   const int* cu_chunk;
   const int* seq_idx;
   const int* last_chunk;
-  float* pool; int64_t slot_stride; int num_slots;
+  void* pool; int64_t slot_stride; int num_slots;
+  int pool_bf16;       // the pool holds bf16 states (else fp32)
   const int* state_idx;
   const int* has_init;
   int write_final;
@@ -55,7 +56,8 @@ struct DecodeParams {
   const float* A;
   const float* D;
   DtPrep prep;
-  float* pool; int64_t slot_stride; int num_slots;
+  void* pool; int64_t slot_stride; int num_slots;
+  int pool_bf16;       // the pool holds bf16 states (else fp32)
   const int* idx;
   const int* num_acc;
   int null_id;

@@ -644,13 +644,13 @@ void k_chunk_march(PrefillParams p) {
       slot = -1;
     }
   }
-  float* pool_h = slot >= 0 ? p.pool + int64_t(slot) * p.slot_stride + (int64_t(h) * P + p0) * N
-                            : nullptr;
+  // element offset of this workgroup's state slice in the pool (-1: no pool slot)
+  const int64_t pool_e = slot >= 0 ? int64_t(slot) * p.slot_stride + (int64_t(h) * P + p0) * N : -1;
 
   // the state slice, held transposed (the MFMA result layout of B^T X~): lane holds
   // H[p0 + pt*16 + li][nt*16 + 4*kg + rr], nt = wave*TNW + q, i.e. 4 consecutive n of one row
   f32x4_v hreg[TNW][TPW];
-  const bool init = pool_h && p.has_init && p.has_init[r];
+  const bool init = pool_e >= 0 && p.has_init && p.has_init[r];
 #pragma unroll
   for (int q = 0; q < TNW; ++q)
 #pragma unroll
@@ -658,7 +658,7 @@ void k_chunk_march(PrefillParams p) {
       const int nt = wave * TNW + q;
       hreg[q][pt] = f32x4_v{0.f, 0.f, 0.f, 0.f};
       if (init && nt < TN) {
-        const float4_v v = *reinterpret_cast<const float4_v*>(pool_h + (pt * 16 + li) * N + nt * 16 + 4 * kg);
+        const float4_v v = pool_ld4(p.pool, p.pool_bf16, pool_e + (pt * 16 + li) * N + nt * 16 + 4 * kg);
         hreg[q][pt] = f32x4_v{v.x, v.y, v.z, v.w};
       }
     }
@@ -933,13 +933,14 @@ void k_chunk_march(PrefillParams p) {
   }
 
   // final state back to the pool slot (read at the start by this same workgroup)
-  if (pool_h && p.write_final) {
+  if (pool_e >= 0 && p.write_final) {
 #pragma unroll
     for (int q = 0; q < TNW; ++q) {
       const int nt = wave * TNW + q;
       if (nt >= TN) continue;
 #pragma unroll
-      for (int pt = 0; pt < TPW; ++pt) st_f4(pool_h + (pt * 16 + li) * N + nt * 16 + 4 * kg, hreg[q][pt]);
+      for (int pt = 0; pt < TPW; ++pt)
+        pool_st4(p.pool, p.pool_bf16, pool_e + (pt * 16 + li) * N + nt * 16 + 4 * kg, as_float4(hreg[q][pt]));
     }
   }
 }
@@ -1141,7 +1142,8 @@ void k_chunk_chain(PrefillParams p) {
       slot = -1;
     }
   }
-  float* pool_h = slot >= 0 ? p.pool + int64_t(slot) * p.slot_stride + int64_t(h) * P * N : nullptr;
+  // element offset of this head's state in the pool slot (-1: no pool slot)
+  const int64_t pool_e = slot >= 0 ? int64_t(slot) * p.slot_stride + int64_t(h) * P * N : -1;
   const int g = h / (p.H / p.G);
   const float Dh = p.D ? p.D[h] : 0.f;
 
@@ -1247,9 +1249,8 @@ void k_chunk_chain(PrefillParams p) {
   const int my_xcd = xcd_id();
   const float* hin = nullptr;
   bool via_l2 = false;
-  if (first) {
-    if (pool_h && p.has_init && p.has_init[r]) hin = pool_h;
-  } else {
+  const bool from_pool = first && pool_e >= 0 && p.has_init && p.has_init[r];
+  if (!first) {
     int fv = 0;
     if (lane == 0) {
       const int* f = flag_of(k - 1);
@@ -1272,9 +1273,18 @@ void k_chunk_chain(PrefillParams p) {
     hin = chain_state(p, k - 1, h, r, k - 1 - k0);
   }
   f32x4_v hreg[TNW][TP];
-  if (hin) {
-    // the predecessor's state through this XCD's L2, else device-coherent (a pool slot:
-    // written before this launch, either form reads it)
+  if (from_pool) {
+    // a pool slot (fp32 or bf16), written before this launch
+#pragma unroll
+    for (int q = 0; q < TNW; ++q)
+#pragma unroll
+      for (int pt = 0; pt < TP; ++pt) {
+        const float4_v v = pool_ld4(p.pool, p.pool_bf16,
+                                    pool_e + (pt * 16 + li) * N + (wave * TNW + q) * 16 + 4 * kg);
+        hreg[q][pt] = f32x4_v{v.x, v.y, v.z, v.w};
+      }
+  } else if (hin) {
+    // the predecessor's state through this XCD's L2, else device-coherent
     const BufRes hb(hin);
     u32x4_v hv[TNW][TP];
     if (via_l2) {
@@ -1317,7 +1327,7 @@ void k_chunk_chain(PrefillParams p) {
   {
     const float dec = fast_exp(s_c[CS - 1]);
     const BufRes hb(chain_state(p, k, h, r, k - k0));
-    const bool to_pool = last && pool_h && p.write_final;
+    const bool to_pool = last && pool_e >= 0 && p.write_final;
     // kept in this XCD's L2 when the successor maps here too (the last chunk has none)
     const bool keep_l2 = !last && my_xcd == int(blockIdx.x % kXcds);
     f32x4_v hn[TNW][TP];
@@ -1349,7 +1359,8 @@ void k_chunk_chain(PrefillParams p) {
 #pragma unroll
       for (int q = 0; q < TNW; ++q)
 #pragma unroll
-        for (int pt = 0; pt < TP; ++pt) st_f4(pool_h + hoff(q, pt) / 4, hn[q][pt]);
+        for (int pt = 0; pt < TP; ++pt)
+          pool_st4(p.pool, p.pool_bf16, pool_e + hoff(q, pt) / 4, as_float4(hn[q][pt]));
     }
     if (!last) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");

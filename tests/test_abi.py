@@ -34,7 +34,7 @@ def test_every_declared_function_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert lib().ssd_abi_version() == 1
+    assert lib().ssd_abi_version() == 2
     for s in range(8):
         assert lib().ssd_status_string(s)
     assert lib().ssd_status_string(99) == b"unknown status"
@@ -152,6 +152,7 @@ def test_kernel_count():
     (dict(chunk_size=0), _abi.SSD_ERR_BAD_SHAPE),
     (dict(in_dtype=7), _abi.SSD_ERR_BAD_SHAPE),
     (dict(a_kind=5), _abi.SSD_ERR_BAD_SHAPE),
+    (dict(state_dtype=2), _abi.SSD_ERR_BAD_SHAPE),
     (dict(num_chunks=1), _abi.SSD_ERR_BAD_SHAPE),         # fewer chunks than sequences
     (dict(num_chunks=600), _abi.SSD_ERR_BAD_SHAPE),       # more chunks than tokens
     (dict(T=1), _abi.SSD_ERR_BAD_SHAPE),                  # fewer tokens than sequences
@@ -231,6 +232,7 @@ def _good_decode(**over):
     (dict(a_kind=_abi.SSD_A_DIAG), _abi.SSD_ERR_BAD_SHAPE),      # diag needs P == G == 1
     (dict(a_kind=_abi.SSD_A_DIAG, P=1, G=1, N=32, slot_stride=48 * 32), _abi.SSD_ERR_UNSUPPORTED),
     (dict(a_kind=7), _abi.SSD_ERR_BAD_SHAPE),
+    (dict(state_dtype=3), _abi.SSD_ERR_BAD_SHAPE),
     (dict(in_dtype=3), _abi.SSD_ERR_BAD_SHAPE),
     (dict(state_pool=None), _abi.SSD_ERR_NULL_POINTER),
     (dict(state_indices=None), _abi.SSD_ERR_NULL_POINTER),

@@ -25,6 +25,22 @@ def test_small_diag_with_pool_and_checkpoints(dtype):
             np.testing.assert_array_equal(got["pool"][s], inp.pool[s])
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_diag_bf16_state_pool(dtype):
+    """The Mamba1 scan gathering from and writing back to a bf16 pool."""
+    from gpu_helpers import TOL, bf16_pool
+    inp = bf16_pool(make_prefill(43, in_dtype=dtype, H=200, P=1, G=1, N=16, chunk_size=128,
+                                 lengths=[300, 77], num_computed=[0, 5], a_kind="diag",
+                                 init="pool", pool_slots=8))
+    got = run_prefill(inp)
+    assert got["flag"] == 0
+    check_prefill(inp, got, oracle_prefill(inp), pool_tol=TOL["bf16"])
+    owned = set(int(v) for v in inp.state_indices)
+    for s in range(8):
+        if s not in owned:
+            np.testing.assert_array_equal(got["pool"][s], inp.pool[s])
+
+
 def test_diag_several_checkpoints_per_token_tile():
     """chunk_size 24 with unaligned resume points: several chunk ends fall inside one
     32-token tile of the scan, so groups of tokens restart at unaligned positions."""
