@@ -15,10 +15,15 @@
 
 namespace ssd {
 
+// States per lane of the decode kernel: 16 bytes of the pool per lane, i.e. 4 fp32 or 8 bf16.
+template <typename S>
+constexpr int decode_vec() { return sizeof(S) == 2 ? 8 : 4; }
+
 template <typename T, typename S, int N, int ITERS>
 __global__ __launch_bounds__(256) void k_state_update(DecodeParams p) {
-  constexpr int NQ = N / 4;          // float4 per state row
-  constexpr int RP = 256 / NQ;       // state rows covered per iteration
+  constexpr int V = decode_vec<S>();   // consecutive states n of one row p per lane
+  constexpr int NQ = N / V;            // lanes per state row
+  constexpr int RP = 256 / NQ;         // state rows covered per iteration
   extern __shared__ __attribute__((aligned(16))) float lds[];
   const int h = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
   const int ntok = p.ntok, P = p.P, H = p.H;
@@ -40,16 +45,22 @@ __global__ __launch_bounds__(256) void k_state_update(DecodeParams p) {
     return;
   }
 
-  // Gather the source state before any write; it is requested first so the 32 KB stream
+  // Gather the source state before any write; it is requested first so the state stream
   // is in flight while the small per-token inputs are staged.
   const int lane_q = tid % NQ, prow = tid / NQ;
   const int64_t head_off = int64_t(h) * P * N;
   const int64_t src = int64_t(idx_r[acc_tok - 1]) * p.slot_stride + head_off;
-  float4_v st[ITERS];
+  float st[ITERS][V];
 #pragma unroll
   for (int i = 0; i < ITERS; ++i) {
     const int pr = i * RP + prow;
-    st[i] = pr < P ? PoolIO<S>::ld4(p.pool, src + pr * N + 4 * lane_q) : float4_v{0.f, 0.f, 0.f, 0.f};
+    const int64_t e = src + (pr < P ? pr : 0) * N + V * lane_q;
+    if constexpr (V == 8) {
+      PoolIO<S>::ld8(p.pool, e, st[i]);
+    } else {
+      const float4_v v = PoolIO<S>::ld4(p.pool, e);
+      st[i][0] = v.x; st[i][1] = v.y; st[i][2] = v.z; st[i][3] = v.w;
+    }
   }
   // Stage this row's token data for head h: x[ntok][P], B[ntok][N], C[ntok][N], delta.
   // B and C first: N is a multiple of 16, so their float4 reads stay 16-byte aligned.
@@ -82,21 +93,33 @@ __global__ __launch_bounds__(256) void k_state_update(DecodeParams p) {
   for (int j = 0; j < ntok; ++j) {
     const float delta = ds[j];
     const float decay = fast_exp(delta * Ah);
-    const float4_v bv = *reinterpret_cast<const float4_v*>(bs + j * N + 4 * lane_q);
-    const float4_v cv = *reinterpret_cast<const float4_v*>(cs + j * N + 4 * lane_q);
+    float bv[V], cv[V];
+#pragma unroll
+    for (int v4 = 0; v4 < V; v4 += 4) {
+      const float4_v b4 = *reinterpret_cast<const float4_v*>(bs + j * N + V * lane_q + v4);
+      const float4_v c4 = *reinterpret_cast<const float4_v*>(cs + j * N + V * lane_q + v4);
+      bv[v4] = b4.x; bv[v4 + 1] = b4.y; bv[v4 + 2] = b4.z; bv[v4 + 3] = b4.w;
+      cv[v4] = c4.x; cv[v4 + 1] = c4.y; cv[v4 + 2] = c4.z; cv[v4 + 3] = c4.w;
+    }
     const int64_t dst = int64_t(idx_r[j]) * p.slot_stride + head_off;
 #pragma unroll
     for (int i = 0; i < ITERS; ++i) {
       const int pr = i * RP + prow;
       const float xp = pr < P ? xs[j * P + pr] : 0.f;
       const float dx = delta * xp;
-      st[i] = decay * st[i] + dx * bv;
-      float part = st[i].x * cv.x + st[i].y * cv.y + st[i].z * cv.z + st[i].w * cv.w;
+      float part = 0.f;
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        st[i][v] = decay * st[i][v] + dx * bv[v];
+        part += st[i][v] * cv[v];
+      }
 #pragma unroll
       for (int off = NQ / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
       if (pr < P) {
         if (lane_q == 0) ys[j * P + pr] = part + Dh * xp;
-        PoolIO<S>::st4_nt(p.pool, dst + pr * N + 4 * lane_q, st[i]);
+        const int64_t e = dst + pr * N + V * lane_q;
+        if constexpr (V == 8) PoolIO<S>::st8_nt(p.pool, e, st[i]);
+        else PoolIO<S>::st4_nt(p.pool, e, float4_v{st[i][0], st[i][1], st[i][2], st[i][3]});
       }
     }
   }
@@ -110,7 +133,7 @@ __global__ __launch_bounds__(256) void k_state_update(DecodeParams p) {
 
 template <typename T, typename S, int N>
 static hipError_t launch_n(const DecodeParams& p, hipStream_t s, void* const* ev) {
-  const int rows_per_iter = 256 / (N / 4);
+  const int rows_per_iter = 256 / (N / decode_vec<S>());
   const int iters = (p.P + rows_per_iter - 1) / rows_per_iter;
   const dim3 grid(p.H, p.B_pad);
   const size_t lds = decode_lds_bytes(p.ntok, p.P, N);

@@ -84,6 +84,21 @@ template <> struct PoolIO<bf16_t> {
     __builtin_nontemporal_store(u32x2_v{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)},
                                 reinterpret_cast<u32x2_v*>(static_cast<bf16_t*>(base) + e));
   }
+  // eight consecutive states (16 bytes)
+  static __device__ __forceinline__ void ld8(const void* base, int64_t e, float* v) {
+    const u32x4_v w = *reinterpret_cast<const u32x4_v*>(static_cast<const bf16_t*>(base) + e);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(ws[i] << 16);
+      v[2 * i + 1] = __uint_as_float(ws[i] & 0xffff0000u);
+    }
+  }
+  static __device__ __forceinline__ void st8_nt(void* base, int64_t e, const float* v) {
+    __builtin_nontemporal_store(u32x4_v{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                        pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])},
+                                reinterpret_cast<u32x4_v*>(static_cast<bf16_t*>(base) + e));
+  }
 };
 __device__ __forceinline__ float4_v as_float4(f32x4_v v) { return float4_v{v[0], v[1], v[2], v[3]}; }
 // The same with the pool dtype chosen at run time (kernels that touch the pool only at a

@@ -120,6 +120,9 @@ ssd_status ssd_state_update(const ssd_decode_args* a, ssd_stream_t stream) {
   if (a->B_pad == 0) return SSD_OK;
   if (ssd::decode_lds_bytes(a->ntok, a->P, a->N) > 64 * 1024) return SSD_ERR_UNSUPPORTED;
   if (!aligned(a->state_pool, 16) || a->slot_stride % 4) return SSD_ERR_UNSUPPORTED;
+  // A bf16 pool is moved 8 states (16 bytes) per lane by the dense-A kernel.
+  if (a->state_dtype == SSD_BF16 && a->a_kind == SSD_A_SCALAR && a->slot_stride % 8)
+    return SSD_ERR_UNSUPPORTED;
   ssd::DecodeParams p{};
   p.B_pad = a->B_pad; p.ntok = a->ntok; p.H = a->H; p.P = a->P; p.G = a->G; p.N = a->N;
   p.diag = a->a_kind == SSD_A_DIAG ? 1 : 0;

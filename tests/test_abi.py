@@ -240,6 +240,7 @@ def _good_decode(**over):
     (dict(num_slots=0), _abi.SSD_ERR_BAD_SHAPE),
     (dict(dt_min=2.0, dt_max=1.0), _abi.SSD_ERR_BAD_SHAPE),
     (dict(state_pool=FAKE + 4), _abi.SSD_ERR_UNSUPPORTED),
+    (dict(state_dtype=_abi.SSD_BF16, slot_stride=48 * 64 * 128 + 4), _abi.SSD_ERR_UNSUPPORTED),
 ])
 def test_decode_host_checks(over, status):
     a = _good_decode(**over)
