@@ -35,6 +35,12 @@ What it computes, and where that is defined
   padded with NULL_BLOCK_ID skipped, and the restore checkpoint chosen by
   num_accepted_tokens ("[vLLM] Mamba (SSM)": metadata dataclass, MetadataBuilder init,
   CUDA Graph support section, and "why this design", items 2 and 4).
+* "all" cache mode (prefix caching, same page: the MetadataBuilder init keeps one state
+  index per cache block, and the metadata carries block_idx_first_scheduled_token,
+  block_idx_last_computed_token and block_idx_last_scheduled_token).  The pages give the
+  names only; the reading used here: a token at absolute position t of its sequence
+  belongs to block t // block_size, the state after a block's last token is that block's
+  entry, and a partial block's entry holds the state after its last processed token.
 
 Everything is computed in float64 from inputs upcast exactly from their stored dtype.
 No blocking, fusion or reordering is applied: tokens are visited one at a time.
@@ -48,6 +54,7 @@ import numpy as np
 
 __all__ = [
     "transform_dt", "scan_prefill", "scan_decode", "chunk_metadata", "group_of_head",
+    "block_indices",
 ]
 
 
@@ -92,7 +99,7 @@ def _step(h: np.ndarray, delta: np.ndarray, A: np.ndarray, x: np.ndarray,
 def scan_prefill(x, dt, A, B, C, D, cu_seqlens, chunk_size: int,
                  num_computed=None, initial_states=None, dt_bias=None,
                  dt_softplus: bool = False, dt_min: float = 0.0,
-                 dt_max: float = math.inf):
+                 dt_max: float = math.inf, block_size: Optional[int] = None):
     """Sequential varlen prefill.
 
     x [T, H, P]; dt [T, H]; A [H] or [H, N]; B, C [T, G, N]; D [H] or None;
@@ -106,6 +113,9 @@ def scan_prefill(x, dt, A, B, C, D, cu_seqlens, chunk_size: int,
                                           chunk order (sequence-major)
       boundary_ends   [K]                 token offset one past each recorded token
       final_states    [S, H, P, N]
+      block_states    list of (sequence r, block column b, [H, P, N]) for every new token
+                      that closes a cache block (absolute position + 1 a multiple of
+                      block_size), in token order; empty unless block_size is given
     """
     x = np.asarray(x, dtype=np.float64)
     T, H, P = x.shape
@@ -121,7 +131,7 @@ def scan_prefill(x, dt, A, B, C, D, cu_seqlens, chunk_size: int,
     nc_all = [0] * S if num_computed is None else [int(v) for v in num_computed]
 
     y = np.zeros((T, H, P))
-    boundary, ends, finals = [], [], []
+    boundary, ends, finals, blocks = [], [], [], []
     for r in range(S):
         t0, t1 = cu[r], cu[r + 1]
         h = np.zeros((H, P, N))
@@ -133,18 +143,22 @@ def scan_prefill(x, dt, A, B, C, D, cu_seqlens, chunk_size: int,
             if (absolute + 1) % chunk_size == 0 or t == t1 - 1:
                 boundary.append(h.copy())
                 ends.append(t + 1)
+            if block_size and (absolute + 1) % block_size == 0:
+                blocks.append((r, absolute // block_size, h.copy()))
         finals.append(h.copy())
     return {
         "y": y,
         "boundary_states": np.array(boundary).reshape(-1, H, P, N),
         "boundary_ends": np.array(ends, dtype=np.int64),
         "final_states": np.array(finals).reshape(S, H, P, N),
+        "block_states": blocks,
     }
 
 
 def scan_decode(pool, state_indices, num_accepted, x, dt, A, B, C, D,
                 null_block_id: int, dt_bias=None, dt_softplus: bool = False,
-                dt_min: float = 0.0, dt_max: float = math.inf, rows=None):
+                dt_min: float = 0.0, dt_max: float = math.inf, rows=None,
+                block_idx_last_computed=None, block_idx_last_scheduled=None):
     """Padded, speculative decode step.
 
     pool [slots, H, P, N] (read only; never modified here); state_indices [B_pad, ntok];
@@ -157,11 +171,21 @@ def scan_decode(pool, state_indices, num_accepted, x, dt, A, B, C, D,
     for each token j the recurrence advances it, y[r, j] is produced and slot
     state_indices[r, j] receives the state after token j.
 
+    "all" cache mode (block_idx_last_computed and block_idx_last_scheduled given, one
+    token per row): state_indices is [B_pad, max_blocks], one entry per cache block; the
+    row is padding when its destination entry state_indices[r, last_scheduled[r]] is
+    null_block_id; the state is read from state_indices[r, last_computed[r]] and the state
+    after the token is written to the destination entry.
+
     Returns (y, writes): y is a dict row -> [ntok, H, P] for the live rows, writes is a
     dict slot -> [H, P, N] with the state each written slot must hold.
     """
     idx = np.asarray(state_indices)
-    B_pad, ntok = idx.shape
+    all_mode = block_idx_last_scheduled is not None
+    B_pad = idx.shape[0]
+    ntok = np.asarray(x).shape[1]
+    if all_mode and (ntok != 1 or num_accepted is not None):
+        raise ValueError("the all cache mode decodes one token per row")
     x = np.asarray(x, dtype=np.float64)
     H, P = x.shape[2], x.shape[3]
     G = B.shape[2]
@@ -171,16 +195,22 @@ def scan_decode(pool, state_indices, num_accepted, x, dt, A, B, C, D,
     delta = transform_dt(dt, dt_bias, dt_softplus, dt_min, dt_max)
     y_rows, writes = {}, {}
     for r in (range(B_pad) if rows is None else rows):
-        if int(idx[r, 0]) == null_block_id:
+        if all_mode:
+            dst = [int(idx[r, int(block_idx_last_scheduled[r])])]
+            src = int(idx[r, int(block_idx_last_computed[r])]) if dst[0] != null_block_id else 0
+        else:
+            a = 1 if num_accepted is None else int(num_accepted[r])
+            dst = [int(idx[r, j]) for j in range(ntok)]
+            src = int(idx[r, a - 1])
+        if dst[0] == null_block_id:
             continue
-        a = 1 if num_accepted is None else int(num_accepted[r])
-        h = np.array(pool[int(idx[r, a - 1])], dtype=np.float64)
+        h = np.array(pool[src], dtype=np.float64)
         ys = np.zeros((ntok, H, P))
         for j in range(ntok):
             Bj = np.asarray(B[r, j], dtype=np.float64)[gmap]
             Cj = np.asarray(C[r, j], dtype=np.float64)[gmap]
             h, ys[j] = _step(h, delta[r, j], A, x[r, j], Bj, Cj, D)
-            writes[int(idx[r, j])] = h.copy()
+            writes[dst[j]] = h.copy()
         y_rows[r] = ys
     return y_rows, writes
 
@@ -213,3 +243,22 @@ def chunk_metadata(cu_seqlens: Sequence[int], num_computed: Optional[Sequence[in
         last.append(len(owner) - 1)
     return (np.array(cuts, dtype=np.int32), np.array(owner, dtype=np.int32),
             np.array(last, dtype=np.int32))
+
+
+def block_indices(num_computed: Sequence[int], new_tokens: Sequence[int], block_size: int):
+    """Cache-block columns of a batch in the "all" cache mode.
+
+    For a sequence with nc tokens already processed and L new ones, with token t of the
+    sequence in block t // block_size:
+      first_scheduled = block of the first new token (position nc)
+      last_computed   = block of the last processed token (position nc - 1), -1 if nc == 0
+      last_scheduled  = block of the last new token (position nc + L - 1)
+    Returns the three int32 arrays.
+    """
+    nc = [int(v) for v in num_computed]
+    L = [int(v) for v in new_tokens]
+    first = [n // block_size for n in nc]
+    last_comp = [(n - 1) // block_size if n > 0 else -1 for n in nc]
+    last_sched = [(n + l - 1) // block_size for n, l in zip(nc, L)]
+    return (np.array(first, dtype=np.int32), np.array(last_comp, dtype=np.int32),
+            np.array(last_sched, dtype=np.int32))

@@ -15,7 +15,7 @@ import numpy as np
 import pytest
 import scipy.signal
 
-from oracle import chunk_metadata, scan_decode, scan_prefill, transform_dt
+from oracle import block_indices, chunk_metadata, scan_decode, scan_prefill, transform_dt
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -294,6 +294,95 @@ def test_decode_null_rows_touch_nothing():
     y, writes = scan_decode(pool, idx, acc, x, dt, A, Bm, Cm, D, null_block_id=-1)
     assert set(y) == {0, 1, 2, 3}
     assert set(writes) == set(int(v) for v in idx[:4].ravel())
+
+
+# ----------------------------------------------------------------------------------------
+# "all" cache mode (one state entry per cache block)
+
+def _block_of_by_counting(t, bs):
+    """Block of absolute position t, found by counting the block ends before it (no
+    division)."""
+    return sum(1 for e in range(1, t + 1) if e % bs == 0)
+
+
+@pytest.mark.parametrize("bs", [1, 3, 4, 8])
+def test_block_indices_by_walking_tokens(bs):
+    nc = [0, 1, 3, 4, 5, 7, 8, 16]
+    L = [1, 3, 1, 4, 11, 1, 8, 2]
+    first, last_comp, last_sched = block_indices(nc, L, bs)
+    for r in range(len(nc)):
+        new_blocks = [_block_of_by_counting(t, bs) for t in range(nc[r], nc[r] + L[r])]
+        old_blocks = [_block_of_by_counting(t, bs) for t in range(nc[r])]
+        assert first[r] == min(new_blocks) and last_sched[r] == max(new_blocks)
+        assert last_comp[r] == (max(old_blocks) if old_blocks else -1)
+
+
+def test_block_states_are_the_states_at_block_ends():
+    """Each recorded block entry is the final state of the same sequence cut right after
+    that block's last token, and exactly the blocks closed by new tokens are recorded."""
+    bs = 4
+    x, dt, A, B, C, D, cu, h0 = _rand_case(31, 29, 2, 3, 1, 4, S=3, init=True)
+    nc = [0, 6, 9]
+    res = scan_prefill(x, dt, A, B, C, D, cu, 2, num_computed=nc, initial_states=h0,
+                       block_size=bs)
+    seen = set()
+    for r, col, h in res["block_states"]:
+        seen.add((r, col))
+        L_cut = (col + 1) * bs - nc[r]               # new tokens up to the block's end
+        t0 = cu[r]
+        assert 1 <= L_cut <= cu[r + 1] - t0
+        sl = slice(t0, t0 + L_cut)
+        ref = scan_prefill(x[sl], dt[sl], A, B[sl], C[sl], D, [0, L_cut], 1000,
+                           initial_states=[h0[r]])
+        np.testing.assert_array_equal(h, ref["final_states"][0])
+    expect = {(r, b) for r in range(3) for b in range(nc[r] // bs, 100)
+              if nc[r] < (b + 1) * bs <= nc[r] + cu[r + 1] - cu[r]}
+    assert seen == expect
+
+
+def test_prefix_cache_resume_from_a_block_entry():
+    """One-shot prefill vs a prefill resumed from a cached entry: resuming after a full
+    block (entry last_computed = that block) and after a partial block (entry written as the
+    final state of the first part, at last_scheduled) both reproduce the one-shot y and
+    final state."""
+    bs, T = 4, 15
+    x, dt, A, B, C, D, _, _ = _rand_case(32, T, 2, 3, 2, 4)
+    full = scan_prefill(x, dt, A, B, C, D, [0, T], 2, block_size=bs)
+    entries = {col: h for _, col, h in full["block_states"]}
+    for cut in (4, 8, 6, 9):
+        first = scan_prefill(x[:cut], dt[:cut], A, B[:cut], C[:cut], D, [0, cut], 2,
+                             block_size=bs)
+        _, _, last_sched = block_indices([0], [cut], bs)
+        cache = {col: h for _, col, h in first["block_states"]}
+        cache[int(last_sched[0])] = first["final_states"][0]
+        _, last_comp, _ = block_indices([cut], [T - cut], bs)
+        h_in = cache[int(last_comp[0])]
+        rest = scan_prefill(x[cut:], dt[cut:], A, B[cut:], C[cut:], D, [0, T - cut], 2,
+                            num_computed=[cut], initial_states=[h_in], block_size=bs)
+        np.testing.assert_allclose(rest["y"], full["y"][cut:], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(rest["final_states"], full["final_states"], rtol=1e-12,
+                                   atol=1e-12)
+        for _, col, h in rest["block_states"]:
+            np.testing.assert_allclose(h, entries[col], rtol=1e-12, atol=1e-12)
+
+
+def test_all_mode_decode_reads_last_computed_and_writes_last_scheduled():
+    pool, _, _, x, dt, A, Bm, Cm, D = _decode_case(33, B_pad=5, ntok=1)
+    rng = np.random.default_rng(34)
+    idx = rng.permutation(np.arange(1, 20))[:5 * 3].reshape(5, 3)
+    lc = np.array([0, 1, 2, 1, 0])
+    ls = np.array([1, 1, 2, 2, 0])
+    idx[4, 0] = 0                                   # padding row: its destination is null
+    y, writes = scan_decode(pool, idx, None, x, dt, A, Bm, Cm, D, null_block_id=0,
+                            block_idx_last_computed=lc, block_idx_last_scheduled=ls)
+    assert set(y) == {0, 1, 2, 3}
+    assert set(writes) == {int(idx[r, ls[r]]) for r in range(4)}
+    for r in range(4):
+        ref = scan_prefill(x[r], dt[r], A, Bm[r], Cm[r], D, [0, 1], 1,
+                           initial_states=[pool[idx[r, lc[r]]]])
+        np.testing.assert_allclose(y[r], ref["y"], rtol=1e-14, atol=1e-14)
+        np.testing.assert_allclose(writes[int(idx[r, ls[r]])], ref["final_states"][0],
+                                   rtol=1e-14, atol=1e-14)
 
 
 # ----------------------------------------------------------------------------------------
