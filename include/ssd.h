@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 2
+#define SSD_ABI_VERSION 3
 
 typedef enum ssd_status {
   SSD_OK = 0,
@@ -210,6 +210,34 @@ typedef struct ssd_prefill_args {
    * that dtype (round to nearest even) and carried in fp32 everywhere else; chunk_states_out
    * stays fp32. */
   int32_t state_dtype;
+
+  /* "all" cache mode: prefix caching with one state entry per cache block ("[vLLM] Mamba
+   * (SSM)": the MetadataBuilder init sizes the decode index tensor by the maximum number
+   * of blocks in this mode, and the metadata carries block_idx_first_scheduled_token,
+   * block_idx_last_computed_token and block_idx_last_scheduled_token).  block_size == 0
+   * keeps one slot per sequence as described above.  With block_size > 0 (a multiple of
+   * chunk_size; SSD_A_SCALAR only):
+   *   - state_indices is [S, idx_stride]: entry (r, b) is the pool slot of cache block b of
+   *     sequence r, the block of the sequence's tokens [b*block_size, (b+1)*block_size);
+   *   - the initial state (has_initial_state[r]) is read from entry
+   *     (r, block_idx_last_computed[r]);
+   *   - a chunk whose end lies at absolute position e of its sequence (num_computed[r]
+   *     plus the sequence's new tokens up to the chunk end) with e % block_size == 0 writes
+   *     its end state to entry (r, e / block_size - 1);
+   *   - with write_final_to_pool the final state goes to entry
+   *     (r, block_idx_last_scheduled[r]);
+   *   - block_idx_first_scheduled_token is not an input: it is num_computed / block_size,
+   *     the entry of the first block end above.
+   * A partial block's entry holds the state after its last processed token, so a sequence
+   * may resume from the entry it then overwrites.  Entries written by one sequence must not
+   * be read or written by another.  A column or slot out of range skips that read or write
+   * and raises SSD_DEVERR_SLOT_RANGE; a block end falling inside a chunk (num_computed not
+   * the value the chunk metadata was built with) raises SSD_DEVERR_CHUNK_RANGE. */
+  int32_t block_size;
+  int32_t idx_stride;                       /* row stride of state_indices, >= 1      */
+  const int32_t* num_computed;              /* [S] (device) tokens processed before    */
+  const int32_t* block_idx_last_computed;   /* [S] (device) entry of the initial state */
+  const int32_t* block_idx_last_scheduled;  /* [S] (device) entry of the final state   */
 } ssd_prefill_args;
 
 #define SSD_PREFILL_MAX_KERNELS 2
@@ -284,12 +312,26 @@ typedef struct ssd_decode_args {
                                          the update kernel (timing hook)              */
   int32_t state_dtype;                /* ssd_dtype of state_pool: SSD_F32 (0) or SSD_BF16;
                                          the state is carried in fp32 inside the step  */
+
+  /* "all" cache mode (one state entry per cache block, as for the prefill): idx_stride ==
+   * 0 keeps state_indices [B_pad, ntok] as described above.  With idx_stride > 0,
+   * state_indices is [B_pad, idx_stride], ntok must be 1 and num_accepted_tokens NULL; a
+   * row is padding when its destination entry state_indices[r, block_idx_last_scheduled[r]]
+   * is null_block_id; otherwise the state is read from entry
+   * (r, block_idx_last_computed[r]) and the state after the token is written to the
+   * destination entry.  A column out of range skips the row and raises
+   * SSD_DEVERR_SLOT_RANGE. */
+  int32_t idx_stride;
+  const int32_t* block_idx_last_computed;   /* [B_pad] (device) */
+  const int32_t* block_idx_last_scheduled;  /* [B_pad] (device) */
 } ssd_decode_args;
 
-/* Errors: SSD_ERR_NULL_POINTER, SSD_ERR_BAD_SHAPE (also an unknown a_kind, or SSD_A_DIAG
- * with P != 1 or G != 1), SSD_ERR_UNSUPPORTED (N, ntok or P*N outside the instantiated
- * range; state_pool not 16-byte aligned or slot_stride not a multiple of 4, or of 8 for a
- * bf16 pool with SSD_A_SCALAR), SSD_ERR_HIP.  B_pad == 0 is a no-op. */
+/* Errors: SSD_ERR_NULL_POINTER (also a NULL block index array in the all cache mode),
+ * SSD_ERR_BAD_SHAPE (also an unknown a_kind, SSD_A_DIAG with P != 1 or G != 1, or the all
+ * cache mode with ntok != 1 or num_accepted_tokens set), SSD_ERR_UNSUPPORTED (N, ntok or
+ * P*N outside the instantiated range; state_pool not 16-byte aligned or slot_stride not a
+ * multiple of 4, or of 8 for a bf16 pool with SSD_A_SCALAR), SSD_ERR_HIP.  B_pad == 0 is a
+ * no-op. */
 ssd_status ssd_state_update(const ssd_decode_args* args, ssd_stream_t stream);
 
 #ifdef __cplusplus

@@ -55,6 +55,8 @@ class PrefillArgs(ctypes.Structure):
         ("chunk_states_out", _vp), ("device_error_flag", _vp),
         ("dA_cumsum_out", _vp), ("cb_out", _vp), ("chunk_local_states_out", _vp),
         ("profile_events", _vp), ("state_dtype", _i32),
+        ("block_size", _i32), ("idx_stride", _i32), ("num_computed", _vp),
+        ("block_idx_last_computed", _vp), ("block_idx_last_scheduled", _vp),
     ]
 
 
@@ -72,6 +74,8 @@ class DecodeArgs(ctypes.Structure):
         ("state_indices", _vp), ("num_accepted_tokens", _vp),
         ("null_block_id", _i32), ("device_error_flag", _vp), ("profile_events", _vp),
         ("state_dtype", _i32),
+        ("idx_stride", _i32), ("block_idx_last_computed", _vp),
+        ("block_idx_last_scheduled", _vp),
     ]
 
 

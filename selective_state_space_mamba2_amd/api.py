@@ -93,8 +93,11 @@ def prefill_args(x, dt, A, B, C, chunk_size: int, cu_seqlens, cu_chunk_seqlens, 
                  dt_limit=(0.0, math.inf), state_pool=None, state_indices=None,
                  has_initial_state=None, write_final_to_pool: bool = False,
                  chunk_states_out=None, device_error_flag=None, dA_cumsum_out=None,
-                 cb_out=None, chunk_local_states_out=None) -> PrefillArgs:
-    """Fill an ssd_prefill_args from tensors (no device work)."""
+                 cb_out=None, chunk_local_states_out=None, block_size: int = 0,
+                 num_computed=None, block_idx_last_computed=None,
+                 block_idx_last_scheduled=None) -> PrefillArgs:
+    """Fill an ssd_prefill_args from tensors (no device work).  block_size > 0 selects the
+    all cache mode: state_indices is then [S, max_blocks] (row stride taken from it)."""
     T, H, P = x.shape
     G, N = B.shape[1], B.shape[2]
     for name, t, inner in (("x", x, (P, 1)), ("y", y, (P, 1)), ("B", B, (N, 1)),
@@ -132,6 +135,14 @@ def prefill_args(x, dt, A, B, C, chunk_size: int, cu_seqlens, cu_chunk_seqlens, 
     a.dA_cumsum_out = _dptr(dA_cumsum_out)
     a.cb_out = _dptr(cb_out)
     a.chunk_local_states_out = _dptr(chunk_local_states_out)
+    a.block_size = int(block_size)
+    if block_size and state_indices is not None:
+        if state_indices.dim() != 2 or state_indices.stride(1) != 1:
+            raise ValueError("state_indices must be [S, max_blocks] with contiguous rows")
+        a.idx_stride = state_indices.stride(0)
+    a.num_computed = _dptr(num_computed)
+    a.block_idx_last_computed = _dptr(block_idx_last_computed)
+    a.block_idx_last_scheduled = _dptr(block_idx_last_scheduled)
     return a
 
 
@@ -163,7 +174,10 @@ def ssd_prefill(x, dt, A, B, C, chunk_size: int, cu_seqlens, cu_chunk_seqlens, s
 
 def decode_args(x, dt, A, B, C, y, state_pool, state_indices, num_accepted_tokens=None,
                 null_block_id: int = 0, D=None, dt_bias=None, dt_softplus: bool = False,
-                dt_limit=(0.0, math.inf), device_error_flag=None) -> DecodeArgs:
+                dt_limit=(0.0, math.inf), device_error_flag=None,
+                block_idx_last_computed=None, block_idx_last_scheduled=None) -> DecodeArgs:
+    """Fill an ssd_decode_args.  Passing the two block index tensors selects the all cache
+    mode: state_indices is then [B_pad, max_blocks] and ntok must be 1."""
     B_pad, ntok, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
     for name, t in (("x", x), ("dt", dt), ("B", B), ("C", C), ("y", y),
@@ -186,6 +200,10 @@ def decode_args(x, dt, A, B, C, y, state_pool, state_indices, num_accepted_token
     a.num_accepted_tokens = _dptr(num_accepted_tokens)
     a.null_block_id = int(null_block_id)
     a.device_error_flag = _dptr(device_error_flag)
+    if block_idx_last_scheduled is not None:
+        a.idx_stride = state_indices.shape[1]
+        a.block_idx_last_computed = _dptr(block_idx_last_computed)
+        a.block_idx_last_scheduled = _dptr(block_idx_last_scheduled)
     return a
 
 

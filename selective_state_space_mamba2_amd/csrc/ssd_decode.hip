@@ -15,6 +15,62 @@
 
 namespace ssd {
 
+// The pool slots of decode row r: `src` is read before any write, dst(j) receives the
+// state after token j.  state_indices is [B_pad, ntok] (column j: token j's destination,
+// column num_accepted-1: the source), or in the all cache mode [B_pad, idx_stride] with one
+// token per row, source column block_idx_last_computed and destination column
+// block_idx_last_scheduled.
+struct DecodeRow {
+  const int* idx;   // the row of state_indices
+  int src;
+  int one;          // the all cache mode's destination slot, else -1
+  __device__ int dst(int j) const { return one >= 0 ? one : idx[j]; }
+};
+
+// 1: a live row; 0: a padding row (its first destination is null_block_id: nothing is read
+// or written); -1: an invalid row (a column, slot or num_accepted out of range), skipped
+// with the flag raised when `report`.
+__device__ __forceinline__ int decode_row(const DecodeParams& p, int r, bool report,
+                                          DecodeRow& row) {
+  int err = 0;
+  if (p.idx_stride > 0) {
+    row.idx = p.idx + int64_t(r) * p.idx_stride;
+    const int ls = p.blk_last_sched[r], lc = p.blk_last_comp[r];
+    if (ls < 0 || ls >= p.idx_stride) {
+      err = SSD_DEVERR_SLOT_RANGE;
+    } else {
+      row.one = row.idx[ls];
+      if (row.one == p.null_id) return 0;
+      if (lc < 0 || lc >= p.idx_stride) {
+        err = SSD_DEVERR_SLOT_RANGE;
+      } else {
+        row.src = row.idx[lc];
+        if (row.src < 0 || row.src >= p.num_slots || row.one < 0 || row.one >= p.num_slots)
+          err = SSD_DEVERR_SLOT_RANGE;
+      }
+    }
+  } else {
+    row.idx = p.idx + int64_t(r) * p.ntok;
+    row.one = -1;
+    if (row.idx[0] == p.null_id) return 0;
+    const int acc = p.num_acc ? p.num_acc[r] : 1;
+    if (acc < 1 || acc > p.ntok) {
+      err = SSD_DEVERR_ACCEPTED;
+    } else {
+      for (int j = 0; j < p.ntok; ++j) {
+        const int s = row.idx[j];
+        if (s < 0 || s >= p.num_slots) err = SSD_DEVERR_SLOT_RANGE;
+      }
+      row.src = row.idx[acc - 1];
+    }
+  }
+  if (err) {
+    if (report) raise_flag(p.flag, err);
+    return -1;
+  }
+  return 1;
+}
+
 // States per lane of the decode kernel: 16 bytes of the pool per lane, i.e. 4 fp32 or 8 bf16.
 template <typename S>
 constexpr int decode_vec() { return sizeof(S) == 2 ? 8 : 4; }
@@ -27,29 +83,14 @@ __global__ __launch_bounds__(256) void k_state_update(DecodeParams p) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   const int h = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
   const int ntok = p.ntok, P = p.P, H = p.H;
-  const int* idx_r = p.idx + int64_t(r) * ntok;
-  if (idx_r[0] == p.null_id) return;  // padding row: nothing read, nothing written
-
-  const int acc_tok = p.num_acc ? p.num_acc[r] : 1;
-  bool bad = acc_tok < 1 || acc_tok > ntok;
-  if (!bad) {
-    for (int j = 0; j < ntok; ++j) {
-      const int s = idx_r[j];
-      bad |= (s < 0 || s >= p.num_slots);
-    }
-  }
-  if (bad) {
-    if (tid == 0)
-      raise_flag(p.flag, (acc_tok < 1 || acc_tok > ntok) ? SSD_DEVERR_ACCEPTED
-                                                         : SSD_DEVERR_SLOT_RANGE);
-    return;
-  }
+  DecodeRow row;
+  if (decode_row(p, r, tid == 0, row) <= 0) return;   // padding or invalid: nothing touched
 
   // Gather the source state before any write; it is requested first so the state stream
   // is in flight while the small per-token inputs are staged.
   const int lane_q = tid % NQ, prow = tid / NQ;
   const int64_t head_off = int64_t(h) * P * N;
-  const int64_t src = int64_t(idx_r[acc_tok - 1]) * p.slot_stride + head_off;
+  const int64_t src = int64_t(row.src) * p.slot_stride + head_off;
   float st[ITERS][V];
 #pragma unroll
   for (int i = 0; i < ITERS; ++i) {
@@ -101,7 +142,7 @@ __global__ __launch_bounds__(256) void k_state_update(DecodeParams p) {
       bv[v4] = b4.x; bv[v4 + 1] = b4.y; bv[v4 + 2] = b4.z; bv[v4 + 3] = b4.w;
       cv[v4] = c4.x; cv[v4 + 1] = c4.y; cv[v4 + 2] = c4.z; cv[v4 + 3] = c4.w;
     }
-    const int64_t dst = int64_t(idx_r[j]) * p.slot_stride + head_off;
+    const int64_t dst = int64_t(row.dst(j)) * p.slot_stride + head_off;
 #pragma unroll
     for (int i = 0; i < ITERS; ++i) {
       const int pr = i * RP + prow;
@@ -163,27 +204,12 @@ __global__ __launch_bounds__(256) void k_state_update_diag(DecodeParams p) {
   const int r = blockIdx.y, tid = threadIdx.x;
   const int c = blockIdx.x * kDiagDecodeChannels + tid / SPL, q = tid % SPL;
   const int ntok = p.ntok, H = p.H;
-  const int* idx_r = p.idx + int64_t(r) * ntok;
-  if (idx_r[0] == p.null_id) return;  // padding row: nothing read, nothing written
-
-  const int acc_tok = p.num_acc ? p.num_acc[r] : 1;
-  bool bad = acc_tok < 1 || acc_tok > ntok;
-  if (!bad) {
-    for (int j = 0; j < ntok; ++j) {
-      const int s = idx_r[j];
-      bad |= (s < 0 || s >= p.num_slots);
-    }
-  }
-  if (bad) {
-    if (tid == 0 && blockIdx.x == 0)
-      raise_flag(p.flag, (acc_tok < 1 || acc_tok > ntok) ? SSD_DEVERR_ACCEPTED
-                                                         : SSD_DEVERR_SLOT_RANGE);
-    return;
-  }
+  DecodeRow row;
+  if (decode_row(p, r, tid == 0 && blockIdx.x == 0, row) <= 0) return;   // padding or invalid
   // the source state first (read before any write), then the row's B and C
   const bool live = c < H;
   const int cc = live ? c : H - 1;
-  float4_v h = PoolIO<S>::ld4(p.pool, int64_t(idx_r[acc_tok - 1]) * p.slot_stride + int64_t(cc) * N + SPL * q);
+  float4_v h = PoolIO<S>::ld4(p.pool, int64_t(row.src) * p.slot_stride + int64_t(cc) * N + SPL * q);
   const float4_v a = *reinterpret_cast<const float4_v*>(p.A + int64_t(cc) * N + SPL * q);
   const float A2[SPL] = {a.x * kLog2e, a.y * kLog2e, a.z * kLog2e, a.w * kLog2e};
   const T* bg = static_cast<const T*>(p.B);
@@ -214,7 +240,7 @@ __global__ __launch_bounds__(256) void k_state_update_diag(DecodeParams p) {
     acc += __shfl_xor(acc, 1, 64);
     acc += __shfl_xor(acc, 2, 64);
     if (q == 0) Elem<T>::store(yg + tj, acc + Dc * xv);
-    PoolIO<S>::st4_nt(p.pool, int64_t(idx_r[j]) * p.slot_stride + int64_t(c) * N + SPL * q, h);
+    PoolIO<S>::st4_nt(p.pool, int64_t(row.dst(j)) * p.slot_stride + int64_t(c) * N + SPL * q, h);
   }
 }
 

@@ -69,6 +69,9 @@ ssd_status ssd_prefill(const ssd_prefill_args* a, void* workspace, size_t worksp
   p.pool_bf16 = a->state_dtype == SSD_BF16 ? 1 : 0;
   p.state_idx = a->state_indices; p.has_init = a->has_initial_state;
   p.write_final = (a->write_final_to_pool && a->state_pool) ? 1 : 0;
+  p.block_size = a->block_size; p.idx_stride = a->block_size > 0 ? a->idx_stride : 1;
+  p.num_computed = a->num_computed;
+  p.blk_last_comp = a->block_idx_last_computed; p.blk_last_sched = a->block_idx_last_scheduled;
   p.flag = a->device_error_flag;
   p.dA_cumsum_out = a->dA_cumsum_out;
   p.cb_out = a->cb_out;
@@ -81,6 +84,7 @@ ssd_status ssd_prefill(const ssd_prefill_args* a, void* workspace, size_t worksp
     p.dcw = plan.chain ? nullptr : reinterpret_cast<float*>(ws + plan.off_dc);
     p.cfw = ws + plan.off_cf;
     p.seq_ord = reinterpret_cast<int*>(ws + plan.off_ord);
+    p.blk_slot = a->block_size > 0 ? reinterpret_cast<int*>(ws + plan.off_blk) : nullptr;
     if (plan.chain) {
       p.chain_flag = reinterpret_cast<int*>(ws + plan.off_flag);
       p.chunk_ord = reinterpret_cast<int*>(ws + plan.off_cord);
@@ -133,6 +137,8 @@ ssd_status ssd_state_update(const ssd_decode_args* a, ssd_stream_t stream) {
   p.pool_bf16 = a->state_dtype == SSD_BF16 ? 1 : 0;
   p.idx = a->state_indices; p.num_acc = a->num_accepted_tokens;
   p.null_id = a->null_block_id; p.flag = a->device_error_flag;
+  p.idx_stride = a->idx_stride;
+  p.blk_last_comp = a->block_idx_last_computed; p.blk_last_sched = a->block_idx_last_scheduled;
   const hipError_t e = ssd::launch_state_update(a->in_dtype, p, static_cast<hipStream_t>(stream),
                                                 a->profile_events);
   return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;

@@ -58,6 +58,15 @@ ssd_status plan_prefill(const ssd_prefill_args* a, PrefillPlan* plan) {
   if (std::isnan(a->dt_min) || std::isnan(a->dt_max) || a->dt_min > a->dt_max)
     return SSD_ERR_BAD_SHAPE;
   if (!valid_dtype(a->state_dtype)) return SSD_ERR_BAD_SHAPE;
+  // the all cache mode: one pool entry per cache block of block_size tokens
+  if (a->block_size < 0) return SSD_ERR_BAD_SHAPE;
+  if (a->block_size > 0) {
+    if (a->a_kind != SSD_A_SCALAR) return SSD_ERR_UNSUPPORTED;
+    if (a->block_size % a->chunk_size != 0 || a->idx_stride < 1) return SSD_ERR_BAD_SHAPE;
+    if (!a->state_pool || !a->state_indices || !a->num_computed) return SSD_ERR_NULL_POINTER;
+    if (a->has_initial_state && !a->block_idx_last_computed) return SSD_ERR_NULL_POINTER;
+    if (a->write_final_to_pool && !a->block_idx_last_scheduled) return SSD_ERR_NULL_POINTER;
+  }
 
   const int64_t C = a->num_chunks;
   if (a->a_kind == SSD_A_DIAG) {
@@ -107,6 +116,8 @@ ssd_status plan_prefill(const ssd_prefill_args* a, PrefillPlan* plan) {
     if (!a->chunk_states_out)
       off = align_up(off + size_t(a->num_seqs) * a->H * 2 * size_t(state / a->H) * sizeof(float), 256);
   }
+  plan->off_blk = off;
+  if (a->block_size > 0) off = align_up(off + size_t(C) * sizeof(int32_t), 256);
   plan->ws_bytes = off;
   return SSD_OK;
 }
@@ -129,9 +140,14 @@ ssd_status check_decode(const ssd_decode_args* a) {
   }
   if (std::isnan(a->dt_min) || std::isnan(a->dt_max) || a->dt_min > a->dt_max)
     return SSD_ERR_BAD_SHAPE;
+  // the all cache mode: one token per row, no speculative restore
+  if (a->idx_stride < 0) return SSD_ERR_BAD_SHAPE;
+  if (a->idx_stride > 0 && (a->ntok != 1 || a->num_accepted_tokens)) return SSD_ERR_BAD_SHAPE;
   if (a->B_pad == 0) return SSD_OK;
   if (!a->x || !a->dt || !a->B || !a->C || !a->y || !a->A || !a->state_pool ||
       !a->state_indices)
+    return SSD_ERR_NULL_POINTER;
+  if (a->idx_stride > 0 && (!a->block_idx_last_computed || !a->block_idx_last_scheduled))
     return SSD_ERR_NULL_POINTER;
   if (a->num_slots < 1 || a->slot_stride < int64_t(a->H) * a->P * a->N)
     return SSD_ERR_BAD_SHAPE;

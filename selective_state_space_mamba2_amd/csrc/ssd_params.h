@@ -30,6 +30,11 @@ struct PrefillParams {
   const int* state_idx;
   const int* has_init;
   int write_final;
+  int block_size;      // > 0: the all cache mode (state_idx is [S, idx_stride])
+  int idx_stride;
+  const int* num_computed;
+  const int* blk_last_comp;
+  const int* blk_last_sched;
   float* states;       // [C, H, P, N] chunk_states_out (NULL: not written)
   void* cbw;           // workspace, input dtype: C.B^T fragments per chunk and group
   void* btw;           // workspace, input dtype: B^T fragments per chunk and group
@@ -39,6 +44,8 @@ struct PrefillParams {
   int* chain_flag;     // workspace [C, H, kChainWaves]: chain publication flags (NULL: march)
   int* chunk_ord;      // workspace [C]: chunks in chain dispatch order
   float* hring;        // workspace [S, H, 2, P, N] when states is NULL: published states
+  int* blk_slot;       // workspace [C], all cache mode: pool slot of each chunk's end state
+                       // (-1: none), set by k_chunk_prep; NULL when the mode is off
   int* flag;
   float* dA_cumsum_out;
   float* cb_out;
@@ -62,6 +69,9 @@ struct DecodeParams {
   const int* num_acc;
   int null_id;
   int* flag;
+  int idx_stride;      // > 0: the all cache mode (idx is [B_pad, idx_stride], ntok == 1)
+  const int* blk_last_comp;
+  const int* blk_last_sched;
 };
 
 // `events` (may be NULL): hipEvent_t handles recorded before each launch and after the

@@ -29,6 +29,8 @@ struct PrefillPlan {
   size_t off_cord = 0;       // int32 [C]: chain dispatch order of the chunks
   size_t off_ring = 0;       // fp32 [S, H, 2, P, N]: published states when no chunk-state
                              // output is given (0 bytes otherwise)
+  size_t off_blk = 0;        // int32 [C]: the all cache mode's pool slot for every chunk's
+                             // end state, -1 for none (0 bytes when the mode is off)
 };
 
 // Shapes that run the chunk-chain kernel (bf16, head dim 64, dstate and chunk size

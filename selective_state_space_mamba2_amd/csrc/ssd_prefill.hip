@@ -216,6 +216,60 @@ __device__ __forceinline__ void wave_lds_sync() {
 __device__ __forceinline__ int xsw(int p, int s) { return s ^ (((p >> 3) & 3) << 4); }
 
 // ---------------------------------------------------------------------------------------
+// Pool entries of a sequence.  state_idx is [S, idx_stride]: one slot per sequence
+// (idx_stride 1, column 0), or in the all cache mode one entry per cache block of
+// block_size tokens (block b: tokens [b*block_size, (b+1)*block_size) of the sequence).
+// ---------------------------------------------------------------------------------------
+
+// Slot of entry `col` of sequence r, or -1 (SSD_DEVERR_SLOT_RANGE raised if `report`)
+// when the column or the slot is out of range.
+__device__ __forceinline__ int pool_slot(const PrefillParams& p, int r, int col, bool report) {
+  int slot = -1;
+  if (col >= 0 && col < p.idx_stride) slot = p.state_idx[int64_t(r) * p.idx_stride + col];
+  if (slot < 0 || slot >= p.num_slots) {
+    if (report) raise_flag(p.flag, SSD_DEVERR_SLOT_RANGE);
+    return -1;
+  }
+  return slot;
+}
+
+// The all cache mode's entry for the state at the end of chunk [cs0, cs1) of sequence r
+// (first token t0): column e / block_size - 1 when the chunk ends at an absolute position
+// e that closes a block, else -1.  A block end strictly inside the chunk means the chunk
+// metadata was built for another num_computed: SSD_DEVERR_CHUNK_RANGE if `report`.
+__device__ __forceinline__ int block_end_col(const PrefillParams& p, int r, int t0, int cs0,
+                                             int cs1, bool report) {
+  if (p.block_size <= 0) return -1;
+  // absolute positions fit in int32 (the chunk-metadata builder rejects larger ones)
+  const int64_t a0 = int64_t(p.num_computed[r]) + (cs0 - t0), a1 = a0 + (cs1 - cs0);
+  const uint32_t bs = uint32_t(p.block_size), u0 = uint32_t(a0), u1 = uint32_t(a1);
+  if (a0 < 0 || a1 > INT32_MAX || (u1 - 1) / bs != u0 / bs) {
+    if (report) raise_flag(p.flag, SSD_DEVERR_CHUNK_RANGE);
+    return -1;
+  }
+  return u1 % bs == 0 ? int(u1 / bs) - 1 : -1;
+}
+
+// Source and final pool slots of sequence r (-1: none): the sequence's slot, or in the all
+// cache mode the entries block_idx_last_computed (read only with an initial state) and
+// block_idx_last_scheduled (written only with write_final).
+struct SeqSlots { int src, fin; };
+__device__ __forceinline__ SeqSlots seq_slots(const PrefillParams& p, int r, bool need_src,
+                                              bool need_fin, bool report) {
+  SeqSlots s{-1, -1};
+  if (!p.pool || !p.state_idx || !(need_src || need_fin)) return s;
+  if (p.block_size <= 0) {
+    const int slot = pool_slot(p, r, 0, report);
+    s.src = need_src ? slot : -1;
+    s.fin = need_fin ? slot : -1;
+    return s;
+  }
+  if (need_src && p.has_init && p.has_init[r]) s.src = pool_slot(p, r, p.blk_last_comp[r], report);
+  if (need_fin && p.write_final) s.fin = pool_slot(p, r, p.blk_last_sched[r], report);
+  return s;
+}
+
+// ---------------------------------------------------------------------------------------
 // Chunk-local cumsum (dA cumsum) and the march's sequence order, both produced inside
 // k_chunk_prep.
 // ---------------------------------------------------------------------------------------
@@ -369,7 +423,19 @@ __global__ __launch_bounds__(256) void k_chunk_prep(PrefillParams p) {
       p.chain_flag[(int64_t(k) * p.H + g * (p.H / p.G)) * kChainWaves + i] = 0;
   }
   int cs0, L, r;
-  if (!chunk_bounds(p, k, CS, cs0, L, r)) {
+  const bool bounds_ok = chunk_bounds(p, k, CS, cs0, L, r);
+  // the all cache mode: the pool slot that receives this chunk's end state when the chunk
+  // closes a cache block (-1: none; at a sequence's last chunk the final write takes its
+  // place when there is one)
+  if (p.blk_slot && g == 0 && z == 0 && tid == 0) {
+    int slot = -1;
+    if (bounds_ok) {
+      const int col = block_end_col(p, r, p.cu_seqlens[r], cs0, cs0 + L, true);
+      if (col >= 0 && !(k == p.last_chunk[r] && p.write_final)) slot = pool_slot(p, r, col, true);
+    }
+    p.blk_slot[k] = slot;
+  }
+  if (!bounds_ok) {
     if (tid == 0 && g == 0 && z == 0) raise_flag(p.flag, SSD_DEVERR_CHUNK_RANGE);
     return;
   }
@@ -535,6 +601,36 @@ struct ChunkLoc {
   int cs0, L;
 };
 
+// The march kernel's state slice (hreg: wave w holds n-tiles [w*TNW, (w+1)*TNW) of the
+// slice's PW rows) to the pool slot whose slice starts at element e.
+template <int PW, int N>
+__device__ __forceinline__ void march_pool_store(const PrefillParams& p, int64_t e,
+                                                 const f32x4_v (&hreg)[(N / 16 + 3) / 4][PW / 16],
+                                                 int wave, int li, int kg) {
+  constexpr int TN = N / 16, TNW = (TN + 3) / 4, TPW = PW / 16;
+  // buffer stores: the slot in a descriptor, one lane offset, the tile offset in soffset
+  const int esz = p.pool_bf16 ? 2 : 4;
+  const BufRes b(static_cast<char*>(p.pool) + e * esz);
+  const uint32_t lane_e = uint32_t(li * N + 4 * kg);
+#pragma unroll
+  for (int q = 0; q < TNW; ++q) {
+    const int nt = wave * TNW + q;
+    if (nt >= TN) continue;
+#pragma unroll
+    for (int pt = 0; pt < TPW; ++pt) {
+      const f32x4_v v = hreg[q][pt];
+      const uint32_t tile_e = uint32_t(pt * 16 * N + nt * 16);
+      if (p.pool_bf16)
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2_v{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])},
+                                              b.r, lane_e * 2, tile_e * 2, 0);
+      else
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4_v{__float_as_uint(v[0]), __float_as_uint(v[1]),
+                                                       __float_as_uint(v[2]), __float_as_uint(v[3])},
+                                               b.r, lane_e * 4, tile_e * 4, 0);
+    }
+  }
+}
+
 // Work item `it`: columns 8*g8 .. 8*g8+7 of the slice, tokens 4*sg .. 4*sg+3.
 template <typename T, int P, int PW, int N, int CS>
 __device__ __forceinline__ void march_load_stage(StageIn<T, MarchCfg<T, P, PW, N, CS>::NI>& st,
@@ -636,21 +732,15 @@ void k_chunk_march(PrefillParams p) {
     if (tid == 0) raise_flag(p.flag, SSD_DEVERR_CHUNK_RANGE);
     return;
   }
-  int slot = -1;
-  if (p.pool && p.state_idx) {
-    slot = p.state_idx[r];
-    if (slot < 0 || slot >= p.num_slots) {
-      if (tid == 0) raise_flag(p.flag, SSD_DEVERR_SLOT_RANGE);
-      slot = -1;
-    }
-  }
-  // element offset of this workgroup's state slice in the pool (-1: no pool slot)
-  const int64_t pool_e = slot >= 0 ? int64_t(slot) * p.slot_stride + (int64_t(h) * P + p0) * N : -1;
+  // element offset of this workgroup's state slice in a pool slot (-1: none)
+  const int64_t slice_e = (int64_t(h) * P + p0) * N;
+  auto slot_e = [&](int slot) { return slot >= 0 ? int64_t(slot) * p.slot_stride + slice_e : int64_t(-1); };
+  const int64_t src_e = slot_e(seq_slots(p, r, true, true, tid == 0).src);
 
   // the state slice, held transposed (the MFMA result layout of B^T X~): lane holds
   // H[p0 + pt*16 + li][nt*16 + 4*kg + rr], nt = wave*TNW + q, i.e. 4 consecutive n of one row
   f32x4_v hreg[TNW][TPW];
-  const bool init = pool_e >= 0 && p.has_init && p.has_init[r];
+  const bool init = src_e >= 0 && p.has_init && p.has_init[r];
 #pragma unroll
   for (int q = 0; q < TNW; ++q)
 #pragma unroll
@@ -658,7 +748,7 @@ void k_chunk_march(PrefillParams p) {
       const int nt = wave * TNW + q;
       hreg[q][pt] = f32x4_v{0.f, 0.f, 0.f, 0.f};
       if (init && nt < TN) {
-        const float4_v v = pool_ld4(p.pool, p.pool_bf16, pool_e + (pt * 16 + li) * N + nt * 16 + 4 * kg);
+        const float4_v v = pool_ld4(p.pool, p.pool_bf16, src_e + (pt * 16 + li) * N + nt * 16 + 4 * kg);
         hreg[q][pt] = f32x4_v{v.x, v.y, v.z, v.w};
       }
     }
@@ -800,6 +890,10 @@ void k_chunk_march(PrefillParams p) {
 #pragma unroll
       for (int pt = 0; pt < TPW; ++pt) hreg[q][pt] = dec * hreg[q][pt] + sacc[q][pt];
     const int64_t sbase = (int64_t(k) * p.H + h) * (int64_t(P) * N) + int64_t(p0) * N;
+    if (p.blk_slot) {   // the all cache mode: a chunk that closes a cache block
+      const int slot = ld_meta(p.blk_slot, k);
+      if (slot >= 0 && slot < p.num_slots) march_pool_store<PW, N>(p, slot_e(slot), hreg, wave, li, kg);
+    }
     if (p.states) {
 #pragma unroll
       for (int q = 0; q < TNW; ++q) {
@@ -932,17 +1026,10 @@ void k_chunk_march(PrefillParams p) {
     cur = nxt;
   }
 
-  // final state back to the pool slot (read at the start by this same workgroup)
-  if (pool_e >= 0 && p.write_final) {
-#pragma unroll
-    for (int q = 0; q < TNW; ++q) {
-      const int nt = wave * TNW + q;
-      if (nt >= TN) continue;
-#pragma unroll
-      for (int pt = 0; pt < TPW; ++pt)
-        pool_st4(p.pool, p.pool_bf16, pool_e + (pt * 16 + li) * N + nt * 16 + 4 * kg, as_float4(hreg[q][pt]));
-    }
-  }
+  // final state back to the pool (a slot read at the start by this same workgroup, or a
+  // later entry of the sequence)
+  const int64_t fin_e = slot_e(seq_slots(p, r, false, true, false).fin);
+  if (fin_e >= 0) march_pool_store<PW, N>(p, fin_e, hreg, wave, li, kg);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1134,16 +1221,16 @@ void k_chunk_chain(PrefillParams p) {
     return;
   }
   const bool first = k == k0, last = k == k1;
-  int slot = -1;
-  if (p.pool && p.state_idx && (first || last)) {
-    slot = p.state_idx[r];
-    if (slot < 0 || slot >= p.num_slots) {
-      if (tid == 0 && first) raise_flag(p.flag, SSD_DEVERR_SLOT_RANGE);
-      slot = -1;
-    }
-  }
-  // element offset of this head's state in the pool slot (-1: no pool slot)
-  const int64_t pool_e = slot >= 0 ? int64_t(slot) * p.slot_stride + int64_t(h) * P * N : -1;
+  // pool slots: the initial state (first chunk), the final state (last chunk) and, in the
+  // all cache mode, the entry of a cache block this chunk closes (-1: none)
+  const SeqSlots ss = seq_slots(p, r, first, last, tid == 0 && (first || p.block_size > 0));
+  int blk = p.blk_slot ? ld_meta(p.blk_slot, k) : -1;
+  if (blk >= p.num_slots) blk = -1;
+  // element offsets of this head's state in those slots (-1: none)
+  auto slot_e = [&](int slot) {
+    return slot >= 0 ? int64_t(slot) * p.slot_stride + int64_t(h) * P * N : int64_t(-1);
+  };
+  const int64_t src_e = slot_e(ss.src), fin_e = slot_e(ss.fin), blk_e = slot_e(blk);
   const int g = h / (p.H / p.G);
   const float Dh = p.D ? p.D[h] : 0.f;
 
@@ -1249,7 +1336,7 @@ void k_chunk_chain(PrefillParams p) {
   const int my_xcd = xcd_id();
   const float* hin = nullptr;
   bool via_l2 = false;
-  const bool from_pool = first && pool_e >= 0 && p.has_init && p.has_init[r];
+  const bool from_pool = src_e >= 0 && p.has_init && p.has_init[r];
   if (!first) {
     int fv = 0;
     if (lane == 0) {
@@ -1280,7 +1367,7 @@ void k_chunk_chain(PrefillParams p) {
 #pragma unroll
       for (int pt = 0; pt < TP; ++pt) {
         const float4_v v = pool_ld4(p.pool, p.pool_bf16,
-                                    pool_e + (pt * 16 + li) * N + (wave * TNW + q) * 16 + 4 * kg);
+                                    src_e + (pt * 16 + li) * N + (wave * TNW + q) * 16 + 4 * kg);
         hreg[q][pt] = f32x4_v{v.x, v.y, v.z, v.w};
       }
   } else if (hin) {
@@ -1327,7 +1414,7 @@ void k_chunk_chain(PrefillParams p) {
   {
     const float dec = fast_exp(s_c[CS - 1]);
     const BufRes hb(chain_state(p, k, h, r, k - k0));
-    const bool to_pool = last && pool_e >= 0 && p.write_final;
+
     // kept in this XCD's L2 when the successor maps here too (the last chunk has none)
     const bool keep_l2 = !last && my_xcd == int(blockIdx.x % kXcds);
     f32x4_v hn[TNW][TP];
@@ -1355,13 +1442,15 @@ void k_chunk_chain(PrefillParams p) {
         for (int pt = 0; pt < TP; ++pt)
           __builtin_amdgcn_raw_buffer_store_b128(hbits(hn[q][pt]), hb.r, hoff(q, pt), 0, kCohDev);
     }
-    if (to_pool) {
+    auto to_pool = [&](int64_t e) {
 #pragma unroll
       for (int q = 0; q < TNW; ++q)
 #pragma unroll
         for (int pt = 0; pt < TP; ++pt)
-          pool_st4(p.pool, p.pool_bf16, pool_e + hoff(q, pt) / 4, as_float4(hn[q][pt]));
-    }
+          pool_st4(p.pool, p.pool_bf16, e + hoff(q, pt) / 4, as_float4(hn[q][pt]));
+    };
+    if (fin_e >= 0) to_pool(fin_e);
+    if (blk_e >= 0) to_pool(blk_e);
     if (!last) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       if (lane == 0)

@@ -34,7 +34,7 @@ def test_every_declared_function_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert lib().ssd_abi_version() == 2
+    assert lib().ssd_abi_version() == 3
     for s in range(8):
         assert lib().ssd_status_string(s)
     assert lib().ssd_status_string(99) == b"unknown status"
@@ -126,6 +126,35 @@ def test_workspace_size_layout():
     st, n = _ws(_good_prefill(a_kind=_abi.SSD_A_DIAG, H=64, P=1, G=1, N=16, x_stride_t=64,
                               y_stride_t=64, dt_stride_t=64, bc_stride_t=16))
     assert st == 0 and n == 0
+    # the all cache mode adds one int32 per chunk: the pool slot of its end state
+    st, n = _ws(_good_prefill(chunk_states_out=FAKE, **_ALL_MODE))
+    assert st == 0 and n == prep + chain + _al(C * 4)
+
+
+_ALL_MODE = dict(block_size=512, idx_stride=6, num_computed=FAKE, state_pool=FAKE,
+                 state_indices=FAKE, num_slots=16, slot_stride=8 * 64 * 128)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(), _abi.SSD_OK),
+    (dict(block_size=-1), _abi.SSD_ERR_BAD_SHAPE),
+    (dict(block_size=384), _abi.SSD_ERR_BAD_SHAPE),            # not a multiple of chunk_size
+    (dict(idx_stride=0), _abi.SSD_ERR_BAD_SHAPE),
+    (dict(num_computed=None), _abi.SSD_ERR_NULL_POINTER),
+    (dict(state_indices=None), _abi.SSD_ERR_NULL_POINTER),
+    (dict(has_initial_state=FAKE), _abi.SSD_ERR_NULL_POINTER),  # needs block_idx_last_computed
+    (dict(has_initial_state=FAKE, block_idx_last_computed=FAKE), _abi.SSD_OK),
+    (dict(write_final_to_pool=1), _abi.SSD_ERR_NULL_POINTER),   # needs block_idx_last_scheduled
+    (dict(write_final_to_pool=1, block_idx_last_scheduled=FAKE), _abi.SSD_OK),
+])
+def test_prefill_all_cache_mode_host_checks(over, status):
+    assert _ws(_good_prefill(**{**_ALL_MODE, **over}))[0] == status
+
+
+def test_prefill_all_cache_mode_is_scalar_a_only():
+    diag = dict(a_kind=_abi.SSD_A_DIAG, H=64, P=1, G=1, N=16, x_stride_t=64, y_stride_t=64,
+                dt_stride_t=64, bc_stride_t=16, chunk_size=256, slot_stride=64 * 16)
+    assert _ws(_good_prefill(**{**_ALL_MODE, **diag}))[0] == _abi.SSD_ERR_UNSUPPORTED
 
 
 def test_kernel_count():
@@ -241,6 +270,11 @@ def _good_decode(**over):
     (dict(dt_min=2.0, dt_max=1.0), _abi.SSD_ERR_BAD_SHAPE),
     (dict(state_pool=FAKE + 4), _abi.SSD_ERR_UNSUPPORTED),
     (dict(state_dtype=_abi.SSD_BF16, slot_stride=48 * 64 * 128 + 4), _abi.SSD_ERR_UNSUPPORTED),
+    (dict(idx_stride=-1), _abi.SSD_ERR_BAD_SHAPE),
+    (dict(idx_stride=5), _abi.SSD_ERR_BAD_SHAPE),                # all cache mode needs ntok 1
+    (dict(idx_stride=5, ntok=1, num_accepted_tokens=FAKE), _abi.SSD_ERR_BAD_SHAPE),
+    (dict(idx_stride=5, ntok=1), _abi.SSD_ERR_NULL_POINTER),     # block index arrays missing
+    (dict(idx_stride=5, ntok=1, block_idx_last_computed=FAKE), _abi.SSD_ERR_NULL_POINTER),
 ])
 def test_decode_host_checks(over, status):
     a = _good_decode(**over)
