@@ -47,20 +47,24 @@ def _log(msg):
 # ----------------------------------------------------------------------------------------
 # algorithmic work (bytes and flops a kernel must move / do; redundant work not counted)
 # ----------------------------------------------------------------------------------------
-def prefill_work(inp, cuc, sidx):
+def prefill_work(inp, cuc, sidx, state_writes=None):
+    """Algorithmic bytes and flops per kernel.  ``state_writes``: fp32 states written per
+    call (default: one per chunk plus the final states; the all cache mode passes its
+    block-end entries plus the final states)."""
     b = 2 if inp.in_dtype == "bf16" else 4
     T, H, P, G, N = inp.T, inp.H, inp.P, inp.G, inp.N
     S, C = inp.num_seqs, len(sidx)
     st = H * P * N * 4
     n_init = 0 if inp.has_initial_state is None else int(inp.has_initial_state.sum())
     n_final = 0 if inp.pool is None else S
+    n_states = n_init + (C + n_final if state_writes is None else state_writes)
     lens = [int(cuc[k + 1] - cuc[k]) for k in range(C)]
     cs = inp.chunk_size
     nfrag = sum(i // 2 + 1 for i in range(cs // 16))
     frags = C * G * (nfrag * 512 + 2 * N * cs) * b
     flops_y = sum(H * (4 * l * P * N + P * l * (l + 1)) for l in lens)
     flops_cb = sum(G * N * l * (l + 1) for l in lens)
-    io = T * 2 * H * P * b + (n_init + C + n_final) * st    # x in, y out, states
+    io = T * 2 * H * P * b + n_states * st                   # x in, y out, states
     dc = C * H * 2 * cs * 4                                   # cumsum + delta (fp32)
     # march path: the prep kernel reads dt, B and C and writes the cumsum, delta and the
     # C.B^T / B^T / C fragments; the march kernel reads x, C, the cumsum and the initial
@@ -72,7 +76,7 @@ def prefill_work(inp, cuc, sidx):
     # counted, it is not algorithmic)
     k_prep_chain = dict(bytes=2 * T * G * N * b + frags, flops=flops_cb)
     k_chain = dict(bytes=io + T * G * N * b + T * H * b, flops=flops_y)
-    path = dict(bytes=T * (2 * H * P * b + H * b + 2 * G * N * b) + (n_init + C + n_final) * st,
+    path = dict(bytes=T * (2 * H * P * b + H * b + 2 * G * N * b) + n_states * st,
                 flops=flops_y + flops_cb)
     return {"k_chunk_prep": k_prep, "k_chunk_march": k_march, "k_chunk_chain": k_chain,
             "k_chunk_prep/chain": k_prep_chain, "path": path}
@@ -182,7 +186,34 @@ def _roofline(bound, achieved, peak, unit, traffic=None, kernel=None):
 # ----------------------------------------------------------------------------------------
 # prefill (scalar A)
 # ----------------------------------------------------------------------------------------
-def bench_prefill(torch, name, steps, warmup, sets=4):
+def all_mode_blocks(inp, cuc, sidx, last, block_size, seed=77):
+    """The all cache mode's block table for a workload: distinct pool slots per (sequence,
+    block), the last-computed / last-scheduled columns, and the number of block-end entries
+    a call writes besides the final states."""
+    import numpy as np
+    S = inp.num_seqs
+    nc = np.asarray(inp.num_computed, dtype=np.int64)
+    L = np.diff(np.asarray(inp.cu_seqlens, dtype=np.int64))
+    lc = np.where(nc > 0, (nc - 1) // block_size, -1).astype(np.int32)
+    ls = ((nc + L - 1) // block_size).astype(np.int32)
+    mb = int(ls.max()) + 1
+    slots = inp.pool.shape[0]
+    if S * mb >= slots:
+        raise ValueError("pool too small for the block table")
+    rng = np.random.default_rng(seed)
+    table = (rng.permutation(slots - 1)[:S * mb] + 1).reshape(S, mb).astype(np.int32)
+    n_blk = 0
+    for k in range(len(sidx)):
+        r = int(sidx[k])
+        end = nc[r] + (int(cuc[k + 1]) - int(inp.cu_seqlens[r]))
+        if end % block_size == 0 and k != int(last[r]):
+            n_blk += 1
+    return table, lc, ls, n_blk
+
+
+def bench_prefill(torch, name, steps, warmup, sets=4, block_size=0):
+    """Time the prefill on a named workload.  block_size > 0 runs the all cache mode: one
+    pool entry per cache block, no chunk-state output."""
     import numpy as np
     from selective_state_space_mamba2_amd import api
     from selective_state_space_mamba2_amd._abi import SSD_PREFILL_MAX_KERNELS, check, lib
@@ -202,11 +233,20 @@ def bench_prefill(torch, name, steps, warmup, sets=4):
     hinit_d = (None if inp.has_initial_state is None
                else torch.from_numpy(inp.has_initial_state).cuda())
     base = {n: _dev_token(torch, inp, n) for n in ("x", "dt", "B", "C")}
+    extra, state_writes = {}, None
+    if block_size:
+        table, lc, ls, n_blk = all_mode_blocks(inp, cuc, sidx, last, block_size)
+        extra = dict(block_size=block_size, num_computed=torch.from_numpy(nc_np).cuda(),
+                     block_idx_last_computed=torch.from_numpy(lc).cuda(),
+                     block_idx_last_scheduled=torch.from_numpy(ls).cuda())
+        sidx_d = torch.from_numpy(table).cuda()
+        state_writes = n_blk + S
     bufs = []
     for i in range(sets):
         d = {n: (t if i == 0 else t.clone()) for n, t in base.items()}
         d["y"] = torch.empty_like(d["x"])
-        d["states"] = torch.empty(C, inp.H, inp.P, inp.N, dtype=torch.float32, device="cuda")
+        d["states"] = (None if block_size else
+                       torch.empty(C, inp.H, inp.P, inp.N, dtype=torch.float32, device="cuda"))
         # the four metadata arrays packed in one device buffer, filled by one copy per step
         d["meta"] = torch.empty(S + 1 + C + 1 + C + S, dtype=torch.int32, device="cuda")
         d["cu_seq"] = d["meta"][:S + 1]
@@ -219,7 +259,8 @@ def bench_prefill(torch, name, steps, warmup, sets=4):
                              d["cu_chunk"], d["seq_idx"], d["last"], d["y"], D=D,
                              state_pool=pool, state_indices=sidx_d,
                              has_initial_state=hinit_d, write_final_to_pool=pool is not None,
-                             chunk_states_out=d["states"]) for d in bufs]
+                             chunk_states_out=None if block_size else d["states"], **extra)
+            for d in bufs]
     ws_bytes = api.ssd_prefill_workspace_size(args[0])
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
     nk = ctypes.c_int32(0)
@@ -255,7 +296,7 @@ def bench_prefill(torch, name, steps, warmup, sets=4):
         torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     kt = _kernel_times(ev_sets, nk.value)
-    work = prefill_work(inp, cuc, sidx)
+    work = prefill_work(inp, cuc, sidx, state_writes)
     if "k_chunk_chain" in knames:
         work["k_chunk_prep"] = work.pop("k_chunk_prep/chain")
     return dict(inp=inp, C=C, total_ms=total_ms, ms_per_step=total_ms / steps,
@@ -490,6 +531,18 @@ def main():
             "ms_per_step": round(res2["ms_per_step"], 5), "roofline": rep2["roofline"],
             "kernels": rep2["kernels"], "path": rep2["path"]}
         del res2
+        torch.cuda.empty_cache()
+        _log("nemotron_h_prefix_cache, all cache mode")
+        res3 = bench_prefill(torch, "nemotron_h_prefix_cache", args.steps, args.warmup,
+                             block_size=256)
+        rep3 = prefill_report(res3, "nemotron_h_prefix_cache/all", with_counters=False)
+        line["prefill_nemotron_all_mode"] = {
+            "workload": "nemotron_h_prefix_cache, all cache mode (block_size 256, one pool "
+                        "entry per block, no chunk-state output)",
+            "value": round(rep3["tokens_per_s"], 1), "unit": "tokens/s",
+            "ms_per_step": round(res3["ms_per_step"], 5), "roofline": rep3["roofline"],
+            "kernels": rep3["kernels"], "path": rep3["path"]}
+        del res3
         torch.cuda.empty_cache()
         _log("mamba1_long_diag")
         line["diag"] = bench_diag(torch, max(3, args.steps // 5), max(1, args.warmup // 5))

@@ -1142,11 +1142,18 @@ __device__ __forceinline__ int chain_xs(int p, int s) { return s ^ ((((p >> 3) ^
 __device__ __forceinline__ int chain_hs(int pl, int n) { return n ^ ((pl & 15) << 3); }
 
 // The state buffer a chain publishes H_k through: the checkpoint output when there is one,
-// else a two-deep ring per (sequence, head) in the workspace (chunk j of a sequence uses
-// entry j & 1; entry reuse is safe because chunk j+2 publishes only after chunk j+1 has
-// read H_j).
+// else (all cache mode, fp32 pool) the pool entry of the cache block chunk k closes, else a
+// two-deep ring per (sequence, head) in the workspace (chunk j of a sequence uses entry
+// j & 1; entry reuse is safe because chunk j+2 publishes only after chunk j+1 has read H_j).
+__device__ __forceinline__ int chain_pool_pub(const PrefillParams& p, int k) {
+  if (p.states || !p.blk_slot || p.pool_bf16) return -1;
+  const int s = ld_meta(p.blk_slot, k);
+  return s < p.num_slots ? s : -1;
+}
 __device__ __forceinline__ float* chain_state(const PrefillParams& p, int k, int h, int r, int j) {
   if (p.states) return p.states + (int64_t(k) * p.H + h) * int64_t(p.P) * p.N;
+  const int s = chain_pool_pub(p, k);
+  if (s >= 0) return static_cast<float*>(p.pool) + int64_t(s) * p.slot_stride + int64_t(h) * p.P * p.N;
   return p.hring + ((int64_t(r) * p.H + h) * 2 + (j & 1)) * int64_t(p.P) * p.N;
 }
 
@@ -1450,7 +1457,8 @@ void k_chunk_chain(PrefillParams p) {
           pool_st4(p.pool, p.pool_bf16, e + hoff(q, pt) / 4, as_float4(hn[q][pt]));
     };
     if (fin_e >= 0) to_pool(fin_e);
-    if (blk_e >= 0) to_pool(blk_e);
+    // the block entry, unless the publication above already went there
+    if (blk_e >= 0 && (last || chain_pool_pub(p, k) < 0)) to_pool(blk_e);
     if (!last) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       if (lane == 0)
