@@ -35,6 +35,15 @@ What it computes, and where that is defined
   padded with NULL_BLOCK_ID skipped, and the restore checkpoint chosen by
   num_accepted_tokens ("[vLLM] Mamba (SSM)": metadata dataclass, MetadataBuilder init,
   CUDA Graph support section, and "why this design", items 2 and 4).
+* Causal depthwise conv1d ahead of the SSD ("vLLM Mamba2 SSD kernel warm-up",
+  mamba_mixer2.py section: hidden_states, B and C are taken after a depthwise
+  convolution; "vLLM v0.20.0 adds disaggregated serving for hybrid SSM models": the conv
+  state of a block is (conv_dim, state_len) or its transpose, state_len 3 in the worked
+  example, i.e. a kernel width of 4).  Per channel c with width W and the previous W-1
+  inputs kept as the conv state (oldest first):
+      out[t, c] = bias[c] + sum_{k=0..W-1} w[c, k] * u[t - (W-1) + k, c]
+  where u is the state followed by the new inputs; an optional SiLU v * sigmoid(v)
+  follows; the new state is the last W-1 entries of u.
 * "all" cache mode (prefix caching, same page: the MetadataBuilder init keeps one state
   index per cache block, and the metadata carries block_idx_first_scheduled_token,
   block_idx_last_computed_token and block_idx_last_scheduled_token).  The pages give the
@@ -54,7 +63,7 @@ import numpy as np
 
 __all__ = [
     "transform_dt", "scan_prefill", "scan_decode", "chunk_metadata", "group_of_head",
-    "block_indices",
+    "block_indices", "conv1d_prefill", "conv1d_update",
 ]
 
 
@@ -262,3 +271,66 @@ def block_indices(num_computed: Sequence[int], new_tokens: Sequence[int], block_
     last_sched = [(n + l - 1) // block_size for n, l in zip(nc, L)]
     return (np.array(first, dtype=np.int32), np.array(last_comp, dtype=np.int32),
             np.array(last_sched, dtype=np.int32))
+
+
+def _conv_window(u: np.ndarray, w: np.ndarray, bias: np.ndarray, activation: bool):
+    """Outputs of a causal depthwise conv over u [W-1 + L, D] (state rows first): one row
+    per new input, out[i] = bias + sum_k w[:, k] * u[i + k]."""
+    W = w.shape[1]
+    L = u.shape[0] - (W - 1)
+    out = np.zeros((L, u.shape[1]))
+    for i in range(L):
+        v = bias.copy()
+        for k in range(W):
+            v = v + w[:, k] * u[i + k]
+        if activation:
+            v = v / (1.0 + np.exp(-v))
+        out[i] = v
+    return out
+
+
+def conv1d_prefill(x, weight, bias, cu_seqlens, conv_states=None,
+                   activation: bool = False):
+    """Varlen causal depthwise conv1d.
+
+    x [T, D]; weight [D, W]; bias [D] or None; cu_seqlens [S+1]; conv_states: None, or a
+    list of S entries, each None (zeros) or a [W-1, D] array (oldest input first).
+    Returns (out [T, D], new_states [S, W-1, D]) in float64.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(weight, dtype=np.float64)
+    D, W = w.shape
+    b = np.zeros(D) if bias is None else np.asarray(bias, dtype=np.float64)
+    cu = [int(v) for v in cu_seqlens]
+    out = np.zeros_like(x)
+    new_states = []
+    for r in range(len(cu) - 1):
+        t0, t1 = cu[r], cu[r + 1]
+        st = np.zeros((W - 1, D))
+        if conv_states is not None and conv_states[r] is not None:
+            st = np.asarray(conv_states[r], dtype=np.float64)
+        u = np.concatenate([st, x[t0:t1]], axis=0)
+        out[t0:t1] = _conv_window(u, w, b, activation)
+        new_states.append(u[u.shape[0] - (W - 1):].copy())
+    return out, np.array(new_states).reshape(len(cu) - 1, W - 1, D)
+
+
+def conv1d_update(conv_pool, state_indices, x, weight, bias, null_block_id: int,
+                  activation: bool = False):
+    """Decode step of the conv: for every row r whose slot state_indices[r] is not
+    null_block_id, the row's ntok inputs x[r] [ntok, D] continue the conv state
+    conv_pool[slot] [W-1, D] (read, never modified here).  Returns (out, writes): out is a
+    dict row -> [ntok, D], writes a dict slot -> the new [W-1, D] state."""
+    w = np.asarray(weight, dtype=np.float64)
+    D, W = w.shape
+    b = np.zeros(D) if bias is None else np.asarray(bias, dtype=np.float64)
+    out, writes = {}, {}
+    for r in range(len(state_indices)):
+        slot = int(state_indices[r])
+        if slot == null_block_id:
+            continue
+        u = np.concatenate([np.asarray(conv_pool[slot], dtype=np.float64),
+                            np.asarray(x[r], dtype=np.float64)], axis=0)
+        out[r] = _conv_window(u, w, b, activation)
+        writes[slot] = u[u.shape[0] - (W - 1):].copy()
+    return out, writes
