@@ -6,6 +6,8 @@
  *   ssd_prefill               device: chunked varlen prefill with initial states gathered
  *                             from a state pool and the state written at every chunk end;
  *   ssd_state_update          device: padded single-token / speculative decode update.
+ * and two more the step before it needs (the causal depthwise conv1d whose outputs are
+ * the scan's x, B and C): ssd_conv1d_prefill and ssd_conv1d_update.
  *
  * The recurrence (per head h, state in R^{P x N}):
  *     h_t = exp(delta_t * A_h) * h_{t-1} + delta_t * x_t B_t^T,   y_t = h_t C_t + D_h x_t
@@ -333,6 +335,94 @@ typedef struct ssd_decode_args {
  * multiple of 4, or of 8 for a bf16 pool with SSD_A_SCALAR), SSD_ERR_HIP.  B_pad == 0 is a
  * no-op. */
 ssd_status ssd_state_update(const ssd_decode_args* args, ssd_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Causal depthwise conv1d (the convolution whose outputs the SSD takes as x, B and C)
+ *
+ * "vLLM Mamba2 SSD kernel warm-up" (mamba_mixer2.py section) takes hidden_states, B and C
+ * after a depthwise convolution; "vLLM v0.20.0 adds disaggregated serving for hybrid SSM
+ * models" keeps one conv state per cache block, (conv_dim, state_len) or its transpose,
+ * with state_len 3 in its worked example ([num_blocks, 3, 3072]).  Per channel c of D, a
+ * width-W causal filter runs over the W-1 carried inputs followed by the new ones:
+ *   out[t, c] = act(bias[c] + sum_{k=0..W-1} weight[c, k] * u[t - (W-1) + k, c])
+ * (weight[c, W-1] multiplies the newest input; act is the identity or SiLU v*sigmoid(v)),
+ * and the conv state becomes the last W-1 inputs of u (the old state shifted left when a
+ * sequence has fewer than W-1 new inputs).  W == 4 is the instantiated width.
+ *
+ * Conv state pool: element (slot, k, c) of a [num_slots] pool with slot_stride elements
+ * between slots, k = 0 the oldest input, in in_dtype, laid out
+ *   SSD_CONV_LAYOUT_SD: [slot][k][c]  (slot_stride >= (W-1)*D, the printed block shape)
+ *   SSD_CONV_LAYOUT_DS: [slot][c][k]  (slot_stride >= D*(W-1), the per-channel layout)
+ * ------------------------------------------------------------------------------------- */
+#define SSD_CONV_LAYOUT_SD 0
+#define SSD_CONV_LAYOUT_DS 1
+#define SSD_CONV_MAX_KERNELS 2
+
+typedef struct ssd_conv1d_args {
+  int32_t T;            /* total tokens                                                 */
+  int32_t D;            /* channels (conv_dim), a multiple of 8                         */
+  int32_t W;            /* kernel width                                                 */
+  int32_t num_seqs;     /* S                                                            */
+  int32_t num_chunks;   /* C of the chunk metadata (ssd_build_chunk_metadata, any
+                           chunk_size): the unit of work, never two sequences           */
+  int32_t in_dtype;     /* ssd_dtype of x, out and the conv state                        */
+  const void* x;   int64_t x_stride_t;    /* [T, D] (device), stride >= D               */
+  void* out;       int64_t out_stride_t;  /* [T, D] out (device), stride >= D           */
+  const float* weight;  /* [D, W] (device, fp32)                                          */
+  const float* bias;    /* [D] (device, fp32) or NULL = 0                                 */
+  int32_t activation;   /* 0: none, 1: SiLU                                               */
+  const int32_t* cu_seqlens;        /* [S+1] (device) */
+  const int32_t* cu_chunk_seqlens;  /* [C+1] (device) */
+  const int32_t* seq_idx;           /* [C]   (device) */
+  void* conv_states;    /* pool (device) or NULL: zero initial states, nothing written     */
+  int64_t slot_stride;
+  int32_t num_slots;
+  int32_t state_layout;               /* SSD_CONV_LAYOUT_*                                */
+  const int32_t* state_indices;       /* [S] slot per sequence (device); NULL only without
+                                         a pool                                           */
+  const int32_t* has_initial_state;   /* [S] 0/1 (device) or NULL = none                  */
+  int32_t* device_error_flag;         /* NULL or an int32 receiving SSD_DEVERR_* bits     */
+  void* const* profile_events;        /* NULL or SSD_CONV_MAX_KERNELS + 1 hipEvent_t,
+                                         recorded before each kernel and after the last */
+} ssd_conv1d_args;
+
+/* Varlen prefill of the conv: out for every token; with a pool, each sequence's state is
+ * read (has_initial_state) and then replaced by its last W-1 inputs, in place.  Two
+ * kernels: the outputs, then the state writes (so every read of an old state precedes
+ * every write).  state_indices of different sequences must be distinct.  Errors:
+ * SSD_ERR_NULL_POINTER, SSD_ERR_BAD_SHAPE, SSD_ERR_UNSUPPORTED (W != 4, D % 8, pointers
+ * not 16-byte aligned or strides not multiples of 8 elements), SSD_ERR_HIP.  Device
+ * checks: a bad chunk raises SSD_DEVERR_CHUNK_RANGE, a slot out of range
+ * SSD_DEVERR_SLOT_RANGE (that sequence's state is neither read nor written).  S == 0 is a
+ * no-op. */
+ssd_status ssd_conv1d_prefill(const ssd_conv1d_args* args, ssd_stream_t stream);
+
+typedef struct ssd_conv1d_update_args {
+  int32_t B_pad;        /* rows, including padding rows                                 */
+  int32_t ntok;         /* inputs per row, 1..16, processed in order                    */
+  int32_t D, W;
+  int32_t in_dtype;
+  const void* x;        /* [B_pad, ntok, D] (device, contiguous)                          */
+  void* out;            /* [B_pad, ntok, D] out                                           */
+  const float* weight;  /* [D, W] fp32                                                    */
+  const float* bias;    /* [D] fp32 or NULL                                               */
+  int32_t activation;
+  void* conv_states;    /* pool (device), as for the prefill                              */
+  int64_t slot_stride;
+  int32_t num_slots;
+  int32_t state_layout;
+  const int32_t* state_indices;  /* [B_pad] (device); rows whose entry is null_block_id are
+                                    padding: nothing read or written                      */
+  int32_t null_block_id;
+  int32_t* device_error_flag;
+  void* const* profile_events;   /* NULL or 2 hipEvent_t around the kernel                */
+} ssd_conv1d_update_args;
+
+/* Decode step of the conv: each live row's ntok inputs continue its slot's state, which is
+ * then replaced in place.  Slots of live rows must be distinct.  Errors as for the
+ * prefill (also ntok outside 1..16: SSD_ERR_UNSUPPORTED); a slot out of range skips the
+ * row and raises SSD_DEVERR_SLOT_RANGE.  B_pad == 0 is a no-op. */
+ssd_status ssd_conv1d_update(const ssd_conv1d_update_args* args, ssd_stream_t stream);
 
 #ifdef __cplusplus
 }

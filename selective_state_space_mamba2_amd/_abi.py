@@ -79,6 +79,34 @@ class DecodeArgs(ctypes.Structure):
     ]
 
 
+SSD_CONV_LAYOUT_SD = 0
+SSD_CONV_LAYOUT_DS = 1
+SSD_CONV_MAX_KERNELS = 2
+
+
+class Conv1dArgs(ctypes.Structure):
+    _fields_ = [
+        ("T", _i32), ("D", _i32), ("W", _i32), ("num_seqs", _i32), ("num_chunks", _i32),
+        ("in_dtype", _i32),
+        ("x", _vp), ("x_stride_t", _i64), ("out", _vp), ("out_stride_t", _i64),
+        ("weight", _vp), ("bias", _vp), ("activation", _i32),
+        ("cu_seqlens", _vp), ("cu_chunk_seqlens", _vp), ("seq_idx", _vp),
+        ("conv_states", _vp), ("slot_stride", _i64), ("num_slots", _i32),
+        ("state_layout", _i32), ("state_indices", _vp), ("has_initial_state", _vp),
+        ("device_error_flag", _vp), ("profile_events", _vp),
+    ]
+
+
+class Conv1dUpdateArgs(ctypes.Structure):
+    _fields_ = [
+        ("B_pad", _i32), ("ntok", _i32), ("D", _i32), ("W", _i32), ("in_dtype", _i32),
+        ("x", _vp), ("out", _vp), ("weight", _vp), ("bias", _vp), ("activation", _i32),
+        ("conv_states", _vp), ("slot_stride", _i64), ("num_slots", _i32),
+        ("state_layout", _i32), ("state_indices", _vp), ("null_block_id", _i32),
+        ("device_error_flag", _vp), ("profile_events", _vp),
+    ]
+
+
 EXPORTS = {
     "ssd_abi_version": (ctypes.c_int, []),
     "ssd_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -91,6 +119,8 @@ EXPORTS = {
                                                 ctypes.POINTER(ctypes.c_int32),
                                                 ctypes.POINTER(ctypes.c_char_p)]),
     "ssd_state_update": (ctypes.c_int, [ctypes.POINTER(DecodeArgs), _vp]),
+    "ssd_conv1d_prefill": (ctypes.c_int, [ctypes.POINTER(Conv1dArgs), _vp]),
+    "ssd_conv1d_update": (ctypes.c_int, [ctypes.POINTER(Conv1dUpdateArgs), _vp]),
 }
 
 _lib = None

@@ -18,7 +18,7 @@ from ._abi import DecodeArgs, PrefillArgs, check, lib
 __all__ = [
     "ssd_abi_version", "ssd_status_string", "ssd_chunk_metadata_count",
     "ssd_build_chunk_metadata", "ssd_prefill_workspace_size", "ssd_prefill",
-    "ssd_state_update", "prefill_args",
+    "ssd_state_update", "prefill_args", "ssd_conv1d_prefill", "ssd_conv1d_update",
 ]
 
 
@@ -215,3 +215,85 @@ def ssd_state_update(x, dt, A, B, C, state_pool, state_indices, y=None, stream=N
     args = decode_args(x, dt, A, B, C, y, state_pool, state_indices, **kw)
     check("ssd_state_update", lib().ssd_state_update(ctypes.byref(args), _stream_ptr(stream)))
     return y
+
+
+def conv1d_args(x, weight, bias, out, cu_seqlens, cu_chunk_seqlens, seq_idx,
+                activation: bool = False, conv_states=None, state_indices=None,
+                has_initial_state=None, state_layout: str = "sd",
+                device_error_flag=None) -> _abi.Conv1dArgs:
+    """Fill an ssd_conv1d_args.  x, out [T, D] (rows contiguous); weight [D, W] fp32;
+    conv_states [slots, W-1, D] ("sd") or [slots, D, W-1] ("ds") in x's dtype."""
+    T, D = x.shape
+    for name, t in (("x", x), ("out", out)):
+        if t.stride(1) != 1:
+            raise ValueError(f"{name}: each token row must be contiguous")
+    if not weight.is_contiguous():
+        raise ValueError("weight must be contiguous")
+    a = _abi.Conv1dArgs()
+    a.T, a.D, a.W = T, D, weight.shape[1]
+    a.num_seqs = cu_seqlens.numel() - 1
+    a.num_chunks = seq_idx.numel()
+    a.in_dtype = _dtype_code(x)
+    a.x, a.x_stride_t = x.data_ptr(), x.stride(0)
+    a.out, a.out_stride_t = out.data_ptr(), out.stride(0)
+    a.weight, a.bias = weight.data_ptr(), _dptr(bias)
+    a.activation = 1 if activation else 0
+    a.cu_seqlens, a.cu_chunk_seqlens = cu_seqlens.data_ptr(), cu_chunk_seqlens.data_ptr()
+    a.seq_idx = seq_idx.data_ptr()
+    if conv_states is not None:
+        a.conv_states = conv_states.data_ptr()
+        a.slot_stride = conv_states.stride(0)
+        a.num_slots = conv_states.shape[0]
+    a.state_layout = _abi.SSD_CONV_LAYOUT_DS if state_layout == "ds" else _abi.SSD_CONV_LAYOUT_SD
+    a.state_indices = _dptr(state_indices)
+    a.has_initial_state = _dptr(has_initial_state)
+    a.device_error_flag = _dptr(device_error_flag)
+    return a
+
+
+def ssd_conv1d_prefill(x, weight, bias, cu_seqlens, cu_chunk_seqlens, seq_idx, out=None,
+                       stream=None, **kw):
+    """Run the varlen causal conv1d (states updated in place when a pool is given).
+    Returns out."""
+    import torch
+    if out is None:
+        out = torch.empty_like(x)
+    args = conv1d_args(x, weight, bias, out, cu_seqlens, cu_chunk_seqlens, seq_idx, **kw)
+    check("ssd_conv1d_prefill", lib().ssd_conv1d_prefill(ctypes.byref(args),
+                                                         _stream_ptr(stream)))
+    return out
+
+
+def conv1d_update_args(x, weight, bias, out, conv_states, state_indices,
+                       activation: bool = False, null_block_id: int = 0,
+                       state_layout: str = "sd", device_error_flag=None) -> _abi.Conv1dUpdateArgs:
+    """Fill an ssd_conv1d_update_args.  x, out [B_pad, ntok, D] contiguous."""
+    B_pad, ntok, D = x.shape
+    for name, t in (("x", x), ("out", out), ("weight", weight),
+                    ("state_indices", state_indices)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    a = _abi.Conv1dUpdateArgs()
+    a.B_pad, a.ntok, a.D, a.W = B_pad, ntok, D, weight.shape[1]
+    a.in_dtype = _dtype_code(x)
+    a.x, a.out, a.weight, a.bias = x.data_ptr(), out.data_ptr(), weight.data_ptr(), _dptr(bias)
+    a.activation = 1 if activation else 0
+    a.conv_states = conv_states.data_ptr()
+    a.slot_stride = conv_states.stride(0)
+    a.num_slots = conv_states.shape[0]
+    a.state_layout = _abi.SSD_CONV_LAYOUT_DS if state_layout == "ds" else _abi.SSD_CONV_LAYOUT_SD
+    a.state_indices = state_indices.data_ptr()
+    a.null_block_id = int(null_block_id)
+    a.device_error_flag = _dptr(device_error_flag)
+    return a
+
+
+def ssd_conv1d_update(x, weight, bias, conv_states, state_indices, out=None, stream=None,
+                      **kw):
+    """One decode step of the conv, in place on ``conv_states``.  Returns out."""
+    import torch
+    if out is None:
+        out = torch.empty_like(x)
+    args = conv1d_update_args(x, weight, bias, out, conv_states, state_indices, **kw)
+    check("ssd_conv1d_update", lib().ssd_conv1d_update(ctypes.byref(args), _stream_ptr(stream)))
+    return out

@@ -250,6 +250,53 @@ def _nemotron_structure(seed: int, n_seqs: int = 16, cs: int = 256):
     return [int(v) for v in lengths], nc
 
 
+@dataclasses.dataclass
+class ConvInputs:
+    """A causal conv1d batch: x [T, D] (stored like the prefill token tensors), weight
+    [D, W] and bias [D] (exact fp32 values), a conv-state pool [slots, W-1, D] of values
+    rounded to the input dtype (fp64 here), one slot per sequence and has_initial_state."""
+    in_dtype: str
+    T: int
+    D: int
+    W: int
+    cu_seqlens: np.ndarray
+    num_computed: np.ndarray
+    x: np.ndarray
+    weight: np.ndarray
+    bias: np.ndarray
+    pool: np.ndarray
+    state_indices: np.ndarray
+    has_initial_state: np.ndarray
+
+    def values(self, a: np.ndarray) -> np.ndarray:
+        return bf16_from_bits(a) if self.in_dtype == "bf16" else np.asarray(a, dtype=np.float64)
+
+
+def make_conv(seed: int, *, in_dtype: str, D: int, lengths, num_computed=None, W: int = 4,
+              pool_slots: int = 0, p_init: float = 0.5) -> ConvInputs:
+    """Draw one conv1d batch: x ~ N(0, 1), weight ~ N(0, 1/W), bias ~ N(0, 0.1), pool
+    states ~ N(0, 1) rounded to the input dtype, distinct slots in [1, pool_slots),
+    has_initial_state ~ Bernoulli(p_init)."""
+    rng = np.random.default_rng(seed)
+    lengths = [int(v) for v in lengths]
+    S = len(lengths)
+    cu = np.zeros(S + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lengths)
+    T = int(cu[-1])
+    nc = np.zeros(S, dtype=np.int32) if num_computed is None else np.asarray(num_computed, dtype=np.int32)
+    x = _store(_draw_normal(rng, (T, D), T * D > (1 << 24)), in_dtype)
+    weight = (rng.standard_normal((D, W)) / np.sqrt(W)).astype(np.float32).astype(np.float64)
+    bias = (0.1 * rng.standard_normal(D)).astype(np.float32).astype(np.float64)
+    slots = max(pool_slots, S + 1)
+    pool = rng.standard_normal((slots, W - 1, D), dtype=np.float32)
+    pool = bf16_round(pool) if in_dtype == "bf16" else pool.astype(np.float64)
+    sidx = (rng.permutation(slots - 1)[:S] + 1).astype(np.int32)
+    has_init = (rng.uniform(size=S) < p_init).astype(np.int32)
+    return ConvInputs(in_dtype=in_dtype, T=T, D=D, W=W, cu_seqlens=cu, num_computed=nc, x=x,
+                      weight=weight, bias=bias, pool=pool, state_indices=sidx,
+                      has_initial_state=has_init)
+
+
 def workload(name: str, seed: Optional[int] = None):
     """Build one of the named workloads (full size).  Returns PrefillInputs or
     DecodeInputs."""

@@ -19,7 +19,7 @@ HEADER = os.path.join(ROOT, "include", "ssd.h")
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(ssd_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(ssd_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_every_declared_function_is_exported():
@@ -56,7 +56,9 @@ def _c_layout(struct_name, fields):
 
 
 @pytest.mark.parametrize("struct,cls", [("ssd_prefill_args", PrefillArgs),
-                                        ("ssd_decode_args", DecodeArgs)])
+                                        ("ssd_decode_args", DecodeArgs),
+                                        ("ssd_conv1d_args", _abi.Conv1dArgs),
+                                        ("ssd_conv1d_update_args", _abi.Conv1dUpdateArgs)])
 def test_struct_layout_matches_header(struct, cls):
     names = [f[0] for f in cls._fields_]
     got = _c_layout(struct, names)
@@ -283,3 +285,72 @@ def test_decode_host_checks(over, status):
 
 def test_decode_empty_batch_is_a_noop():
     assert lib().ssd_state_update(ctypes.byref(_good_decode(B_pad=0, x=None)), None) == 0
+
+
+# ----------------------------------------------------------------------------------------
+# conv1d host checks (no launch happens for any of these)
+# ----------------------------------------------------------------------------------------
+def _good_conv(**over):
+    a = _abi.Conv1dArgs()
+    a.T, a.D, a.W, a.num_seqs, a.num_chunks, a.in_dtype = 512, 3072, 4, 2, 3, _abi.SSD_BF16
+    a.x = a.out = a.weight = a.cu_seqlens = a.cu_chunk_seqlens = a.seq_idx = FAKE
+    a.x_stride_t = a.out_stride_t = 3072
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+_CONV_POOL = dict(conv_states=FAKE, state_indices=FAKE, num_slots=8, slot_stride=3 * 3072)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(T=-1), _abi.SSD_ERR_BAD_SHAPE),
+    (dict(W=1), _abi.SSD_ERR_BAD_SHAPE),
+    (dict(W=3), _abi.SSD_ERR_UNSUPPORTED),
+    (dict(D=3076, x_stride_t=3076, out_stride_t=3076), _abi.SSD_ERR_UNSUPPORTED),
+    (dict(in_dtype=5), _abi.SSD_ERR_BAD_SHAPE),
+    (dict(activation=2), _abi.SSD_ERR_BAD_SHAPE),
+    (dict(state_layout=2), _abi.SSD_ERR_BAD_SHAPE),
+    (dict(num_chunks=1), _abi.SSD_ERR_BAD_SHAPE),            # fewer chunks than sequences
+    (dict(x_stride_t=3000), _abi.SSD_ERR_BAD_SHAPE),
+    (dict(x=None), _abi.SSD_ERR_NULL_POINTER),
+    (dict(weight=None), _abi.SSD_ERR_NULL_POINTER),
+    (dict(conv_states=FAKE), _abi.SSD_ERR_NULL_POINTER),     # a pool needs state_indices
+    (dict(_CONV_POOL, slot_stride=3 * 3072 - 8), _abi.SSD_ERR_BAD_SHAPE),
+    (dict(_CONV_POOL, num_slots=0), _abi.SSD_ERR_BAD_SHAPE),
+    (dict(_CONV_POOL, conv_states=FAKE + 8), _abi.SSD_ERR_UNSUPPORTED),
+    (dict(x=FAKE + 4), _abi.SSD_ERR_UNSUPPORTED),
+    (dict(x_stride_t=3076), _abi.SSD_ERR_UNSUPPORTED),
+    (dict(bias=FAKE + 4), _abi.SSD_ERR_UNSUPPORTED),
+])
+def test_conv1d_prefill_host_checks(over, status):
+    assert lib().ssd_conv1d_prefill(ctypes.byref(_good_conv(**over)), None) == status
+
+
+def test_conv1d_prefill_empty_batch_is_a_noop():
+    a = _good_conv(T=0, num_seqs=0, num_chunks=0, x=None)
+    assert lib().ssd_conv1d_prefill(ctypes.byref(a), None) == _abi.SSD_OK
+
+
+def _good_conv_update(**over):
+    a = _abi.Conv1dUpdateArgs()
+    a.B_pad, a.ntok, a.D, a.W, a.in_dtype = 8, 1, 3072, 4, _abi.SSD_BF16
+    a.x = a.out = a.weight = a.conv_states = a.state_indices = FAKE
+    a.num_slots, a.slot_stride = 16, 3 * 3072
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(ntok=0), _abi.SSD_ERR_BAD_SHAPE),
+    (dict(ntok=17), _abi.SSD_ERR_UNSUPPORTED),
+    (dict(W=5), _abi.SSD_ERR_UNSUPPORTED),
+    (dict(conv_states=None), _abi.SSD_ERR_NULL_POINTER),
+    (dict(state_indices=None), _abi.SSD_ERR_NULL_POINTER),
+    (dict(slot_stride=100), _abi.SSD_ERR_BAD_SHAPE),
+    (dict(out=FAKE + 2), _abi.SSD_ERR_UNSUPPORTED),
+    (dict(B_pad=0, x=None), _abi.SSD_OK),
+])
+def test_conv1d_update_host_checks(over, status):
+    assert lib().ssd_conv1d_update(ctypes.byref(_good_conv_update(**over)), None) == status

@@ -1,0 +1,182 @@
+"""GPU parity of the causal depthwise conv1d (varlen prefill and decode update) against
+the fp64 oracle on the same seeded inputs: outputs at the input dtype's tolerance, the new
+conv states bit-exact (they are copies of inputs and old states), every other slot
+untouched, in both conv-state layouts."""
+import numpy as np
+import pytest
+
+from gpu_helpers import TOL, assert_close, host64, torch
+from oracle import conv1d_prefill, conv1d_update
+from selective_state_space_mamba2_amd import _abi, api
+from selective_state_space_mamba2_amd.inputs import make_conv
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev_x(inp, a):
+    t = torch()
+    if inp.in_dtype == "bf16":
+        return t.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(t.bfloat16).cuda()
+    return t.from_numpy(np.asarray(a, dtype=np.float32)).cuda()
+
+
+def _dev_pool(inp, layout):
+    t = torch()
+    pool = inp.pool if layout == "sd" else np.ascontiguousarray(inp.pool.transpose(0, 2, 1))
+    d = t.from_numpy(pool.astype(np.float32)).cuda()
+    return d.to(t.bfloat16) if inp.in_dtype == "bf16" else d
+
+
+def _host_pool(d, layout):
+    a = d.float().cpu().numpy().astype(np.float64)
+    return a if layout == "sd" else np.ascontiguousarray(a.transpose(0, 2, 1))
+
+
+def _i32(a):
+    return torch().from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+
+def _run_prefill(inp, cs, *, layout="sd", act=False, pool=True, x_pad=0, out_pad=0):
+    t = torch()
+    cuc, sidx, _ = api.ssd_build_chunk_metadata(inp.cu_seqlens, inp.num_computed, cs)
+    xd = _dev_x(inp, inp.x)
+    if x_pad:
+        buf = t.zeros(inp.T, inp.D + x_pad, dtype=xd.dtype, device="cuda")
+        buf[:, :inp.D] = xd
+        xd = buf[:, :inp.D]
+    obuf = t.full((inp.T, inp.D + out_pad), float("nan"), dtype=xd.dtype, device="cuda")
+    out = obuf[:, :inp.D]
+    pd = _dev_pool(inp, layout) if pool else None
+    flag = t.zeros(1, dtype=t.int32, device="cuda")
+    api.ssd_conv1d_prefill(
+        xd, _f32(inp.weight), _f32(inp.bias), _i32(inp.cu_seqlens), _i32(cuc), _i32(sidx),
+        out=out, activation=act, conv_states=pd,
+        state_indices=_i32(inp.state_indices) if pool else None,
+        has_initial_state=_i32(inp.has_initial_state) if pool else None,
+        state_layout=layout, device_error_flag=flag)
+    t.cuda.synchronize()
+    return dict(out=host64(out), flag=int(flag.item()),
+                pool=_host_pool(pd, layout) if pool else None)
+
+
+def _f32(a):
+    return torch().from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def _oracle_prefill(inp, act, pool=True):
+    states = None
+    if pool:
+        states = [inp.pool[inp.state_indices[r]] if inp.has_initial_state[r] else None
+                  for r in range(len(inp.state_indices))]
+    return conv1d_prefill(inp.values(inp.x), inp.weight, inp.bias, inp.cu_seqlens,
+                          conv_states=states, activation=act)
+
+
+def _check_prefill(inp, got, ref_out, ref_states, pool=True):
+    assert got["flag"] == 0
+    assert_close(got["out"], ref_out, TOL[inp.in_dtype], "conv out")
+    if pool:
+        for r, slot in enumerate(inp.state_indices):
+            np.testing.assert_array_equal(got["pool"][slot], ref_states[r], f"state seq {r}")
+        untouched = sorted(set(range(inp.pool.shape[0])) - set(int(s) for s in inp.state_indices))
+        np.testing.assert_array_equal(got["pool"][untouched], inp.pool[untouched])
+
+
+LENGTHS = [300, 1, 2, 3, 77, 256, 5]
+NC = [0, 5, 255, 0, 100, 3, 62]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("layout", ["sd", "ds"])
+@pytest.mark.parametrize("act", [False, True])
+def test_prefill_varlen_with_pool(dtype, layout, act):
+    """Sequences of 1, 2 and 3 tokens (windows reaching into the state, states only
+    partly replaced), chunks cut at unaligned resume points, a partial channel block."""
+    inp = make_conv(61, in_dtype=dtype, D=1040, lengths=LENGTHS, num_computed=NC,
+                    pool_slots=12)
+    got = _run_prefill(inp, 64, layout=layout, act=act)
+    _check_prefill(inp, got, *_oracle_prefill(inp, act))
+
+
+@pytest.mark.parametrize("cs", [1, 16, 256, 2048])
+def test_prefill_any_chunk_size(cs):
+    inp = make_conv(62, in_dtype="bf16", D=512, lengths=LENGTHS, num_computed=NC, pool_slots=9)
+    got = _run_prefill(inp, cs)
+    _check_prefill(inp, got, *_oracle_prefill(inp, False))
+
+
+def test_prefill_without_pool_and_strided_rows():
+    inp = make_conv(63, in_dtype="bf16", D=256, lengths=[40, 9, 1], pool_slots=4)
+    got = _run_prefill(inp, 32, pool=False, x_pad=24, out_pad=8)
+    ref_out, _ = _oracle_prefill(inp, False, pool=False)
+    _check_prefill(inp, got, ref_out, None, pool=False)
+
+
+def test_prefill_full_size_prefix_cache_structure():
+    """The Nemotron-H-like batch (16 sequences of 512..8192 new tokens resuming at
+    unaligned points) with 3072 conv channels and chunks of 256, in the launch the bench
+    times: three sequences' outputs and states against the oracle, every sequence's state
+    against the property that holds at any size (L >= W-1: the last W-1 inputs)."""
+    from selective_state_space_mamba2_amd.inputs import _nemotron_structure
+    lengths, nc = _nemotron_structure(2, cs=256)
+    inp = make_conv(64, in_dtype="bf16", D=3072, lengths=lengths, num_computed=nc,
+                    pool_slots=1024, p_init=1.0)
+    got = _run_prefill(inp, 256, act=True)
+    assert got["flag"] == 0
+    cu = inp.cu_seqlens
+    for r in (0, 7, 15):
+        t0, t1 = int(cu[r]), int(cu[r + 1])
+        out, st = conv1d_prefill(inp.values(inp.x[t0:t1]), inp.weight, inp.bias, [0, t1 - t0],
+                                 conv_states=[inp.pool[inp.state_indices[r]]], activation=True)
+        assert_close(got["out"][t0:t1], out, TOL["bf16"], f"seq {r}")
+        np.testing.assert_array_equal(got["pool"][inp.state_indices[r]], st[0])
+    for r in range(len(lengths)):
+        t1 = int(cu[r + 1])
+        np.testing.assert_array_equal(got["pool"][inp.state_indices[r]],
+                                      inp.values(inp.x[t1 - 3:t1]), f"state seq {r}")
+
+
+def test_prefill_bad_slot_raises_the_flag():
+    inp = make_conv(65, in_dtype="bf16", D=64, lengths=[5, 6], pool_slots=4, p_init=1.0)
+    inp.state_indices[1] = 4                      # one past the pool
+    got = _run_prefill(inp, 64)
+    assert got["flag"] == _abi.SSD_DEVERR_SLOT_RANGE
+    # sequence 0 is complete and exact; sequence 1 is flagged (no slot of it touched)
+    ref_out, ref_states = conv1d_prefill(inp.values(inp.x[:5]), inp.weight, inp.bias, [0, 5],
+                                         conv_states=[inp.pool[inp.state_indices[0]]])
+    assert_close(got["out"][:5], ref_out, TOL["bf16"], "seq 0")
+    np.testing.assert_array_equal(got["pool"][inp.state_indices[0]], ref_states[0])
+    others = [s for s in range(inp.pool.shape[0]) if s != inp.state_indices[0]]
+    np.testing.assert_array_equal(got["pool"][others], inp.pool[others])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("layout", ["sd", "ds"])
+@pytest.mark.parametrize("ntok", [1, 3])
+def test_update_padded_batch(dtype, layout, ntok):
+    t = torch()
+    rng = np.random.default_rng(66)
+    B_pad, n_live, D = 10, 7, 1040
+    inp = make_conv(67, in_dtype=dtype, D=D, lengths=[ntok] * B_pad, pool_slots=24)
+    idx = np.zeros(B_pad, dtype=np.int32)        # null_block_id 0 marks padding rows
+    idx[:n_live] = rng.permutation(np.arange(1, 24))[:n_live]
+    xd = _dev_x(inp, inp.x).reshape(B_pad, ntok, D)
+    out = t.full_like(xd, 5.0)
+    pd = _dev_pool(inp, layout)
+    flag = t.zeros(1, dtype=t.int32, device="cuda")
+    api.ssd_conv1d_update(xd, _f32(inp.weight), _f32(inp.bias), pd, _i32(idx), out=out,
+                          activation=True, null_block_id=0, state_layout=layout,
+                          device_error_flag=flag)
+    t.cuda.synchronize()
+    assert int(flag.item()) == 0
+    ref, writes = conv1d_update(inp.pool, idx, inp.values(inp.x).reshape(B_pad, ntok, D),
+                                inp.weight, inp.bias, null_block_id=0, activation=True)
+    oh = host64(out)
+    for r, o in ref.items():
+        assert_close(oh[r], o, TOL[dtype], f"row {r}")
+    assert np.all(oh[n_live:] == 5.0)
+    ph = _host_pool(pd, layout)
+    for slot, st in writes.items():
+        np.testing.assert_array_equal(ph[slot], st, f"slot {slot}")
+    untouched = sorted(set(range(inp.pool.shape[0])) - set(writes))
+    np.testing.assert_array_equal(ph[untouched], inp.pool[untouched])
