@@ -10,8 +10,9 @@ device, and the two prefill kernels.  Inputs are resident in HBM before timing s
 four input/output buffer sets rotate so the 256 MB Infinity Cache cannot hold a step's
 working set.  The line printed also carries the decode state update (256 live requests of
 a 512-row padded batch, 1+3 tokens, [2048,48,64,128] fp32 pool), the Nemotron-H-like
-varlen prefill with prefix caching and the Mamba1 long-context diagonal scan as secondary
-objects.
+varlen prefill with prefix caching (also in the all cache mode), the Mamba1 long-context
+diagonal scan and decode, the decode with a bf16 state pool, and the causal conv1d prefill
+and decode update as secondary objects.
 
 Roofline: each kernel's duration comes from HIP events the library records around its
 own launches on the launch stream (the C ABI's timing hook), averaged over the timed
@@ -390,7 +391,7 @@ def bench_decode(torch, steps, warmup, with_cpu=True, name="decode_spec", pool_b
            "value": round(w["updates"] / (ms * 1e-3), 1), "unit": "state-updates/s",
            "ms_per_step": round(ms, 5),
            "roofline": _roofline("hbm", w["bytes"] / (kms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s",
-                                 None if pool_bf16 else _counter_traffic(kname, name,
+                                 _counter_traffic(kname, name + ("/bf16_pool" if pool_bf16 else ""),
                                                   _source_digest("ssd_decode.hip", "ssd_device.h")),
                                  kname),
            "kernel_ms": round(kms, 5), "alg_bytes": w["bytes"]}
@@ -456,9 +457,188 @@ def bench_diag(torch, steps, warmup):
             "value": round(inp.T / (ms * 1e-3), 1), "unit": "tokens/s",
             "ms_per_step": round(ms, 5), "kernel_ms": round(kms, 5),
             "roofline": _roofline("alu", lane_ops / (kms * 1e-3) / 1e12,
-                                  round(VALU_LANE_OPS / 1e12, 2), "T lane-op/s", None,
+                                  round(VALU_LANE_OPS / 1e12, 2), "T lane-op/s",
+                                  _counter_traffic("k_diag_scan", "mamba1_long_diag",
+                                                   _source_digest("ssd_diag.hip", "ssd_device.h")),
                                   "k_diag_scan"),
             "hbm_gb_s": round(w["bytes"] / (kms * 1e-3) / 1e9, 1), "alg_bytes": w["bytes"]}
+
+
+# ----------------------------------------------------------------------------------------
+# causal depthwise conv1d (the step before the scan): varlen prefill and decode update
+# ----------------------------------------------------------------------------------------
+CONV_D = 3072        # conv channels of the pages' worked example (conv state [nb, 3, 3072])
+
+
+def _conv_inputs(torch, inp):
+    import numpy as np
+    if inp.in_dtype == "bf16":
+        x = torch.from_numpy(np.ascontiguousarray(inp.x).view(np.int16)).view(torch.bfloat16)
+    else:
+        x = torch.from_numpy(np.asarray(inp.x, dtype=np.float32))
+    pool = torch.from_numpy(inp.pool.astype(np.float32)).cuda()
+    if inp.in_dtype == "bf16":
+        pool = pool.to(torch.bfloat16)
+    w = torch.from_numpy(inp.weight.astype(np.float32)).cuda()
+    b = torch.from_numpy(inp.bias.astype(np.float32)).cuda()
+    return x.cuda(), pool, w, b
+
+
+def bench_conv_prefill(torch, steps, warmup):
+    """The conv over the Nemotron-H-like varlen batch (16 sequences resuming at unaligned
+    points, chunk metadata of chunk 256), 3072 bf16 channels, SiLU, every conv state read
+    from and written back to a 1024-slot pool."""
+    import ctypes
+    import numpy as np
+    from selective_state_space_mamba2_amd import api
+    from selective_state_space_mamba2_amd._abi import SSD_CONV_MAX_KERNELS, check, lib
+    from selective_state_space_mamba2_amd.inputs import _nemotron_structure, make_conv
+    lengths, nc = _nemotron_structure(2, cs=256)
+    inp = make_conv(64, in_dtype="bf16", D=CONV_D, lengths=lengths, num_computed=nc,
+                    pool_slots=1024, p_init=1.0)
+    cuc, sidx, _ = api.ssd_build_chunk_metadata(inp.cu_seqlens, inp.num_computed, 256)
+    x, pool, w, b = _conv_inputs(torch, inp)
+    out = torch.empty_like(x)
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+    a = api.conv1d_args(x, w, b, out, i32(inp.cu_seqlens), i32(cuc), i32(sidx),
+                        activation=True, conv_states=pool, state_indices=i32(inp.state_indices),
+                        has_initial_state=i32(inp.has_initial_state))
+    sp = torch.cuda.current_stream().cuda_stream
+    for _ in range(warmup):
+        check("ssd_conv1d_prefill", lib().ssd_conv1d_prefill(ctypes.byref(a), sp))
+    nk = SSD_CONV_MAX_KERNELS
+    ev_sets = [_events(torch, nk + 1) for _ in _profiled(steps)]
+    handles = [_handles(e) for e in ev_sets]
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with _quiet_gc():
+        start.record()
+        for i in range(steps):
+            a.profile_events = (ctypes.cast(handles[i // PROFILE_EVERY], ctypes.c_void_p)
+                                if i % PROFILE_EVERY == 0 else None)
+            check("ssd_conv1d_prefill", lib().ssd_conv1d_prefill(ctypes.byref(a), sp))
+        end.record()
+        torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    kt = _kernel_times(ev_sets, nk)
+    T, D, S, W = inp.T, inp.D, len(lengths), inp.W
+    # x in and out once; every sequence's old state read (all have one) and new state
+    # written; the taps and bias
+    st = (W - 1) * D * 2
+    k_out = T * D * 2 * 2 + S * st + D * (W + 1) * 4
+    k_state = S * st
+    return {"workload": f"conv1d prefill, nemotron_h_prefix_cache batch ({T} tokens, 16 "
+                        f"sequences), {D} bf16 channels, width {W}, SiLU, 1024-slot pool",
+            "metric": "tokens/s", "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s",
+            "ms_per_step": round(ms, 5),
+            "roofline": _roofline("hbm", k_out / (kt[0] * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s",
+                                  _counter_traffic("k_conv_prefill", "conv1d_prefill",
+                                                   _source_digest("ssd_conv.hip", "ssd_device.h")),
+                                  "k_conv_prefill"),
+            "kernels": {"k_conv_prefill": {"ms": round(kt[0], 5), "alg_bytes": k_out},
+                        "k_conv_state": {"ms": round(kt[1], 5), "alg_bytes": k_state}}}
+
+
+def bench_conv_update(torch, steps, warmup):
+    """One decode step of the conv: 256 live rows of a 512-row padded batch, 1 input each,
+    3072 bf16 channels, SiLU, a 2048-slot pool."""
+    import ctypes
+    import numpy as np
+    from selective_state_space_mamba2_amd import api
+    from selective_state_space_mamba2_amd._abi import check, lib
+    from selective_state_space_mamba2_amd.inputs import make_conv
+    B_pad, n_live, ntok, slots = 512, 256, 1, 2048
+    inp = make_conv(68, in_dtype="bf16", D=CONV_D, lengths=[ntok] * B_pad, pool_slots=slots)
+    rng = np.random.default_rng(69)
+    idx = np.zeros(B_pad, dtype=np.int32)
+    idx[:n_live] = rng.permutation(np.arange(1, slots))[:n_live]
+    x, pool, w, b = _conv_inputs(torch, inp)
+    x = x.reshape(B_pad, ntok, inp.D)
+    out = torch.empty_like(x)
+    a = api.conv1d_update_args(x, w, b, out, pool, torch.from_numpy(idx).cuda(),
+                               activation=True, null_block_id=0)
+    sp = torch.cuda.current_stream().cuda_stream
+    for _ in range(warmup):
+        check("ssd_conv1d_update", lib().ssd_conv1d_update(ctypes.byref(a), sp))
+    ev_sets = [_events(torch, 2) for _ in _profiled(steps)]
+    handles = [_handles(e) for e in ev_sets]
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with _quiet_gc():
+        start.record()
+        for i in range(steps):
+            a.profile_events = (ctypes.cast(handles[i // PROFILE_EVERY], ctypes.c_void_p)
+                                if i % PROFILE_EVERY == 0 else None)
+            check("ssd_conv1d_update", lib().ssd_conv1d_update(ctypes.byref(a), sp))
+        end.record()
+        torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    kms = _kernel_times(ev_sets, 1)[0]
+    D, W = inp.D, inp.W
+    alg = n_live * (2 * (W - 1) * D * 2 + 2 * ntok * D * 2) + D * (W + 1) * 4
+    return {"workload": f"conv1d update, {n_live} live rows of {B_pad}, {ntok} input each, "
+                        f"{D} bf16 channels, SiLU, {slots}-slot pool",
+            "metric": "rows/s", "value": round(n_live / (ms * 1e-3), 1), "unit": "rows/s",
+            "ms_per_step": round(ms, 5), "kernel_ms": round(kms, 5),
+            "roofline": _roofline("hbm", alg / (kms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s",
+                                  _counter_traffic("k_conv_update", "conv1d_update",
+                                                   _source_digest("ssd_conv.hip", "ssd_device.h")),
+                                  "k_conv_update"),
+            "alg_bytes": alg}
+
+
+def measured_peaks(torch, mib=2048, reps=10):
+    """What this GPU reaches with library kernels, as a second scale beside the spec peaks:
+    a device copy (read + write), a fill (write only), a sum (read only) of ``mib`` MiB
+    and a square bf16 GEMM of 8192 (hipBLASLt).  Best of ``reps`` launches each."""
+    n = mib * (1 << 20) // 4
+    a = torch.empty(n, dtype=torch.float32, device="cuda").normal_()
+    b = torch.empty_like(a)
+    s = torch.empty((), dtype=torch.float32, device="cuda")
+
+    def best(fn):
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return min(ts) * 1e-3
+
+    fn_copy, fn_fill = (lambda: b.copy_(a)), (lambda: b.fill_(1.0))
+    fn_sum = lambda: torch.sum(a, dim=0, out=s)
+    for f in (fn_copy, fn_fill, fn_sum):
+        f()
+    nbytes = n * 4
+    out = {"copy_gb_s": round(2 * nbytes / best(fn_copy) / 1e9, 1),
+           "write_gb_s": round(nbytes / best(fn_fill) / 1e9, 1),
+           "read_gb_s": round(nbytes / best(fn_sum) / 1e9, 1)}
+    del a, b
+    m = 8192
+    x = torch.randn(m, m, device="cuda").to(torch.bfloat16)
+    y = torch.randn(m, m, device="cuda").to(torch.bfloat16)
+    z = torch.empty(m, m, device="cuda", dtype=torch.bfloat16)
+    torch.matmul(x, y, out=z)
+    out["bf16_gemm_tflop_s"] = round(2 * m ** 3 / best(lambda: torch.matmul(x, y, out=z)) / 1e12, 1)
+    out["note"] = (f"library kernels on this GPU, best of {reps}: copy/fill/sum of {mib} MiB, "
+                   f"bf16 GEMM {m}^3")
+    del x, y, z
+    torch.cuda.empty_cache()
+    return out
+
+
+def _add_measured_frac(obj, peaks):
+    """Beside each HBM roofline's spec fraction, its fraction of the measured copy rate."""
+    if isinstance(obj, dict):
+        r = obj.get("roofline")
+        if isinstance(r, dict) and r.get("bound") == "hbm":
+            r["measured_peak"] = peaks["copy_gb_s"]
+            r["measured_frac"] = round(r["achieved"] / peaks["copy_gb_s"], 4)
+        for v in obj.values():
+            if isinstance(v, dict) and v is not r:
+                _add_measured_frac(v, peaks)
 
 
 def copy_calibration(torch, mib=1024, reps=3):
@@ -535,7 +715,7 @@ def main():
         _log("nemotron_h_prefix_cache, all cache mode")
         res3 = bench_prefill(torch, "nemotron_h_prefix_cache", args.steps, args.warmup,
                              block_size=256)
-        rep3 = prefill_report(res3, "nemotron_h_prefix_cache/all", with_counters=False)
+        rep3 = prefill_report(res3, "nemotron_h_prefix_cache/all")
         line["prefill_nemotron_all_mode"] = {
             "workload": "nemotron_h_prefix_cache, all cache mode (block_size 256, one pool "
                         "entry per block, no chunk-state output)",
@@ -555,6 +735,16 @@ def main():
         _log("decode_spec, bf16 state pool")
         line["decode_bf16_pool"] = bench_decode(torch, args.steps, args.warmup, with_cpu=False,
                                                 pool_bf16=True)
+        torch.cuda.empty_cache()
+        _log("conv1d prefill")
+        line["conv1d_prefill"] = bench_conv_prefill(torch, args.steps, args.warmup)
+        torch.cuda.empty_cache()
+        _log("conv1d update")
+        line["conv1d_update"] = bench_conv_update(torch, args.steps, args.warmup)
+        _log("measured peaks")
+        peaks = measured_peaks(torch)
+        line["measured_peaks"] = peaks
+        _add_measured_frac(line, peaks)
     print(json.dumps(line), flush=True)
 
 
