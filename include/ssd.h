@@ -391,7 +391,8 @@ typedef struct ssd_conv1d_args {
  * kernels: the outputs, then the state writes (so every read of an old state precedes
  * every write).  state_indices of different sequences must be distinct.  Errors:
  * SSD_ERR_NULL_POINTER, SSD_ERR_BAD_SHAPE, SSD_ERR_UNSUPPORTED (W != 4, D % 8, pointers
- * not 16-byte aligned or strides not multiples of 8 elements), SSD_ERR_HIP.  Device
+ * not 16-byte aligned, strides not multiples of 8 elements, or (T/8 + 1) rows of x or out
+ * spanning 2 GiB or more), SSD_ERR_HIP.  Device
  * checks: a bad chunk raises SSD_DEVERR_CHUNK_RANGE, a slot out of range
  * SSD_DEVERR_SLOT_RANGE (that sequence's state is neither read nor written).  S == 0 is a
  * no-op. */

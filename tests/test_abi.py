@@ -322,6 +322,8 @@ _CONV_POOL = dict(conv_states=FAKE, state_indices=FAKE, num_slots=8, slot_stride
     (dict(x=FAKE + 4), _abi.SSD_ERR_UNSUPPORTED),
     (dict(x_stride_t=3076), _abi.SSD_ERR_UNSUPPORTED),
     (dict(bias=FAKE + 4), _abi.SSD_ERR_UNSUPPORTED),
+    # a wave's rows (T/8 + 1 of them) would span 2 GiB or more of x: 32-bit row offsets
+    (dict(T=1 << 21, x_stride_t=8192, out_stride_t=8192), _abi.SSD_ERR_UNSUPPORTED),
 ])
 def test_conv1d_prefill_host_checks(over, status):
     assert lib().ssd_conv1d_prefill(ctypes.byref(_good_conv(**over)), None) == status
