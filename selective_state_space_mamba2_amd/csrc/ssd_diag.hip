@@ -34,6 +34,18 @@ struct DiagCfg {
   static constexpr int N = kDiagN, LPC = N / SPL, CH = 256 / LPC;
 };
 
+// Sum of v over the aligned group of LPC (2 or 4) lanes, on every lane of the group: DPP
+// quad permutations (lane ^ 1, then lane ^ 2) feed the adds directly, with no LDS trip.
+template <int LPC>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(LPC == 1 || LPC == 2 || LPC == 4, "lanes per channel within a quad");
+  if constexpr (LPC >= 2)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+  if constexpr (LPC >= 4)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+  return v;
+}
+
 template <typename T, int SPL>
 __global__ __launch_bounds__(256) void k_diag_scan(PrefillParams p) {
   constexpr int N = kDiagN;    // 16 states per channel
@@ -179,10 +191,7 @@ __global__ __launch_bounds__(256) void k_diag_scan(PrefillParams p) {
         }
       }
 #pragma unroll
-      for (int u = 0; u < V; ++u) {
-#pragma unroll
-        for (int off = 1; off < LPC; off <<= 1) acc[u] += __shfl_xor(acc[u], off, 64);
-      }
+      for (int u = 0; u < V; ++u) acc[u] = group_sum<LPC>(acc[u]);
       if (ng == 0) {
 #pragma unroll
         for (int u = 0; u < V; ++u) s_y[tt + u][cl] = acc[u] + Dc * xv[u];
