@@ -330,8 +330,10 @@ def prefill_report(res, name, with_counters=True):
     )
 
 
-def cpu_baseline_prefill(inp, n_seqs=2):
-    """The fp64 oracle on the first ``n_seqs`` sequences of the workload, all heads."""
+def cpu_baseline_prefill(inp, n_seqs=None):
+    """The fp64 oracle on the first ``n_seqs`` sequences of the workload (default: all of
+    them, i.e. the whole timed step), all heads."""
+    n_seqs = inp.num_seqs if n_seqs is None else n_seqs
     from oracle import scan_prefill
     from selective_state_space_mamba2_amd.inputs import bf16_from_bits
     t1 = int(inp.cu_seqlens[n_seqs])
@@ -398,7 +400,7 @@ def bench_decode(torch, steps, warmup, with_cpu=True, name="decode_spec", pool_b
     if with_cpu:
         from oracle import scan_decode
         from selective_state_space_mamba2_amd.inputs import bf16_from_bits
-        rows = list(range(32))
+        rows = list(range(inp.n_live))     # every live row: the whole timed step
         w0, c0 = time.perf_counter(), time.process_time()
         scan_decode(inp.pool, inp.state_indices, inp.num_accepted, bf16_from_bits(inp.x),
                     bf16_from_bits(inp.dt), inp.A, bf16_from_bits(inp.B), bf16_from_bits(inp.C),
