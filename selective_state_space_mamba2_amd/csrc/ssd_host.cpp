@@ -14,6 +14,7 @@ namespace ssd {
 const ChunkedShape kChunkedShapes[] = {
     {SSD_BF16, 64, 128, 256}, {SSD_BF16, 64, 128, 128}, {SSD_BF16, 64, 128, 64},
     {SSD_BF16, 16, 16, 64},   {SSD_F32, 16, 16, 64},    {SSD_F32, 64, 128, 64},
+    {SSD_BF16, 16, 16, 256},  {SSD_F32, 16, 16, 256},   {SSD_F32, 64, 128, 256},
 };
 const int kNumChunkedShapes = sizeof(kChunkedShapes) / sizeof(kChunkedShapes[0]);
 

@@ -1575,6 +1575,8 @@ static const RunFn kRun[] = {
     run_chunked<bf16_t, 64, 128, 256>, run_chunked<bf16_t, 64, 128, 128>,
     run_chunked<bf16_t, 64, 128, 64>,  run_chunked<bf16_t, 16, 16, 64>,
     run_chunked<float, 16, 16, 64>,    run_chunked<float, 64, 128, 64>,
+    run_chunked<bf16_t, 16, 16, 256>,  run_chunked<float, 16, 16, 256>,
+    run_chunked<float, 64, 128, 256>,
 };
 
 hipError_t launch_chunked_prefill(int variant, const PrefillParams& p, hipStream_t s,

@@ -202,7 +202,7 @@ def test_kernel_count():
      _abi.SSD_ERR_BAD_SHAPE),
     (dict(P=32), _abi.SSD_ERR_UNSUPPORTED),                # not instantiated
     (dict(chunk_size=100), _abi.SSD_ERR_UNSUPPORTED),
-    (dict(in_dtype=_abi.SSD_F32), _abi.SSD_ERR_UNSUPPORTED),   # fp32 at cs=256
+    (dict(in_dtype=_abi.SSD_F32, chunk_size=128), _abi.SSD_ERR_UNSUPPORTED),   # fp32 at cs=128
     (dict(a_kind=_abi.SSD_A_DIAG), _abi.SSD_ERR_BAD_SHAPE),    # diag needs P == 1
     (dict(dt_min=-1.0), _abi.SSD_ERR_UNSUPPORTED),          # chunked path needs delta >= 0
 ])

@@ -22,7 +22,8 @@ def _case(seed, in_dtype, P, N, cs, lengths, nc, H=8, G=2, init="pool", slots=16
 
 
 VARIANTS = [("bf16", 64, 128, 256), ("bf16", 64, 128, 128), ("bf16", 64, 128, 64),
-            ("bf16", 16, 16, 64), ("f32", 16, 16, 64), ("f32", 64, 128, 64)]
+            ("bf16", 16, 16, 64), ("f32", 16, 16, 64), ("f32", 64, 128, 64),
+            ("bf16", 16, 16, 256), ("f32", 16, 16, 256), ("f32", 64, 128, 256)]
 
 
 @pytest.mark.parametrize("dtype,P,N,cs", VARIANTS)
