@@ -152,6 +152,19 @@ def _kernel_times(evs_per_step, n_kernels):
     return [t / len(evs_per_step) for t in tot]     # ms per launch
 
 
+def _kernel_spread(evs_per_step, n_kernels):
+    """p10 / median / p90 of each kernel's per-launch duration (ms) over the profiled
+    steps."""
+    import numpy as np
+    out = []
+    for i in range(n_kernels):
+        d = np.array([evs[i].elapsed_time(evs[i + 1]) for evs in evs_per_step])
+        out.append({"p10": round(float(np.percentile(d, 10)), 5),
+                    "median": round(float(np.median(d)), 5),
+                    "p90": round(float(np.percentile(d, 90)), 5)})
+    return out
+
+
 def _source_digest(*names):
     h = hashlib.sha256()
     for n in names:
@@ -298,6 +311,7 @@ def bench_prefill(torch, name, steps, warmup, sets=4, block_size=0, graph=False)
         torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     kt = _kernel_times(ev_sets, nk.value)
+    spread = _kernel_spread(ev_sets, nk.value)
     work = prefill_work(inp, cuc, sidx, state_writes)
     if "k_chunk_chain" in knames:
         work["k_chunk_prep"] = work.pop("k_chunk_prep/chain")
@@ -330,7 +344,8 @@ def bench_prefill(torch, name, steps, warmup, sets=4, block_size=0, graph=False)
         graph_ms = g0.elapsed_time(g1) / steps
         del graphs
     return dict(inp=inp, C=C, total_ms=total_ms, ms_per_step=total_ms / steps,
-                kernel_ms=dict(zip(knames, kt)), work=work, graph_ms=graph_ms)
+                kernel_ms=dict(zip(knames, kt)), kernel_spread=dict(zip(knames, spread)),
+                work=work, graph_ms=graph_ms)
 
 
 def prefill_report(res, name, with_counters=True):
@@ -348,7 +363,7 @@ def prefill_report(res, name, with_counters=True):
     return dict(
         tokens_per_s=tok_s,
         roofline=_roofline("hbm", gbs, HBM_PEAK_GBS, "GB/s", traffic, dom),
-        kernels={k: {"ms": round(v, 5),
+        kernels={k: {"ms": round(v, 5), "ms_spread": res["kernel_spread"][k],
                      "gb_s": round(w[k]["bytes"] / (v * 1e-3) / 1e9, 1),
                      "tflop_s": round(w[k]["flops"] / (v * 1e-3) / 1e12, 2),
                      "alg_bytes": w[k]["bytes"], "alg_flops": w[k]["flops"]}
@@ -425,7 +440,8 @@ def bench_decode(torch, steps, warmup, with_cpu=True, name="decode_spec", pool_b
                                  _counter_traffic(kname, name + ("/bf16_pool" if pool_bf16 else ""),
                                                   _source_digest("ssd_decode.hip", "ssd_device.h")),
                                  kname),
-           "kernel_ms": round(kms, 5), "alg_bytes": w["bytes"]}
+           "kernel_ms": round(kms, 5), "kernel_ms_spread": _kernel_spread(ev_sets, 1)[0],
+           "alg_bytes": w["bytes"]}
     if with_cpu:
         from oracle import scan_decode
         from selective_state_space_mamba2_amd.inputs import bf16_from_bits
