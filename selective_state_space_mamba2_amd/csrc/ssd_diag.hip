@@ -40,9 +40,9 @@ template <int LPC>
 __device__ __forceinline__ float group_sum(float v) {
   static_assert(LPC == 1 || LPC == 2 || LPC == 4, "lanes per channel within a quad");
   if constexpr (LPC >= 2)
-    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
   if constexpr (LPC >= 4)
-    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
   return v;
 }
 
