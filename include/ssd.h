@@ -218,7 +218,7 @@ typedef struct ssd_prefill_args {
    * of blocks in this mode, and the metadata carries block_idx_first_scheduled_token,
    * block_idx_last_computed_token and block_idx_last_scheduled_token).  block_size == 0
    * keeps one slot per sequence as described above.  With block_size > 0 (a multiple of
-   * chunk_size; SSD_A_SCALAR only):
+   * chunk_size; either a_kind):
    *   - state_indices is [S, idx_stride]: entry (r, b) is the pool slot of cache block b of
    *     sequence r, the block of the sequence's tokens [b*block_size, (b+1)*block_size);
    *   - the initial state (has_initial_state[r]) is read from entry

@@ -81,19 +81,18 @@ __global__ __launch_bounds__(256) void k_diag_scan(PrefillParams p) {
   float h[SPL];
 #pragma unroll
   for (int i = 0; i < SPL; ++i) h[i] = 0.f;
-  int slot = -1;
-  if (p.pool && p.state_idx) {
-    slot = p.state_idx[r];
-    if (slot < 0 || slot >= p.num_slots) {
-      if (tid == 0 && cb == 0) raise_flag(p.flag, SSD_DEVERR_SLOT_RANGE);
-      slot = -1;
-    }
-  }
+  // pool entries: the initial state (read only with has_initial_state) and the final
+  // state (written only with write_final); in the all cache mode the block_idx_last_computed
+  // and block_idx_last_scheduled entries, plus one entry per block end below
+  const bool report = tid == 0 && cb == 0;
+  const SeqSlots ss = seq_slots(p, r, true, true, report);
+  const int src = (ss.src >= 0 && p.has_init && p.has_init[r]) ? ss.src : -1;
+  const int fin = p.write_final ? ss.fin : -1;
   if (valid) {
 #pragma unroll
     for (int i = 0; i < SPL; ++i) A2[i] = p.A[c * N + ng * SPL + i] * kLog2e;
-    if (slot >= 0 && p.has_init && p.has_init[r]) {
-      const int64_t e = int64_t(slot) * p.slot_stride + int64_t(c) * N + ng * SPL;
+    if (src >= 0) {
+      const int64_t e = int64_t(src) * p.slot_stride + int64_t(c) * N + ng * SPL;
 #pragma unroll
       for (int i = 0; i < SPL; i += 4) {
         const float4_v v = pool_ld4(p.pool, p.pool_bf16, e + i);
@@ -211,6 +210,16 @@ __global__ __launch_bounds__(256) void k_diag_scan(PrefillParams p) {
 #pragma unroll
           for (int i = 0; i < SPL; ++i) dst[i] = h[i];
         }
+        if (valid && p.block_size > 0) {   // the all cache mode: a block ends here
+          const int col = block_end_col(p, r, t0, p.cu_chunk[k], next_end, report);
+          const int bslot = col >= 0 ? pool_slot(p, r, col, report) : -1;
+          if (bslot >= 0) {
+            const int64_t e = int64_t(bslot) * p.slot_stride + int64_t(c) * N + ng * SPL;
+#pragma unroll
+            for (int i = 0; i < SPL; i += 4)
+              pool_st4(p.pool, p.pool_bf16, e + i, float4_v{h[i], h[i + 1], h[i + 2], h[i + 3]});
+          }
+        }
         ++k;
         next_end = k <= klast ? p.cu_chunk[k + 1] : -1;
       } else {
@@ -230,8 +239,8 @@ __global__ __launch_bounds__(256) void k_diag_scan(PrefillParams p) {
     __syncthreads();
   }
   if (k != klast + 1 && tid == 0 && cb == 0) raise_flag(p.flag, SSD_DEVERR_CHUNK_RANGE);
-  if (valid && p.write_final && slot >= 0) {
-    const int64_t e = int64_t(slot) * p.slot_stride + int64_t(c) * N + ng * SPL;
+  if (valid && fin >= 0) {
+    const int64_t e = int64_t(fin) * p.slot_stride + int64_t(c) * N + ng * SPL;
 #pragma unroll
     for (int i = 0; i < SPL; i += 4)
       pool_st4(p.pool, p.pool_bf16, e + i, float4_v{h[i], h[i + 1], h[i + 2], h[i + 3]});

@@ -62,7 +62,6 @@ ssd_status plan_prefill(const ssd_prefill_args* a, PrefillPlan* plan) {
   // the all cache mode: one pool entry per cache block of block_size tokens
   if (a->block_size < 0) return SSD_ERR_BAD_SHAPE;
   if (a->block_size > 0) {
-    if (a->a_kind != SSD_A_SCALAR) return SSD_ERR_UNSUPPORTED;
     if (a->block_size % a->chunk_size != 0 || a->idx_stride < 1) return SSD_ERR_BAD_SHAPE;
     if (!a->state_pool || !a->state_indices || !a->num_computed) return SSD_ERR_NULL_POINTER;
     if (a->has_initial_state && !a->block_idx_last_computed) return SSD_ERR_NULL_POINTER;

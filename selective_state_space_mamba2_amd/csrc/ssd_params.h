@@ -52,6 +52,59 @@ struct PrefillParams {
   float* local_states_out;
 };
 
+// Pool entries of a sequence (the chunked kernels and the diagonal scan share these).
+// state_idx is [S, idx_stride]: one slot per sequence (idx_stride 1, column 0), or in the
+// all cache mode one entry per cache block of block_size tokens (block b: tokens
+// [b*block_size, (b+1)*block_size) of the sequence).
+
+// Slot of entry `col` of sequence r, or -1 (SSD_DEVERR_SLOT_RANGE raised if `report`)
+// when the column or the slot is out of range.
+__device__ __forceinline__ int pool_slot(const PrefillParams& p, int r, int col, bool report) {
+  int slot = -1;
+  if (col >= 0 && col < p.idx_stride) slot = p.state_idx[int64_t(r) * p.idx_stride + col];
+  if (slot < 0 || slot >= p.num_slots) {
+    if (report) raise_flag(p.flag, SSD_DEVERR_SLOT_RANGE);
+    return -1;
+  }
+  return slot;
+}
+
+// The all cache mode's entry for the state at the end of chunk [cs0, cs1) of sequence r
+// (first token t0): column e / block_size - 1 when the chunk ends at an absolute position
+// e that closes a block, else -1.  A block end strictly inside the chunk means the chunk
+// metadata was built for another num_computed: SSD_DEVERR_CHUNK_RANGE if `report`.
+__device__ __forceinline__ int block_end_col(const PrefillParams& p, int r, int t0, int cs0,
+                                             int cs1, bool report) {
+  if (p.block_size <= 0) return -1;
+  // absolute positions fit in int32 (the chunk-metadata builder rejects larger ones)
+  const int64_t a0 = int64_t(p.num_computed[r]) + (cs0 - t0), a1 = a0 + (cs1 - cs0);
+  const uint32_t bs = uint32_t(p.block_size), u0 = uint32_t(a0), u1 = uint32_t(a1);
+  if (a0 < 0 || a1 > INT32_MAX || (u1 - 1) / bs != u0 / bs) {
+    if (report) raise_flag(p.flag, SSD_DEVERR_CHUNK_RANGE);
+    return -1;
+  }
+  return u1 % bs == 0 ? int(u1 / bs) - 1 : -1;
+}
+
+// Source and final pool slots of sequence r (-1: none): the sequence's slot, or in the all
+// cache mode the entries block_idx_last_computed (read only with an initial state) and
+// block_idx_last_scheduled (written only with write_final).
+struct SeqSlots { int src, fin; };
+__device__ __forceinline__ SeqSlots seq_slots(const PrefillParams& p, int r, bool need_src,
+                                              bool need_fin, bool report) {
+  SeqSlots s{-1, -1};
+  if (!p.pool || !p.state_idx || !(need_src || need_fin)) return s;
+  if (p.block_size <= 0) {
+    const int slot = pool_slot(p, r, 0, report);
+    s.src = need_src ? slot : -1;
+    s.fin = need_fin ? slot : -1;
+    return s;
+  }
+  if (need_src && p.has_init && p.has_init[r]) s.src = pool_slot(p, r, p.blk_last_comp[r], report);
+  if (need_fin && p.write_final) s.fin = pool_slot(p, r, p.blk_last_sched[r], report);
+  return s;
+}
+
 struct DecodeParams {
   int B_pad, ntok, H, P, G, N;
   int diag;            // SSD_A_DIAG: A is [H, N] (Mamba1, P == 1, G == 1)

@@ -153,10 +153,13 @@ def test_prefill_all_cache_mode_host_checks(over, status):
     assert _ws(_good_prefill(**{**_ALL_MODE, **over}))[0] == status
 
 
-def test_prefill_all_cache_mode_is_scalar_a_only():
+def test_prefill_all_cache_mode_with_diagonal_a():
+    """The Mamba1 scan takes the all cache mode too; it resolves block entries itself, so it
+    needs no workspace."""
     diag = dict(a_kind=_abi.SSD_A_DIAG, H=64, P=1, G=1, N=16, x_stride_t=64, y_stride_t=64,
                 dt_stride_t=64, bc_stride_t=16, chunk_size=256, slot_stride=64 * 16)
-    assert _ws(_good_prefill(**{**_ALL_MODE, **diag}))[0] == _abi.SSD_ERR_UNSUPPORTED
+    assert _ws(_good_prefill(**{**_ALL_MODE, **diag})) == (_abi.SSD_OK, 0)
+    assert _ws(_good_prefill(**{**_ALL_MODE, **diag, "block_size": 384}))[0] == _abi.SSD_ERR_BAD_SHAPE
 
 
 def test_kernel_count():

@@ -37,11 +37,11 @@ def _columns(nc, lengths, bs):
     return lc, ls
 
 
-def _case(seed, dtype, P, N, cs, bs, lengths, nc, H=4, G=2, max_blocks=4):
+def _case(seed, dtype, P, N, cs, bs, lengths, nc, H=4, G=2, max_blocks=4, a_kind="scalar"):
     S = len(lengths)
     inp = make_prefill(seed, in_dtype=dtype, H=H, P=P, G=G, N=N, chunk_size=cs,
                        lengths=lengths, num_computed=nc, init="pool",
-                       pool_slots=S * max_blocks + 1)
+                       pool_slots=S * max_blocks + 1, a_kind=a_kind)
     table = _block_table(seed + 1, S, max_blocks, inp.pool.shape[0])
     lc, ls = _columns(nc, lengths, bs)
     assert ls.max() < max_blocks
@@ -132,6 +132,33 @@ def test_prefill_writes_every_block_entry(dtype, P, N, cs, bs, write_final):
     got = _run(inp, table, bs, lc, ls, write_final=write_final)
     refs, writes = _expected(inp, table, bs, lc, ls, write_final)
     _check(inp, got, refs, writes, TOL[dtype])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("write_final", [True, False])
+def test_prefill_diag_writes_every_block_entry(dtype, write_final):
+    """The Mamba1 scan (diagonal A [200, 16]; 200 channels leave a ragged last workgroup) in
+    the all cache mode: y, the chunk states, every block-end entry and the final entry."""
+    cs, bs = 64, 128
+    lengths, nc = _lengths(cs, bs)
+    inp, table, lc, ls = _case(55, dtype, 1, 16, cs, bs, lengths, nc, H=200, G=1,
+                               a_kind="diag")
+    got = _run(inp, table, bs, lc, ls, write_final=write_final)
+    refs, writes = _expected(inp, table, bs, lc, ls, write_final)
+    assert any(len(o["block_states"]) for o in refs.values())
+    _check(inp, got, refs, writes, TOL[dtype])
+
+
+def test_prefill_diag_bf16_pool():
+    """The same through a bf16 pool (entries at the bf16 tolerance)."""
+    cs, bs = 64, 192
+    lengths, nc = _lengths(cs, bs)
+    inp, table, lc, ls = _case(56, "bf16", 1, 16, cs, bs, lengths, nc, H=72, G=1,
+                               a_kind="diag")
+    inp.pool = torch().from_numpy(inp.pool).to(torch().bfloat16).float().numpy()
+    got = _run(inp, table, bs, lc, ls, pool_bf16=True)
+    refs, writes = _expected(inp, table, bs, lc, ls)
+    _check(inp, got, refs, writes, TOL["bf16"])
 
 
 @pytest.mark.parametrize("dtype,P,N,cs,bs", [SHAPES[0], SHAPES[2]])
