@@ -109,8 +109,8 @@ const char* ssd_status_string(ssd_status status); /* static string, never NULL *
  *
  * Errors: SSD_ERR_NULL_POINTER, SSD_ERR_BAD_SHAPE (S < 0, chunk_size <= 0),
  * SSD_ERR_BAD_METADATA (cu_seqlens[0] != 0, a sequence with < 1 token, num_computed < 0,
- * an int32 overflow), SSD_ERR_CAPACITY (C > capacity; nothing but *num_chunks_out is
- * written).
+ * num_computed + new tokens beyond INT32_MAX, an int32 overflow), SSD_ERR_CAPACITY
+ * (C > capacity; nothing but *num_chunks_out is written).
  * ------------------------------------------------------------------------------------- */
 ssd_status ssd_chunk_metadata_count(int32_t num_seqs, const int32_t* cu_seqlens,
                                     const int32_t* num_computed, int32_t chunk_size,

@@ -191,6 +191,9 @@ static ssd_status chunk_walk(int32_t S, const int32_t* cu, const int32_t* nc, in
     const int64_t new_tokens = int64_t(cu[r + 1]) - cu[r];
     const int64_t done = nc ? nc[r] : 0;
     if (new_tokens < 1 || done < 0) return SSD_ERR_BAD_METADATA;
+    // a sequence's absolute positions (num_computed + new tokens) must fit in int32: the
+    // kernels place block and chunk ends with 32-bit positions
+    if (done + new_tokens > std::numeric_limits<int32_t>::max()) return SSD_ERR_BAD_METADATA;
     int64_t left = new_tokens;
     if (done % cs != 0) {
       const int64_t open = cs - done % cs;

@@ -73,6 +73,10 @@ def test_errors():
     with pytest.raises(SSDError) as e:
         api.ssd_build_chunk_metadata([0, 4], None, 0)
     assert e.value.status == SSD_ERR_BAD_SHAPE
+    with pytest.raises(SSDError) as e:                        # absolute positions past int32
+        api.ssd_build_chunk_metadata([0, 20], [2**31 - 10], 64)
+    assert e.value.status == SSD_ERR_BAD_METADATA
+    assert len(api.ssd_build_chunk_metadata([0, 10], [2**31 - 11], 64)[1]) == 1
     # capacity too small: the status says so and reports the count
     import ctypes
     cu = np.array([0, 10], dtype=np.int32)
