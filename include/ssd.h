@@ -27,6 +27,11 @@
  *     a nonzero SSD_DEVERR_* bit mask (the flag is only ever OR-ed, never cleared).
  *   - No global mutable state: calls on different streams may run concurrently as long
  *     as they do not write the same memory.
+ *   - The pool is updated in place: two sequences of one prefill, or two live rows of one
+ *     decode, must not touch the same pool slot (a race otherwise).  With the environment
+ *     variable SSD_DEBUG set (to anything but "0") each call first launches a check kernel
+ *     that raises SSD_DEVERR_DUPLICATE_SLOT when they do (O(n^2) in the entries touched;
+ *     not counted by ssd_prefill_kernel_count, not timed by profile_events).
  */
 #ifndef SSD_MI355X_H
 #define SSD_MI355X_H
@@ -63,6 +68,10 @@ typedef enum ssd_status {
                                       state was left in the L2 of another XCD than the one
                                       workgroup dispatch placed the chunk on; the outputs
                                       of that sequence are invalid                       */
+#define SSD_DEVERR_DUPLICATE_SLOT 16 /* two sequences (prefill) or two decode rows touch
+                                      the same pool slot; only checked when the
+                                      environment variable SSD_DEBUG is set (not "0"),
+                                      by an extra kernel each call launches first        */
 
 typedef enum ssd_dtype { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
 

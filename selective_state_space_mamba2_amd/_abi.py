@@ -24,6 +24,7 @@ SSD_DEVERR_CHUNK_RANGE = 1
 SSD_DEVERR_SLOT_RANGE = 2
 SSD_DEVERR_ACCEPTED = 4
 SSD_DEVERR_CHAIN_WAIT = 8
+SSD_DEVERR_DUPLICATE_SLOT = 16
 
 SSD_F32 = 0
 SSD_BF16 = 1

@@ -93,6 +93,8 @@ ssd_status ssd_prefill(const ssd_prefill_args* a, void* workspace, size_t worksp
   }
 
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (ssd::debug_checks_enabled() && ssd::launch_prefill_slot_check(p, s) != hipSuccess)
+    return SSD_ERR_HIP;
   const hipError_t e = plan.kind == ssd::PrefillKind::kChunked
                            ? ssd::launch_chunked_prefill(plan.variant, p, s, a->profile_events)
                            : ssd::launch_diag_prefill(a->in_dtype, p, s, a->profile_events);
@@ -139,6 +141,9 @@ ssd_status ssd_state_update(const ssd_decode_args* a, ssd_stream_t stream) {
   p.null_id = a->null_block_id; p.flag = a->device_error_flag;
   p.idx_stride = a->idx_stride;
   p.blk_last_comp = a->block_idx_last_computed; p.blk_last_sched = a->block_idx_last_scheduled;
+  if (ssd::debug_checks_enabled() &&
+      ssd::launch_decode_slot_check(p, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return SSD_ERR_HIP;
   const hipError_t e = ssd::launch_state_update(a->in_dtype, p, static_cast<hipStream_t>(stream),
                                                 a->profile_events);
   return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;

@@ -136,6 +136,11 @@ hipError_t launch_diag_prefill(int in_dtype, const PrefillParams& p, hipStream_t
 hipError_t launch_state_update(int in_dtype, const DecodeParams& p, hipStream_t s,
                                void* const* events);
 
+// SSD_DEBUG: the distinct-slot checks (ssd_debug.hip), launched before a call's kernels.
+bool debug_checks_enabled();
+hipError_t launch_prefill_slot_check(const PrefillParams& p, hipStream_t s);
+hipError_t launch_decode_slot_check(const DecodeParams& p, hipStream_t s);
+
 inline void record_event(void* const* events, int i, hipStream_t s) {
   if (events && events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
 }
