@@ -749,53 +749,55 @@ def main():
         line["cpu_baseline"] = cpu_baseline_prefill(inp)
     del res
     if not args.primary_only:
-        _log("decode_spec")
-        line["decode"] = bench_decode(torch, args.steps, args.warmup,
-                                      with_cpu=not args.no_cpu_baseline)
-        torch.cuda.empty_cache()
-        _log("nemotron_h_prefix_cache")
-        res2 = bench_prefill(torch, "nemotron_h_prefix_cache", args.steps, args.warmup)
-        rep2 = prefill_report(res2, "nemotron_h_prefix_cache")
-        line["prefill_nemotron"] = {
-            "workload": "nemotron_h_prefix_cache", "value": round(rep2["tokens_per_s"], 1),
-            "unit": "tokens/s", "tokens": res2["inp"].T, "chunks": res2["C"],
-            "ms_per_step": round(res2["ms_per_step"], 5), "roofline": rep2["roofline"],
-            "kernels": rep2["kernels"], "path": rep2["path"]}
-        del res2
-        torch.cuda.empty_cache()
-        _log("nemotron_h_prefix_cache, all cache mode")
-        res3 = bench_prefill(torch, "nemotron_h_prefix_cache", args.steps, args.warmup,
-                             block_size=256)
-        rep3 = prefill_report(res3, "nemotron_h_prefix_cache/all")
-        line["prefill_nemotron_all_mode"] = {
-            "workload": "nemotron_h_prefix_cache, all cache mode (block_size 256, one pool "
-                        "entry per block, no chunk-state output)",
-            "value": round(rep3["tokens_per_s"], 1), "unit": "tokens/s",
-            "ms_per_step": round(res3["ms_per_step"], 5), "roofline": rep3["roofline"],
-            "kernels": rep3["kernels"], "path": rep3["path"]}
-        del res3
-        torch.cuda.empty_cache()
-        _log("mamba1_long_diag")
-        line["diag"] = bench_diag(torch, max(3, args.steps // 5), max(1, args.warmup // 5))
-        torch.cuda.empty_cache()
-        _log("mamba1_decode_spec")
-        line["decode_mamba1"] = bench_decode(torch, args.steps, args.warmup,
-                                             with_cpu=not args.no_cpu_baseline,
-                                             name="mamba1_decode_spec")
-        torch.cuda.empty_cache()
-        _log("decode_spec, bf16 state pool")
-        line["decode_bf16_pool"] = bench_decode(torch, args.steps, args.warmup, with_cpu=False,
-                                                pool_bf16=True)
-        torch.cuda.empty_cache()
-        _log("conv1d prefill")
-        line["conv1d_prefill"] = bench_conv_prefill(torch, args.steps, args.warmup)
-        torch.cuda.empty_cache()
-        _log("conv1d update")
-        line["conv1d_update"] = bench_conv_update(torch, args.steps, args.warmup)
+        def nemotron(block_size=0):
+            key = "nemotron_h_prefix_cache" + ("/all" if block_size else "")
+            res = bench_prefill(torch, "nemotron_h_prefix_cache", args.steps, args.warmup,
+                                block_size=block_size)
+            rep = prefill_report(res, key)
+            return {"workload": "nemotron_h_prefix_cache" + (
+                        ", all cache mode (block_size 256, one pool entry per block, no "
+                        "chunk-state output)" if block_size else ""),
+                    "value": round(rep["tokens_per_s"], 1), "unit": "tokens/s",
+                    "tokens": res["inp"].T, "chunks": res["C"],
+                    "ms_per_step": round(res["ms_per_step"], 5), "roofline": rep["roofline"],
+                    "kernels": rep["kernels"], "path": rep["path"]}
+
+        cpu = not args.no_cpu_baseline
+        legs = [
+            ("decode", "decode_spec",
+             lambda: bench_decode(torch, args.steps, args.warmup, with_cpu=cpu)),
+            ("prefill_nemotron", "nemotron_h_prefix_cache", lambda: nemotron()),
+            ("prefill_nemotron_all_mode", "nemotron_h_prefix_cache, all cache mode",
+             lambda: nemotron(block_size=256)),
+            ("diag", "mamba1_long_diag",
+             lambda: bench_diag(torch, max(3, args.steps // 5), max(1, args.warmup // 5))),
+            ("decode_mamba1", "mamba1_decode_spec",
+             lambda: bench_decode(torch, args.steps, args.warmup, with_cpu=cpu,
+                                  name="mamba1_decode_spec")),
+            ("decode_bf16_pool", "decode_spec, bf16 state pool",
+             lambda: bench_decode(torch, args.steps, args.warmup, with_cpu=False,
+                                  pool_bf16=True)),
+            ("conv1d_prefill", "conv1d prefill",
+             lambda: bench_conv_prefill(torch, args.steps, args.warmup)),
+            ("conv1d_update", "conv1d update",
+             lambda: bench_conv_update(torch, args.steps, args.warmup)),
+        ]
+        # a secondary measurement that fails (an exception, not a device fault) is recorded
+        # as such and does not cost the line the others
+        for key, what, fn in legs:
+            _log(what)
+            try:
+                line[key] = fn()
+            except Exception as e:   # noqa: BLE001
+                line[key] = {"workload": what, "error": f"{type(e).__name__}: {e}"}
+            torch.cuda.empty_cache()
         _log("measured peaks")
-        peaks = measured_peaks(torch)
-        line["measured_peaks"] = peaks
-        _add_measured_frac(line, peaks)
+        try:
+            peaks = measured_peaks(torch)
+            line["measured_peaks"] = peaks
+            _add_measured_frac(line, peaks)
+        except Exception as e:   # noqa: BLE001
+            line["measured_peaks"] = {"error": f"{type(e).__name__}: {e}"}
     print(json.dumps(line), flush=True)
 
 
