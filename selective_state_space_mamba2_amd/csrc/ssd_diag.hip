@@ -13,6 +13,7 @@
 // bf16), delta is prepared once per (token, channel) while staging, and y leaves through
 // an LDS tile as coalesced rows.  Checkpoints are written at the chunk ends listed by the
 // chunk metadata.
+#include <cstdint>
 #include <type_traits>
 
 #include "ssd_params.h"
@@ -54,9 +55,9 @@ __global__ __launch_bounds__(256) void k_diag_scan(PrefillParams p) {
   constexpr int TT = 32;       // tokens per LDS tile
   constexpr int U = SSD_DIAG_UNROLL;   // tokens per step of the scan (divides TT)
   static_assert(TT % U == 0, "unroll");
-  __shared__ float s_d[TT][CH];
-  __shared__ float s_x[TT][CH];
-  __shared__ float s_y[TT][CH];
+  __shared__ __attribute__((aligned(16))) float s_d[TT][CH];
+  __shared__ __attribute__((aligned(16))) float s_x[TT][CH];
+  __shared__ __attribute__((aligned(16))) float s_y[TT][CH];
   __shared__ __attribute__((aligned(16))) float s_b[TT][N];
   __shared__ __attribute__((aligned(16))) float s_c[TT][N];
 
@@ -117,16 +118,34 @@ __global__ __launch_bounds__(256) void k_diag_scan(PrefillParams p) {
   constexpr int NBC = TT * 2 * (N / 4);          // B / C float4 items per tile
   T rd[NE], rx[NE];
   float4_v rbc;
+  // Vector path (bf16, 8 channels per thread): thread t owns channels 8*(t % 8) .. +7 of
+  // tile row t / 8, moved as one 16-byte access per tensor; it needs whole 8-channel
+  // groups (H % 8 == 0) and 16-byte aligned rows.  Otherwise one element per access.
+  constexpr bool kVecT = std::is_same<T, bf16_t>::value && NE == 8 && CH == 64;
+  const bool vec = kVecT && H % 8 == 0 && p.x_st % 8 == 0 && p.dt_st % 8 == 0 &&
+                   p.y_st % 8 == 0 &&
+                   ((reinterpret_cast<uintptr_t>(p.x) | reinterpret_cast<uintptr_t>(p.dt) |
+                     reinterpret_cast<uintptr_t>(p.y)) & 15) == 0;
+  const int vtt = tid / 8, vc8 = (tid % 8) * 8, vch = cb * CH + vc8;
+  u32x4_v vd = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
   auto fetch = [&](int tb) {
     const int nt = min(TT, t1 - tb);
+    if (vec) {
+      const bool in = vtt < nt && vch < H;
+      vd = in ? *reinterpret_cast<const u32x4_v*>(dg + int64_t(tb + vtt) * p.dt_st + vch)
+              : u32x4_v{0u, 0u, 0u, 0u};
+      vx = in ? *reinterpret_cast<const u32x4_v*>(xg + int64_t(tb + vtt) * p.x_st + vch)
+              : u32x4_v{0u, 0u, 0u, 0u};
+    } else {
 #pragma unroll
-    for (int u = 0; u < NE; ++u) {
-      const int e = u * 256 + tid, tt = e / CH, ch = cb * CH + e % CH;
-      const bool in = tt < nt && ch < H;
-      const int64_t t = in ? tb + tt : t0;
-      const int chc = in ? ch : 0;
-      rd[u] = in ? dg[t * p.dt_st + chc] : T(0);
-      rx[u] = in ? xg[t * p.x_st + chc] : T(0);
+      for (int u = 0; u < NE; ++u) {
+        const int e = u * 256 + tid, tt = e / CH, ch = cb * CH + e % CH;
+        const bool in = tt < nt && ch < H;
+        const int64_t t = in ? tb + tt : t0;
+        const int chc = in ? ch : 0;
+        rd[u] = in ? dg[t * p.dt_st + chc] : T(0);
+        rx[u] = in ? xg[t * p.x_st + chc] : T(0);
+      }
     }
     rbc = float4_v{0.f, 0.f, 0.f, 0.f};
     if (tid < NBC) {
@@ -142,12 +161,28 @@ __global__ __launch_bounds__(256) void k_diag_scan(PrefillParams p) {
   fetch(t0);
   for (int tb = t0; tb < t1; tb += TT) {
     const int nt = min(TT, t1 - tb);
+    if (vec) {
+      const bool in = vtt < nt && vch < H;
+      float dv8[8], xv8[8];
 #pragma unroll
-    for (int u = 0; u < NE; ++u) {
-      const int e = u * 256 + tid, tt = e / CH, cc = e % CH, ch = cb * CH + cc;
-      const bool in = tt < nt && ch < H;
-      s_d[tt][cc] = in ? p.prep(to_f32(rd[u]), ch) : 0.f;
-      s_x[tt][cc] = to_f32(rx[u]);
+      for (int k = 0; k < 4; ++k) {
+        xv8[2 * k] = __uint_as_float(vx[k] << 16);
+        xv8[2 * k + 1] = __uint_as_float(vx[k] & 0xffff0000u);
+        dv8[2 * k] = in ? p.prep(__uint_as_float(vd[k] << 16), vch + 2 * k) : 0.f;
+        dv8[2 * k + 1] = in ? p.prep(__uint_as_float(vd[k] & 0xffff0000u), vch + 2 * k + 1) : 0.f;
+      }
+      *reinterpret_cast<float4_v*>(&s_d[vtt][vc8]) = float4_v{dv8[0], dv8[1], dv8[2], dv8[3]};
+      *reinterpret_cast<float4_v*>(&s_d[vtt][vc8 + 4]) = float4_v{dv8[4], dv8[5], dv8[6], dv8[7]};
+      *reinterpret_cast<float4_v*>(&s_x[vtt][vc8]) = float4_v{xv8[0], xv8[1], xv8[2], xv8[3]};
+      *reinterpret_cast<float4_v*>(&s_x[vtt][vc8 + 4]) = float4_v{xv8[4], xv8[5], xv8[6], xv8[7]};
+    } else {
+#pragma unroll
+      for (int u = 0; u < NE; ++u) {
+        const int e = u * 256 + tid, tt = e / CH, cc = e % CH, ch = cb * CH + cc;
+        const bool in = tt < nt && ch < H;
+        s_d[tt][cc] = in ? p.prep(to_f32(rd[u]), ch) : 0.f;
+        s_x[tt][cc] = to_f32(rx[u]);
+      }
     }
     if (tid < NBC) {
       const int tt = tid / (2 * (N / 4)), q = tid % (2 * (N / 4));
@@ -232,9 +267,19 @@ __global__ __launch_bounds__(256) void k_diag_scan(PrefillParams p) {
       }
     }
     __syncthreads();
-    for (int e = tid; e < nt * CH; e += 256) {
-      const int tt = e / CH, cc = e % CH, ch = cb * CH + cc;
-      if (ch < H) Elem<T>::store(yg + int64_t(tb + tt) * p.y_st + ch, s_y[tt][cc]);
+    if (vec) {
+      if (vtt < nt && vch < H) {
+        const float4_v a = *reinterpret_cast<const float4_v*>(&s_y[vtt][vc8]);
+        const float4_v b = *reinterpret_cast<const float4_v*>(&s_y[vtt][vc8 + 4]);
+        *reinterpret_cast<u32x4_v*>(yg + int64_t(tb + vtt) * p.y_st + vch) =
+            u32x4_v{pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y),
+                    pack_bf16x2(b.z, b.w)};
+      }
+    } else {
+      for (int e = tid; e < nt * CH; e += 256) {
+        const int tt = e / CH, cc = e % CH, ch = cb * CH + cc;
+        if (ch < H) Elem<T>::store(yg + int64_t(tb + tt) * p.y_st + ch, s_y[tt][cc]);
+      }
     }
     __syncthreads();
   }

@@ -41,6 +41,19 @@ def test_diag_bf16_state_pool(dtype):
             np.testing.assert_array_equal(got["pool"][s], inp.pool[s])
 
 
+@pytest.mark.parametrize("H", [100, 36])
+def test_diag_bf16_element_path(H):
+    """bf16 inputs the 16-byte tile path cannot take (channel counts that are not whole
+    8-channel groups, so the token strides are not multiples of 8 either): one element per
+    access, the same results."""
+    inp = make_prefill(44, in_dtype="bf16", H=H, P=1, G=1, N=16, chunk_size=64,
+                       lengths=[150, 77], num_computed=[0, 9], a_kind="diag",
+                       init="pool", pool_slots=4)
+    got = run_prefill(inp)
+    assert got["flag"] == 0
+    check_prefill(inp, got, oracle_prefill(inp))
+
+
 def test_diag_several_checkpoints_per_token_tile():
     """chunk_size 24 with unaligned resume points: several chunk ends fall inside one
     32-token tile of the scan, so groups of tokens restart at unaligned positions."""
