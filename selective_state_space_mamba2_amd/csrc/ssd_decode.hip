@@ -279,8 +279,9 @@ __global__ __launch_bounds__(256) void k_state_update_diag(DecodeParams p) {
     h.z = __builtin_amdgcn_exp2f(delta * A2[2]) * h.z + dx * bv.z;
     h.w = __builtin_amdgcn_exp2f(delta * A2[3]) * h.w + dx * bv.w;
     float acc = cv.x * h.x + cv.y * h.y + cv.z * h.z + cv.w * h.w;
-    acc += __shfl_xor(acc, 1, 64);
-    acc += __shfl_xor(acc, 2, 64);
+    // the channel's four lanes are one quad, all active: DPP quad permutations feed the adds
+    acc += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, acc), 0xB1, 0xF, 0xF, true));
+    acc += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, acc), 0x4E, 0xF, 0xF, true));
     if (q == 0) Elem<T>::store(yg + tj, acc + Dc * xv);
     PoolIO<S>::st4_nt(p.pool, int64_t(row.dst(j)) * p.slot_stride + int64_t(c) * N + SPL * q, h);
   }
