@@ -169,6 +169,10 @@ def test_full_mamba1_decode_workload():
 
 @pytest.mark.parametrize("dtype,P,N,G,ntok,a_kind", [("bf16", 64, 128, 2, 4, "scalar"),
                                                      ("f32", 32, 64, 1, 3, "scalar"),
+                                                     # the bf16 pool's halving y reduction
+                                                     # with 2 and 8 rows per lane
+                                                     ("f32", 64, 64, 2, 3, "scalar"),
+                                                     ("bf16", 64, 256, 1, 2, "scalar"),
                                                      ("bf16", 1, 16, 1, 4, "diag"),
                                                      ("f32", 1, 16, 1, 2, "diag")])
 def test_bf16_state_pool(dtype, P, N, G, ntok, a_kind):
