@@ -54,6 +54,17 @@ def test_diag_bf16_element_path(H):
     check_prefill(inp, got, oracle_prefill(inp))
 
 
+def test_diag_bf16_tile_path_with_projection_views():
+    """x, B and C as views into one projection buffer (token strides 112, dt and y strides
+    72, all multiples of 8): the 16-byte tile path with strides other than the width."""
+    inp = make_prefill(45, in_dtype="bf16", H=64, P=1, G=1, N=16, chunk_size=64,
+                       lengths=[150, 77], num_computed=[0, 9], a_kind="diag",
+                       init="pool", pool_slots=4)
+    got = run_prefill(inp, views=True)
+    assert got["flag"] == 0
+    check_prefill(inp, got, oracle_prefill(inp))
+
+
 def test_diag_several_checkpoints_per_token_tile():
     """chunk_size 24 with unaligned resume points: several chunk ends fall inside one
     32-token tile of the scan, so groups of tokens restart at unaligned positions."""
