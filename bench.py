@@ -3,29 +3,38 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--primary-only]
 
-One step is one pass of the prefill path over the Mamba2-2.7B-like layer batch (4 packed
-sequences x 2048 tokens, 80 heads, head_dim 64, dstate 128, chunk 256, bf16 in / fp32
-state, the state written at every chunk end): chunk metadata on the host, its copy to the
-device, and the two prefill kernels.  Inputs are resident in HBM before timing starts;
-four input/output buffer sets rotate so the 256 MB Infinity Cache cannot hold a step's
-working set.  The line printed also carries the decode state update (256 live requests of
-a 512-row padded batch, 1+3 tokens, [2048,48,64,128] fp32 pool), the Nemotron-H-like
-varlen prefill with prefix caching (also in the all cache mode), the Mamba1 long-context
-diagonal scan and decode, the decode with a bf16 state pool, and the causal conv1d prefill
-and decode update as secondary objects.
+One step is one pass of the prefill path over the Nemotron-H-like per-layer shard with
+prefix caching (16 varlen sequences of 512..8192 new tokens resuming at unaligned points,
+48 heads, head_dim 64, 4 groups, dstate 128, chunk 256, bf16 in / fp32 state, initial
+states gathered from a 1024-slot pool, the state written at every chunk end and the final
+state back to the pool): chunk metadata on the host, its copy to the device, and the two
+prefill kernels.  It is the largest single-GPU SSD prefill workload, so it carries the
+headline value.  Inputs are resident in HBM before timing starts; four input/output buffer
+sets rotate so the 256 MB Infinity Cache cannot hold a step's working set.  The line also
+carries, each with its own roofline and oracle baseline, the Mamba2-2.7B-like layer
+prefill (4 x 2048 tokens, 80 heads), the tiny fp32 prefill, the decode state update (256
+live requests of a 512-row padded batch, 1+3 tokens, [2048,48,64,128] fp32 pool) and the
+Mamba1 long-context diagonal scan, and as further objects the prefix-cache prefill in the
+all cache mode, the Mamba1 decode, the decode with a bf16 state pool and the causal conv1d
+prefill and decode update.
 
 Roofline: each kernel's duration comes from HIP events the library records around its
 own launches on the launch stream (the C ABI's timing hook), averaged over the timed
 steps; achieved = the kernel's algorithmic bytes (or flops) per launch / that duration.
+Every timed leg passes a device error flag and checks it is still zero after its timed
+loop (outside the timed region).
 """
-from __future__ import annotations
+import os
+
+# The oracle baseline runs single-threaded: set before numpy (or torch) is imported.
+for _v in ("OMP_NUM_THREADS", "MKL_NUM_THREADS", "OPENBLAS_NUM_THREADS"):
+    os.environ[_v] = "1"
 
 import argparse
 import gc
 import hashlib
 import json
 import math
-import os
 import sys
 import time
 
@@ -48,37 +57,42 @@ def _log(msg):
 # ----------------------------------------------------------------------------------------
 # algorithmic work (bytes and flops a kernel must move / do; redundant work not counted)
 # ----------------------------------------------------------------------------------------
+def _rw(read, write, flops=0):
+    """Algorithmic bytes of a kernel, split into reads and writes."""
+    return dict(bytes=read + write, read=read, write=write, flops=flops)
+
+
 def prefill_work(inp, cuc, sidx, state_writes=None):
-    """Algorithmic bytes and flops per kernel.  ``state_writes``: fp32 states written per
-    call (default: one per chunk plus the final states; the all cache mode passes its
-    block-end entries plus the final states)."""
+    """Algorithmic bytes (read / written) and flops per kernel.  ``state_writes``: fp32
+    states written per call (default: one per chunk plus the final states; the all cache
+    mode passes its block-end entries plus the final states)."""
     b = 2 if inp.in_dtype == "bf16" else 4
     T, H, P, G, N = inp.T, inp.H, inp.P, inp.G, inp.N
     S, C = inp.num_seqs, len(sidx)
     st = H * P * N * 4
     n_init = 0 if inp.has_initial_state is None else int(inp.has_initial_state.sum())
     n_final = 0 if inp.pool is None else S
-    n_states = n_init + (C + n_final if state_writes is None else state_writes)
+    n_out = C + n_final if state_writes is None else state_writes
     lens = [int(cuc[k + 1] - cuc[k]) for k in range(C)]
     cs = inp.chunk_size
     nfrag = sum(i // 2 + 1 for i in range(cs // 16))
     frags = C * G * (nfrag * 512 + 2 * N * cs) * b
     flops_y = sum(H * (4 * l * P * N + P * l * (l + 1)) for l in lens)
     flops_cb = sum(G * N * l * (l + 1) for l in lens)
-    io = T * 2 * H * P * b + n_states * st                   # x in, y out, states
+    x_b = T * H * P * b                                       # x in (and y out)
     dc = C * H * 2 * cs * 4                                   # cumsum + delta (fp32)
     # march path: the prep kernel reads dt, B and C and writes the cumsum, delta and the
     # C.B^T / B^T / C fragments; the march kernel reads x, C, the cumsum and the initial
     # states and writes y and the states (fragments come through L2)
-    k_prep = dict(bytes=T * H * b + dc + 2 * T * G * N * b + frags, flops=flops_cb)
-    k_march = dict(bytes=io + T * G * N * b + dc, flops=flops_y)
+    k_prep = _rw(T * H * b + 2 * T * G * N * b, dc + frags, flops_cb)
+    k_march = _rw(x_b + T * G * N * b + dc + n_init * st, x_b + n_out * st, flops_y)
     # chain path: the prep kernel only builds the fragments; the chain kernel reads dt
     # itself (a chain also reads back its predecessor's state, through L2 or HBM: not
     # counted, it is not algorithmic)
-    k_prep_chain = dict(bytes=2 * T * G * N * b + frags, flops=flops_cb)
-    k_chain = dict(bytes=io + T * G * N * b + T * H * b, flops=flops_y)
-    path = dict(bytes=T * (2 * H * P * b + H * b + 2 * G * N * b) + n_states * st,
-                flops=flops_y + flops_cb)
+    k_prep_chain = _rw(2 * T * G * N * b, frags, flops_cb)
+    k_chain = _rw(x_b + T * G * N * b + T * H * b + n_init * st, x_b + n_out * st, flops_y)
+    path = _rw(T * (H * P * b + H * b + 2 * G * N * b) + n_init * st, x_b + n_out * st,
+               flops_y + flops_cb)
     return {"k_chunk_prep": k_prep, "k_chunk_march": k_march, "k_chunk_chain": k_chain,
             "k_chunk_prep/chain": k_prep_chain, "path": path}
 
@@ -86,14 +100,19 @@ def prefill_work(inp, cuc, sidx, state_writes=None):
 def decode_work(inp, state_bytes=4):
     b = 2 if inp.in_dtype == "bf16" else 4
     st = inp.H * inp.P * inp.N * state_bytes
-    tok = inp.ntok * (2 * inp.H * inp.P * b + inp.H * b + 2 * inp.G * inp.N * b)
-    return dict(bytes=inp.n_live * ((1 + inp.ntok) * st + tok), updates=inp.n_live * inp.ntok)
+    tok_in = inp.ntok * (inp.H * inp.P * b + inp.H * b + 2 * inp.G * inp.N * b)
+    tok_out = inp.ntok * inp.H * inp.P * b
+    w = _rw(inp.n_live * (st + tok_in), inp.n_live * (inp.ntok * st + tok_out))
+    w["updates"] = inp.n_live * inp.ntok
+    return w
 
 
 def diag_work(inp, C):
     b = 2 if inp.in_dtype == "bf16" else 4
     T, H, N = inp.T, inp.H, inp.N
-    return dict(bytes=T * (3 * H * b + 2 * N * b) + C * H * N * 4, steps=T * H * N)
+    w = _rw(T * (2 * H * b + 2 * N * b), T * H * b + C * H * N * 4)
+    w["steps"] = T * H * N
+    return w
 
 
 # ----------------------------------------------------------------------------------------
@@ -119,6 +138,21 @@ class _quiet_gc:
     def __exit__(self, *exc):
         gc.enable()
         return False
+
+
+def _error_flag(torch):
+    """A zeroed device error word for one timed leg."""
+    return torch.zeros(1, dtype=torch.int32, device="cuda")
+
+
+def _assert_no_device_error(flag, what):
+    """After a leg's timed loop (outside the timed region): the kernels raised no device
+    error (bad metadata, an index out of range, a chain hand-off that gave up waiting)."""
+    from selective_state_space_mamba2_amd.api import device_error_names
+    bits = int(flag.item())
+    if bits:
+        raise RuntimeError(f"{what}: device error bits 0x{bits:x} "
+                           f"({', '.join(device_error_names(bits))}) during the timed loop")
 
 
 def _events(torch, n):
@@ -189,11 +223,22 @@ def _counter_traffic(kernel, workload, digest):
     return rec.get("bytes_per_launch")
 
 
-def _roofline(bound, achieved, peak, unit, traffic=None, kernel=None):
+TRAFFIC_SOURCE = ("stored record (profiles/counters.json): rocprofv3 FETCH_SIZE and WRITE_SIZE "
+                  "of this kernel on this workload, scaled by a copy-kernel calibration, keyed "
+                  "by a digest of the kernel sources (null once they changed)")
+
+
+def _roofline(bound, achieved, peak, unit, traffic=None, kernel=None, work=None):
     r = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
          "frac": round(achieved / peak, 4), "traffic": traffic}
     if kernel:
         r["kernel"] = kernel
+    if bound == "hbm":
+        r["traffic_source"] = TRAFFIC_SOURCE
+        if work is not None:
+            # the share of the algorithmic bytes that are reads (the measured-peak probe
+            # runs at the same mix)
+            r["read_frac"] = round(work["read"] / work["bytes"], 3)
     return r
 
 
@@ -256,6 +301,7 @@ def bench_prefill(torch, name, steps, warmup, sets=4, block_size=0, graph=False)
                      block_idx_last_scheduled=torch.from_numpy(ls).cuda())
         sidx_d = torch.from_numpy(table).cuda()
         state_writes = n_blk + S
+    flag = _error_flag(torch)
     bufs = []
     for i in range(sets):
         d = {n: (t if i == 0 else t.clone()) for n, t in base.items()}
@@ -274,7 +320,8 @@ def bench_prefill(torch, name, steps, warmup, sets=4, block_size=0, graph=False)
                              d["cu_chunk"], d["seq_idx"], d["last"], d["y"], D=D,
                              state_pool=pool, state_indices=sidx_d,
                              has_initial_state=hinit_d, write_final_to_pool=pool is not None,
-                             chunk_states_out=None if block_size else d["states"], **extra)
+                             chunk_states_out=None if block_size else d["states"],
+                             device_error_flag=flag, **extra)
             for d in bufs]
     ws_bytes = api.ssd_prefill_workspace_size(args[0])
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
@@ -310,6 +357,7 @@ def bench_prefill(torch, name, steps, warmup, sets=4, block_size=0, graph=False)
         end.record()
         torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
+    _assert_no_device_error(flag, f"prefill {name}")
     kt = _kernel_times(ev_sets, nk.value)
     spread = _kernel_spread(ev_sets, nk.value)
     work = prefill_work(inp, cuc, sidx, state_writes)
@@ -342,6 +390,7 @@ def bench_prefill(torch, name, steps, warmup, sets=4, block_size=0, graph=False)
             g1.record()
             torch.cuda.synchronize()
         graph_ms = g0.elapsed_time(g1) / steps
+        _assert_no_device_error(flag, f"prefill {name} (graph replay)")
         del graphs
     return dict(inp=inp, C=C, total_ms=total_ms, ms_per_step=total_ms / steps,
                 kernel_ms=dict(zip(knames, kt)), kernel_spread=dict(zip(knames, spread)),
@@ -362,7 +411,7 @@ def prefill_report(res, name, with_counters=True):
     path_gbs = w["path"]["bytes"] / (dev_ms * 1e-3) / 1e9
     return dict(
         tokens_per_s=tok_s,
-        roofline=_roofline("hbm", gbs, HBM_PEAK_GBS, "GB/s", traffic, dom),
+        roofline=_roofline("hbm", gbs, HBM_PEAK_GBS, "GB/s", traffic, dom, w[dom]),
         kernels={k: {"ms": round(v, 5), "ms_spread": res["kernel_spread"][k],
                      "gb_s": round(w[k]["bytes"] / (v * 1e-3) / 1e9, 1),
                      "tflop_s": round(w[k]["flops"] / (v * 1e-3) / 1e12, 2),
@@ -374,23 +423,60 @@ def prefill_report(res, name, with_counters=True):
     )
 
 
-def cpu_baseline_prefill(inp, n_seqs=None):
-    """The fp64 oracle on the first ``n_seqs`` sequences of the workload (default: all of
-    them, i.e. the whole timed step), all heads."""
-    n_seqs = inp.num_seqs if n_seqs is None else n_seqs
+def _cpu_info():
+    return {"host_logical_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "threads_env": "OMP_NUM_THREADS=MKL_NUM_THREADS=OPENBLAS_NUM_THREADS=1"}
+
+
+def cpu_baseline_prefill(inp, budget_s=None, min_s=0.5):
+    """The fp64 oracle timed on the GPU machine's host, on whole sequences of the workload in
+    order (each with its initial state and resume point, every chunk-end state recorded)
+    until ``budget_s`` of wall time is spent (None: all of them).  A batch that finishes in
+    under ``min_s`` is repeated until it has run that long.  Inputs are converted from
+    their storage dtype before the clock starts."""
+    import numpy as np
     from oracle import scan_prefill
     from selective_state_space_mamba2_amd.inputs import bf16_from_bits
-    t1 = int(inp.cu_seqlens[n_seqs])
     conv = (lambda a: bf16_from_bits(a)) if inp.in_dtype == "bf16" else (lambda a: a)
-    x, dt, B, C = (conv(getattr(inp, n)[:t1]) for n in ("x", "dt", "B", "C"))
-    w0, c0 = time.perf_counter(), time.process_time()
-    scan_prefill(x, dt, inp.A, B, C, inp.D, inp.cu_seqlens[:n_seqs + 1], inp.chunk_size)
-    wall, cpu = time.perf_counter() - w0, time.process_time() - c0
-    return {"value": round(t1 / wall, 2), "unit": "tokens/s",
+    cu = [int(v) for v in inp.cu_seqlens]
+    nc = [int(v) for v in inp.num_computed]
+    tokens, wall, cpu, n, reps = 0, 0.0, 0.0, 0, 1
+    for r in range(inp.num_seqs):
+        t0, t1 = cu[r], cu[r + 1]
+        x, dt, B, C = (conv(getattr(inp, k)[t0:t1]) for k in ("x", "dt", "B", "C"))
+        h0 = None
+        if inp.has_initial_state is not None and inp.has_initial_state[r]:
+            h0 = np.asarray(inp.pool[inp.state_indices[r]], dtype=np.float64)
+        w0, c0 = time.perf_counter(), time.process_time()
+        scan_prefill(x, dt, inp.A, B, C, inp.D, [0, t1 - t0], inp.chunk_size,
+                     num_computed=[nc[r]], initial_states=[h0])
+        wall += time.perf_counter() - w0
+        cpu += time.process_time() - c0
+        tokens += t1 - t0
+        n += 1
+        if budget_s is not None and wall >= budget_s:
+            break
+    while wall < min_s and n == inp.num_seqs:     # a tiny batch: repeat it
+        w0, c0 = time.perf_counter(), time.process_time()
+        for r in range(inp.num_seqs):
+            t0, t1 = cu[r], cu[r + 1]
+            scan_prefill(conv(inp.x[t0:t1]), conv(inp.dt[t0:t1]), inp.A, conv(inp.B[t0:t1]),
+                         conv(inp.C[t0:t1]), inp.D, [0, t1 - t0], inp.chunk_size,
+                         num_computed=[nc[r]])
+        wall += time.perf_counter() - w0
+        cpu += time.process_time() - c0
+        tokens += cu[-1]
+        reps += 1
+    what = "Mamba1 diagonal-A " if inp.a_kind == "diag" else ""
+    return {"value": round(tokens / wall, 2), "unit": "tokens/s",
             "cores": max(1, round(cpu / wall)), "kind": "oracle",
-            "sample": f"first {n_seqs} of {inp.num_seqs} sequences ({t1} tokens), all "
-                      f"{inp.H} heads, fp64 sequential recurrence with every chunk-end state; "
-                      f"{wall:.1f} s wall, host has {os.cpu_count()} logical CPUs"}
+            "sample": f"first {n} of {inp.num_seqs} sequences ({tokens // reps} tokens"
+                      + (f", the batch run {reps} times" if reps > 1 else "")
+                      + f"), all {inp.H} {'channels' if inp.a_kind == 'diag' else 'heads'}, "
+                      f"fp64 {what}sequential recurrence with every chunk-end state; "
+                      f"{wall:.1f} s wall" + ("" if budget_s is None else
+                                              f" (whole sequences until {budget_s:.0f} s)"),
+            **_cpu_info()}
 
 
 # ----------------------------------------------------------------------------------------
@@ -411,8 +497,9 @@ def bench_decode(torch, steps, warmup, with_cpu=True, name="decode_spec", pool_b
     acc = torch.from_numpy(inp.num_accepted).cuda()
     A = torch.tensor(inp.A, dtype=torch.float32).cuda()
     D = torch.tensor(inp.D, dtype=torch.float32).cuda()
+    flag = _error_flag(torch)
     a = api.decode_args(x, dt, A, B, C, y, pool, idx, num_accepted_tokens=acc,
-                        null_block_id=inp.null_block_id, D=D)
+                        null_block_id=inp.null_block_id, D=D, device_error_flag=flag)
     sp = torch.cuda.current_stream().cuda_stream
     for _ in range(warmup):
         check("ssd_state_update", lib().ssd_state_update(ctypes.byref(a), sp))
@@ -429,6 +516,7 @@ def bench_decode(torch, steps, warmup, with_cpu=True, name="decode_spec", pool_b
         end.record()
         torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
+    _assert_no_device_error(flag, f"decode {name}")
     kms = _kernel_times(ev_sets, 1)[0]
     w = decode_work(inp, 2 if pool_bf16 else 4)
     kname = "k_state_update_diag" if inp.A.ndim == 2 else "k_state_update"
@@ -439,7 +527,7 @@ def bench_decode(torch, steps, warmup, with_cpu=True, name="decode_spec", pool_b
            "roofline": _roofline("hbm", w["bytes"] / (kms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s",
                                  _counter_traffic(kname, name + ("/bf16_pool" if pool_bf16 else ""),
                                                   _source_digest("ssd_decode.hip", "ssd_device.h")),
-                                 kname),
+                                 kname, w),
            "kernel_ms": round(kms, 5), "kernel_ms_spread": _kernel_spread(ev_sets, 1)[0],
            "alg_bytes": w["bytes"]}
     if with_cpu:
@@ -454,7 +542,10 @@ def bench_decode(torch, steps, warmup, with_cpu=True, name="decode_spec", pool_b
         out["cpu_baseline"] = {"value": round(len(rows) * inp.ntok / wall, 2),
                                "unit": "state-updates/s", "cores": max(1, round(cpu / wall)),
                                "kind": "oracle",
-                               "sample": f"{len(rows)} live rows x {inp.ntok} tokens"}
+                               "sample": f"every live row ({len(rows)}) x {inp.ntok} tokens, "
+                                         f"fp64 sequential updates with the restore and every "
+                                         f"checkpoint; {wall:.1f} s wall",
+                               **_cpu_info()}
     del pool
     return out
 
@@ -462,7 +553,7 @@ def bench_decode(torch, steps, warmup, with_cpu=True, name="decode_spec", pool_b
 # ----------------------------------------------------------------------------------------
 # Mamba1 diagonal scan
 # ----------------------------------------------------------------------------------------
-def bench_diag(torch, steps, warmup):
+def bench_diag(torch, steps, warmup, with_cpu=True, cpu_budget_s=10.0):
     import ctypes
     import numpy as np
     from selective_state_space_mamba2_amd import api
@@ -478,7 +569,9 @@ def bench_diag(torch, steps, warmup):
     D = torch.tensor(inp.D, dtype=torch.float32).cuda()
     md = [torch.from_numpy(np.asarray(v, dtype=np.int32)).cuda()
           for v in (inp.cu_seqlens, cuc, sidx, last)]
-    a = api.prefill_args(x, dt, A, B, Cm, inp.chunk_size, *md, y, D=D, chunk_states_out=states)
+    flag = _error_flag(torch)
+    a = api.prefill_args(x, dt, A, B, Cm, inp.chunk_size, *md, y, D=D, chunk_states_out=states,
+                         device_error_flag=flag)
     sp = torch.cuda.current_stream().cuda_stream
     for _ in range(warmup):
         check("ssd_prefill", lib().ssd_prefill(ctypes.byref(a), None, 0, sp))
@@ -495,20 +588,27 @@ def bench_diag(torch, steps, warmup):
         end.record()
         torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
+    _assert_no_device_error(flag, "diag mamba1_long_diag")
     kms = _kernel_times(ev_sets, 1)[0]
     w = diag_work(inp, C)
     # VALU lane-ops per (token, channel, state): delta*A, exp (counted as 4: the
     # transcendental unit runs at a quarter of the FMA rate), x*B, the state FMA, the y FMA.
     lane_ops = w["steps"] * 8
-    return {"workload": "mamba1_long_diag", "metric": "tokens/s",
-            "value": round(inp.T / (ms * 1e-3), 1), "unit": "tokens/s",
-            "ms_per_step": round(ms, 5), "kernel_ms": round(kms, 5),
-            "roofline": _roofline("alu", lane_ops / (kms * 1e-3) / 1e12,
-                                  round(VALU_LANE_OPS / 1e12, 2), "T lane-op/s",
-                                  _counter_traffic("k_diag_scan", "mamba1_long_diag",
-                                                   _source_digest("ssd_diag.hip", "ssd_device.h")),
-                                  "k_diag_scan"),
-            "hbm_gb_s": round(w["bytes"] / (kms * 1e-3) / 1e9, 1), "alg_bytes": w["bytes"]}
+    out = {"workload": "mamba1_long_diag", "metric": "tokens/s",
+           "value": round(inp.T / (ms * 1e-3), 1), "unit": "tokens/s",
+           "ms_per_step": round(ms, 5), "kernel_ms": round(kms, 5),
+           "roofline": _roofline("alu", lane_ops / (kms * 1e-3) / 1e12,
+                                 round(VALU_LANE_OPS / 1e12, 2), "T lane-op/s",
+                                 _counter_traffic("k_diag_scan", "mamba1_long_diag",
+                                                  _source_digest("ssd_diag.hip", "ssd_device.h")),
+                                 "k_diag_scan"),
+           "hbm": _roofline("hbm", w["bytes"] / (kms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s",
+                            None, "k_diag_scan", w),
+           "hbm_gb_s": round(w["bytes"] / (kms * 1e-3) / 1e9, 1), "alg_bytes": w["bytes"]}
+    del x, dt, B, Cm, y
+    if with_cpu:
+        out["cpu_baseline"] = cpu_baseline_prefill(inp, budget_s=cpu_budget_s)
+    return out
 
 
 # ----------------------------------------------------------------------------------------
@@ -547,9 +647,10 @@ def bench_conv_prefill(torch, steps, warmup):
     x, pool, w, b = _conv_inputs(torch, inp)
     out = torch.empty_like(x)
     i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+    flag = _error_flag(torch)
     a = api.conv1d_args(x, w, b, out, i32(inp.cu_seqlens), i32(cuc), i32(sidx),
                         activation=True, conv_states=pool, state_indices=i32(inp.state_indices),
-                        has_initial_state=i32(inp.has_initial_state))
+                        has_initial_state=i32(inp.has_initial_state), device_error_flag=flag)
     sp = torch.cuda.current_stream().cuda_stream
     for _ in range(warmup):
         check("ssd_conv1d_prefill", lib().ssd_conv1d_prefill(ctypes.byref(a), sp))
@@ -567,13 +668,14 @@ def bench_conv_prefill(torch, steps, warmup):
         end.record()
         torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
+    _assert_no_device_error(flag, "conv1d prefill")
     kt = _kernel_times(ev_sets, nk)
     T, D, S, W = inp.T, inp.D, len(lengths), inp.W
     # x in and out once; every sequence's old state read (all have one) and new state
     # written; the taps and bias
     st = (W - 1) * D * 2
-    k_out = T * D * 2 * 2 + S * st + D * (W + 1) * 4
-    k_state = S * st
+    w_out = _rw(T * D * 2 + S * st + D * (W + 1) * 4, T * D * 2)
+    k_out, k_state = w_out["bytes"], S * st
     return {"workload": f"conv1d prefill, nemotron_h_prefix_cache batch ({T} tokens, 16 "
                         f"sequences), {D} bf16 channels, width {W}, SiLU, 1024-slot pool",
             "metric": "tokens/s", "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s",
@@ -581,7 +683,7 @@ def bench_conv_prefill(torch, steps, warmup):
             "roofline": _roofline("hbm", k_out / (kt[0] * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s",
                                   _counter_traffic("k_conv_prefill", "conv1d_prefill",
                                                    _source_digest("ssd_conv.hip", "ssd_device.h")),
-                                  "k_conv_prefill"),
+                                  "k_conv_prefill", w_out),
             "kernels": {"k_conv_prefill": {"ms": round(kt[0], 5), "alg_bytes": k_out},
                         "k_conv_state": {"ms": round(kt[1], 5), "alg_bytes": k_state}}}
 
@@ -602,8 +704,9 @@ def bench_conv_update(torch, steps, warmup):
     x, pool, w, b = _conv_inputs(torch, inp)
     x = x.reshape(B_pad, ntok, inp.D)
     out = torch.empty_like(x)
+    flag = _error_flag(torch)
     a = api.conv1d_update_args(x, w, b, out, pool, torch.from_numpy(idx).cuda(),
-                               activation=True, null_block_id=0)
+                               activation=True, null_block_id=0, device_error_flag=flag)
     sp = torch.cuda.current_stream().cuda_stream
     for _ in range(warmup):
         check("ssd_conv1d_update", lib().ssd_conv1d_update(ctypes.byref(a), sp))
@@ -620,9 +723,12 @@ def bench_conv_update(torch, steps, warmup):
         end.record()
         torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
+    _assert_no_device_error(flag, "conv1d update")
     kms = _kernel_times(ev_sets, 1)[0]
     D, W = inp.D, inp.W
-    alg = n_live * (2 * (W - 1) * D * 2 + 2 * ntok * D * 2) + D * (W + 1) * 4
+    w_upd = _rw(n_live * ((W - 1) * D * 2 + ntok * D * 2) + D * (W + 1) * 4,
+                n_live * ((W - 1) * D * 2 + ntok * D * 2))
+    alg = w_upd["bytes"]
     return {"workload": f"conv1d update, {n_live} live rows of {B_pad}, {ntok} input each, "
                         f"{D} bf16 channels, SiLU, {slots}-slot pool",
             "metric": "rows/s", "value": round(n_live / (ms * 1e-3), 1), "unit": "rows/s",
@@ -630,59 +736,89 @@ def bench_conv_update(torch, steps, warmup):
             "roofline": _roofline("hbm", alg / (kms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s",
                                   _counter_traffic("k_conv_update", "conv1d_update",
                                                    _source_digest("ssd_conv.hip", "ssd_device.h")),
-                                  "k_conv_update"),
+                                  "k_conv_update", w_upd),
             "alg_bytes": alg}
 
 
-def measured_peaks(torch, mib=2048, reps=10):
-    """What this GPU reaches with library kernels, as a second scale beside the spec peaks:
-    a device copy (read + write), a fill (write only), a sum (read only) of ``mib`` MiB
-    and a square bf16 GEMM of 8192 (hipBLASLt).  Best of ``reps`` launches each."""
-    n = mib * (1 << 20) // 4
-    a = torch.empty(n, dtype=torch.float32, device="cuda").normal_()
-    b = torch.empty_like(a)
-    s = torch.empty((), dtype=torch.float32, device="cuda")
+def _read_fracs(obj, out=None):
+    """Every HBM roofline's read fraction in the line."""
+    out = set() if out is None else out
+    if isinstance(obj, dict):
+        if obj.get("bound") == "hbm" and "read_frac" in obj:
+            out.add(round(obj["read_frac"], 2))
+        for v in obj.values():
+            _read_fracs(v, out)
+    return out
 
-    def best(fn):
+
+def measured_peaks(torch, read_fracs, mib=2048, reps=10):
+    """What this GPU sustains, as a second scale beside the spec peaks: the library's own
+    streaming probe (ssd_probe_stream) moving ``mib`` MiB per launch as pure reads, pure
+    writes, and at each read/write mix an HBM roofline of the line has (best of ``reps``
+    launches each); and a square bf16 GEMM of 8192 through torch (hipBLASLt) for the MFMA
+    side."""
+    import ctypes
+    from selective_state_space_mamba2_amd._abi import check, lib
+    nbytes = mib * (1 << 20)
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").normal_()
+    dst = torch.empty_like(src)
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    sp = torch.cuda.current_stream().cuda_stream
+
+    def rate(rb, wb):
+        rb, wb = rb // 16 * 16, wb // 16 * 16
         ts = []
-        for _ in range(reps):
+        for i in range(reps + 1):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            fn()
+            check("ssd_probe_stream", lib().ssd_probe_stream(src.data_ptr(), rb, dst.data_ptr(),
+                                                             wb, sink.data_ptr(), sp))
             e1.record()
             torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        return min(ts) * 1e-3
+            if i:
+                ts.append(e0.elapsed_time(e1))
+        return round((rb + wb) / (min(ts) * 1e-3) / 1e9, 1)
 
-    fn_copy, fn_fill = (lambda: b.copy_(a)), (lambda: b.fill_(1.0))
-    fn_sum = lambda: torch.sum(a, dim=0, out=s)
-    for f in (fn_copy, fn_fill, fn_sum):
-        f()
-    nbytes = n * 4
-    out = {"copy_gb_s": round(2 * nbytes / best(fn_copy) / 1e9, 1),
-           "write_gb_s": round(nbytes / best(fn_fill) / 1e9, 1),
-           "read_gb_s": round(nbytes / best(fn_sum) / 1e9, 1)}
-    del a, b
+    out = {"read_gb_s": rate(nbytes, 0), "write_gb_s": rate(0, nbytes),
+           "copy_gb_s": rate(nbytes // 2, nbytes // 2)}
+    out["mix_gb_s"] = {f"{f:.2f}": rate(int(nbytes * f), int(nbytes * (1 - f)))
+                       for f in sorted(read_fracs)}
+    del src, dst
     m = 8192
     x = torch.randn(m, m, device="cuda").to(torch.bfloat16)
     y = torch.randn(m, m, device="cuda").to(torch.bfloat16)
     z = torch.empty(m, m, device="cuda", dtype=torch.bfloat16)
     torch.matmul(x, y, out=z)
-    out["bf16_gemm_tflop_s"] = round(2 * m ** 3 / best(lambda: torch.matmul(x, y, out=z)) / 1e12, 1)
-    out["note"] = (f"library kernels on this GPU, best of {reps}: copy/fill/sum of {mib} MiB, "
-                   f"bf16 GEMM {m}^3")
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.matmul(x, y, out=z)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    out["bf16_gemm_tflop_s"] = round(2 * m ** 3 / (min(ts) * 1e-3) / 1e12, 1)
+    out["note"] = (f"ssd_probe_stream (this library's streaming kernel, non-temporal writes) "
+                   f"moving {mib} MiB per launch, best of {reps}: pure reads, pure writes, a "
+                   f"half/half copy mix and each read fraction (mix_gb_s keys) an HBM roofline "
+                   f"of this line has; torch bf16 GEMM {m}^3")
     del x, y, z
     torch.cuda.empty_cache()
     return out
 
 
 def _add_measured_frac(obj, peaks):
-    """Beside each HBM roofline's spec fraction, its fraction of the measured copy rate."""
+    """Beside each HBM roofline's spec fraction, its fraction of what the probe sustains at
+    the same read/write mix."""
     if isinstance(obj, dict):
         r = obj.get("roofline")
-        if isinstance(r, dict) and r.get("bound") == "hbm":
-            r["measured_peak"] = peaks["copy_gb_s"]
-            r["measured_frac"] = round(r["achieved"] / peaks["copy_gb_s"], 4)
+        for cand in (obj, r):
+            if isinstance(cand, dict) and cand.get("bound") == "hbm" and "read_frac" in cand:
+                key = f"{round(cand['read_frac'], 2):.2f}"
+                peak = peaks["mix_gb_s"].get(key)
+                if peak:
+                    cand["measured_peak"] = peak
+                    cand["measured_frac"] = round(cand["achieved"] / peak, 4)
         for v in obj.values():
             if isinstance(v, dict) and v is not r:
                 _add_measured_frac(v, peaks)
@@ -698,6 +834,46 @@ def copy_calibration(torch, mib=1024, reps=3):
     _log(f"copy calibration: {reps} copies of {mib} MiB")
 
 
+def _prefill_config(inp, C):
+    lens = [int(v) for v in (inp.cu_seqlens[1:] - inp.cu_seqlens[:-1])]
+    nc = [int(v) for v in inp.num_computed]
+    cfg = {"num_seqs": inp.num_seqs, "tokens": inp.T, "chunks": C,
+           "seq_len": lens[0] if len(set(lens)) == 1 else f"{min(lens)}..{max(lens)} (varlen)",
+           "nheads": inp.H, "headdim": inp.P, "ngroups": inp.G, "dstate": inp.N,
+           "chunk_size": inp.chunk_size, "in_dtype": inp.in_dtype, "state_dtype": "f32",
+           "states": "every chunk end" + (" + final state to the pool" if inp.pool is not None else "")}
+    if any(nc):
+        cfg["num_computed"] = f"{min(nc)}..{max(nc)}, none a multiple of the chunk size"
+    if inp.pool is not None:
+        cfg["initial_states"] = f"gathered from a {inp.pool.shape[0]}-slot fp32 pool"
+    return cfg
+
+
+def prefill_leg(torch, name, steps, warmup, graph=False, with_cpu=True, cpu_budget_s=None,
+                block_size=0):
+    """One prefill workload: timing, roofline, kernels, path totals, optional graph replay
+    and the oracle baseline."""
+    res = bench_prefill(torch, name, steps, warmup, graph=graph, block_size=block_size)
+    key = name + ("/all" if block_size else "")
+    rep = prefill_report(res, key)
+    inp = res["inp"]
+    out = {"workload": name + (", all cache mode (block_size 256, one pool entry per block, "
+                               "no chunk-state output)" if block_size else ""),
+           "metric": "tokens/s", "value": round(rep["tokens_per_s"], 1), "unit": "tokens/s",
+           "ms_per_step": round(res["ms_per_step"], 5), "config": _prefill_config(inp, res["C"]),
+           "roofline": rep["roofline"], "kernels": rep["kernels"], "path": rep["path"]}
+    if res["graph_ms"] is not None:
+        out["graph"] = {"ms_per_step": round(res["graph_ms"], 5),
+                        "tokens_per_s": round(inp.T / (res["graph_ms"] * 1e-3), 1),
+                        "note": "the two prefill kernels replayed from HIP graphs (metadata "
+                                "resident); value is the eager step with host metadata"}
+    del res
+    if with_cpu:
+        _log(f"cpu baseline (oracle) {name}")
+        out["cpu_baseline"] = cpu_baseline_prefill(inp, budget_s=cpu_budget_s)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -706,6 +882,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--primary-only", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds of oracle time per sampled baseline")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
@@ -718,59 +896,43 @@ def main():
         sys.exit(1)
     if args.copy_calibration:
         copy_calibration(torch)
+    cpu = not args.no_cpu_baseline
 
-    name = "mamba2_2.7b_prefill"
+    name = "nemotron_h_prefix_cache"
     _log(f"prefill {name}: {args.steps} steps after {args.warmup} warm-up")
-    res = bench_prefill(torch, name, args.steps, args.warmup, graph=True)
-    rep = prefill_report(res, name)
-    inp = res["inp"]
+    head = prefill_leg(torch, name, args.steps, args.warmup, graph=True, with_cpu=cpu,
+                       cpu_budget_s=args.cpu_budget)
     line = {
         "metric": METRIC,
-        "value": round(rep["tokens_per_s"], 1),
+        "value": head["value"],
         "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(res["ms_per_step"], 5),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": name, "num_seqs": inp.num_seqs, "seq_len": 2048,
-                   "tokens": inp.T, "nheads": inp.H, "headdim": inp.P, "ngroups": inp.G,
-                   "dstate": inp.N, "chunk_size": inp.chunk_size,
-                   "states": "every chunk end", "parallelism": "single GPU"},
-        "roofline": rep["roofline"],
-        "kernels": rep["kernels"],
-        "path": rep["path"],
-        "graph": {"ms_per_step": round(res["graph_ms"], 5),
-                  "tokens_per_s": round(inp.T / (res["graph_ms"] * 1e-3), 1),
-                  "note": "the two prefill kernels replayed from HIP graphs (metadata resident); "
-                          "value above is the eager step with host metadata"},
+        "config": {"workload": name, **head["config"], "parallelism": "single GPU"},
+        "roofline": head["roofline"],
+        "kernels": head["kernels"],
+        "path": head["path"],
+        "graph": head["graph"],
     }
-    if not args.no_cpu_baseline:
-        _log("cpu baseline (oracle)")
-        line["cpu_baseline"] = cpu_baseline_prefill(inp)
-    del res
+    if "cpu_baseline" in head:
+        line["cpu_baseline"] = head["cpu_baseline"]
     if not args.primary_only:
-        def nemotron(block_size=0):
-            key = "nemotron_h_prefix_cache" + ("/all" if block_size else "")
-            res = bench_prefill(torch, "nemotron_h_prefix_cache", args.steps, args.warmup,
-                                block_size=block_size)
-            rep = prefill_report(res, key)
-            return {"workload": "nemotron_h_prefix_cache" + (
-                        ", all cache mode (block_size 256, one pool entry per block, no "
-                        "chunk-state output)" if block_size else ""),
-                    "value": round(rep["tokens_per_s"], 1), "unit": "tokens/s",
-                    "tokens": res["inp"].T, "chunks": res["C"],
-                    "ms_per_step": round(res["ms_per_step"], 5), "roofline": rep["roofline"],
-                    "kernels": rep["kernels"], "path": rep["path"]}
-
-        cpu = not args.no_cpu_baseline
         legs = [
+            ("prefill_mamba2_2.7b", "mamba2_2.7b_prefill",
+             lambda: prefill_leg(torch, "mamba2_2.7b_prefill", args.steps, args.warmup,
+                                 graph=True, with_cpu=cpu)),
+            ("prefill_tiny_fp32", "tiny_fp32",
+             lambda: prefill_leg(torch, "tiny_fp32", args.steps, args.warmup, with_cpu=cpu)),
             ("decode", "decode_spec",
              lambda: bench_decode(torch, args.steps, args.warmup, with_cpu=cpu)),
-            ("prefill_nemotron", "nemotron_h_prefix_cache", lambda: nemotron()),
-            ("prefill_nemotron_all_mode", "nemotron_h_prefix_cache, all cache mode",
-             lambda: nemotron(block_size=256)),
             ("diag", "mamba1_long_diag",
-             lambda: bench_diag(torch, max(3, args.steps // 5), max(1, args.warmup // 5))),
+             lambda: bench_diag(torch, max(3, args.steps // 5), max(1, args.warmup // 5),
+                                with_cpu=cpu, cpu_budget_s=args.cpu_budget)),
+            ("prefill_nemotron_all_mode", "nemotron_h_prefix_cache, all cache mode",
+             lambda: prefill_leg(torch, "nemotron_h_prefix_cache", args.steps, args.warmup,
+                                 with_cpu=False, block_size=256)),
             ("decode_mamba1", "mamba1_decode_spec",
              lambda: bench_decode(torch, args.steps, args.warmup, with_cpu=cpu,
                                   name="mamba1_decode_spec")),
@@ -793,7 +955,7 @@ def main():
             torch.cuda.empty_cache()
         _log("measured peaks")
         try:
-            peaks = measured_peaks(torch)
+            peaks = measured_peaks(torch, _read_fracs(line))
             line["measured_peaks"] = peaks
             _add_measured_frac(line, peaks)
         except Exception as e:   # noqa: BLE001

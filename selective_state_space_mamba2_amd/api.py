@@ -3,6 +3,18 @@
 Every function here has the name of the C entry point it calls.  Device tensors are torch
 tensors (torch provides device memory and streams); every step of the scan runs in the
 HIP library, and there is no other implementation to fall back on.
+
+Before anything is handed to the library, every tensor is checked for what the C ABI
+assumes of the memory behind its pointer: on the GPU of ``x`` (a host pointer given to a
+kernel would fault the GPU), the dtype the header declares (int32 metadata and indices,
+fp32 parameters, token tensors in x's dtype), contiguous where the ABI takes no stride,
+and the element count the sizes imply.  A violation raises ValueError and launches
+nothing.
+
+Device-side errors (an index out of range, inconsistent chunk metadata) are OR-ed into
+an int32 error word.  A call given no ``device_error_flag`` uses a persistent error word
+of its GPU, so such errors are never lost: ``ssd_device_errors`` reads it (and
+synchronises the device), ``check_device_errors`` raises when it is set.
 """
 from __future__ import annotations
 
@@ -19,6 +31,7 @@ __all__ = [
     "ssd_abi_version", "ssd_status_string", "ssd_chunk_metadata_count",
     "ssd_build_chunk_metadata", "ssd_prefill_workspace_size", "ssd_prefill",
     "ssd_state_update", "prefill_args", "ssd_conv1d_prefill", "ssd_conv1d_update",
+    "ssd_device_errors", "check_device_errors", "device_error_names",
 ]
 
 
@@ -88,6 +101,103 @@ def _stream_ptr(stream) -> Optional[int]:
     return s.cuda_stream
 
 
+_DEVERR_NAMES = [(_abi.SSD_DEVERR_CHUNK_RANGE, "CHUNK_RANGE"),
+                 (_abi.SSD_DEVERR_SLOT_RANGE, "SLOT_RANGE"),
+                 (_abi.SSD_DEVERR_ACCEPTED, "ACCEPTED"),
+                 (_abi.SSD_DEVERR_CHAIN_WAIT, "CHAIN_WAIT"),
+                 (_abi.SSD_DEVERR_DUPLICATE_SLOT, "DUPLICATE_SLOT")]
+_ERROR_WORDS = {}
+
+
+def _error_word(device):
+    """The persistent int32 error word of a GPU (allocated zeroed on first use)."""
+    import torch
+    idx = torch.device(device).index
+    idx = torch.cuda.current_device() if idx is None else idx
+    w = _ERROR_WORDS.get(idx)
+    if w is None:
+        w = torch.zeros(1, dtype=torch.int32, device=f"cuda:{idx}")
+        _ERROR_WORDS[idx] = w
+    return w
+
+
+def device_error_names(bits: int):
+    """Names of the SSD_DEVERR_* bits set in ``bits``."""
+    return [n for b, n in _DEVERR_NAMES if bits & b]
+
+
+def ssd_device_errors(device=None, clear: bool = True) -> int:
+    """SSD_DEVERR_* bits raised on ``device`` (default: the current GPU) by calls that were
+    given no device_error_flag, since the last clear.  Synchronises the device."""
+    import torch
+    w = _error_word("cuda" if device is None else device)
+    torch.cuda.synchronize(w.device)
+    bits = int(w.item())
+    if clear and bits:
+        w.zero_()
+    return bits
+
+
+def check_device_errors(device=None) -> None:
+    """Raise RuntimeError if a call without its own device_error_flag raised a device-side
+    error on ``device`` (the error word is cleared)."""
+    bits = ssd_device_errors(device)
+    if bits:
+        raise RuntimeError(f"SSD device error bits 0x{bits:x}: {', '.join(device_error_names(bits))}")
+
+
+class _Checker:
+    """Argument checks of one call: everything on ``device``, the declared dtypes, the
+    memory layout the ABI assumes and the element counts the sizes imply."""
+
+    def __init__(self, fn: str, ref):
+        self.fn = fn
+        self.device = ref.device
+
+    def fail(self, msg):
+        raise ValueError(f"{self.fn}: {msg}")
+
+    def t(self, name, t, dtypes=None, numel=None, contiguous=False, min_numel=None):
+        import torch
+        if t is None:
+            return
+        if not isinstance(t, torch.Tensor):
+            self.fail(f"{name} must be a torch tensor")
+        if dtypes is not None and t.dtype not in dtypes:
+            self.fail(f"{name} has dtype {t.dtype}, expected {' or '.join(map(str, dtypes))}")
+        if contiguous and not t.is_contiguous():
+            self.fail(f"{name} must be contiguous")
+        if numel is not None and t.numel() != numel:
+            self.fail(f"{name} has {t.numel()} elements, expected {numel}")
+        if min_numel is not None and t.numel() < min_numel:
+            self.fail(f"{name} has {t.numel()} elements, expected at least {min_numel}")
+        if t.device != self.device:
+            self.fail(f"{name} is on {t.device}, expected {self.device} (the device of the "
+                      f"token tensors)")
+
+    def i32(self, name, t, numel=None, min_numel=None):
+        import torch
+        self.t(name, t, (torch.int32,), numel=numel, contiguous=True, min_numel=min_numel)
+
+    def f32(self, name, t, numel=None):
+        import torch
+        self.t(name, t, (torch.float32,), numel=numel, contiguous=True)
+
+    def gpu(self, name, t):
+        if not t.is_cuda:
+            self.fail(f"{name} must be a GPU tensor (got {t.device})")
+
+
+def _float_dtypes():
+    import torch
+    return (torch.bfloat16, torch.float32)
+
+
+def _flag_for(ck: _Checker, device_error_flag):
+    """The caller's error flag, or the GPU's persistent error word."""
+    return _error_word(ck.device) if device_error_flag is None else device_error_flag
+
+
 def prefill_args(x, dt, A, B, C, chunk_size: int, cu_seqlens, cu_chunk_seqlens, seq_idx,
                  last_chunk_indices, y, D=None, dt_bias=None, dt_softplus: bool = False,
                  dt_limit=(0.0, math.inf), state_pool=None, state_indices=None,
@@ -98,21 +208,64 @@ def prefill_args(x, dt, A, B, C, chunk_size: int, cu_seqlens, cu_chunk_seqlens, 
                  block_idx_last_scheduled=None) -> PrefillArgs:
     """Fill an ssd_prefill_args from tensors (no device work).  block_size > 0 selects the
     all cache mode: state_indices is then [S, max_blocks] (row stride taken from it)."""
+    import torch
+    ck = _Checker("ssd_prefill", x)
+    if x.dim() != 3 or B.dim() != 3 or C.dim() != 3 or dt.dim() != 2 or y.dim() != 3:
+        ck.fail("x, y must be [T, H, P], dt [T, H], B and C [T, G, N]")
     T, H, P = x.shape
     G, N = B.shape[1], B.shape[2]
+    ck.t("x", x, _float_dtypes())
+    for name, t in (("dt", dt), ("B", B), ("C", C), ("y", y)):
+        ck.t(name, t, (x.dtype,))
+    if tuple(dt.shape) != (T, H) or tuple(y.shape) != (T, H, P) or tuple(C.shape) != (T, G, N) \
+            or B.shape[0] != T:
+        ck.fail("dt, B, C and y must match x's tokens and heads")
     for name, t, inner in (("x", x, (P, 1)), ("y", y, (P, 1)), ("B", B, (N, 1)),
                            ("C", C, (N, 1))):
         if tuple(t.stride()[1:]) != inner:
             raise ValueError(f"{name}: each token row must be contiguous")
     if dt.stride(1) != 1 or B.stride(0) != C.stride(0):
         raise ValueError("dt rows must be contiguous and B, C must share a token stride")
+    S = cu_seqlens.numel() - 1
+    Cn = seq_idx.numel()
+    diag = A.dim() == 2
+    ck.f32("A", A, numel=H * N if diag else H)
+    ck.f32("D", D, numel=H)
+    ck.f32("dt_bias", dt_bias, numel=H)
+    ck.i32("cu_seqlens", cu_seqlens)
+    ck.i32("cu_chunk_seqlens", cu_chunk_seqlens, numel=Cn + 1)
+    ck.i32("seq_idx", seq_idx)
+    ck.i32("last_chunk_indices", last_chunk_indices, numel=S)
+    if state_pool is not None:
+        ck.t("state_pool", state_pool, _float_dtypes())
+        if state_pool.dim() != 4 or tuple(state_pool.shape[1:]) != (H, P, N) or \
+                tuple(state_pool.stride()[1:]) != (P * N, N, 1):
+            ck.fail("state_pool must be [slots, H, P, N] with contiguous slots")
+    if state_indices is not None:
+        ck.t("state_indices", state_indices, (torch.int32,))
+        if state_indices.stride(-1) != 1 or state_indices.dim() > 2 or \
+                (not block_size and state_indices.numel() != S) or \
+                (block_size and (state_indices.dim() != 2 or state_indices.shape[0] != S)):
+            ck.fail("state_indices must be [S] (or [S, max_blocks] in the all cache mode) "
+                    "with contiguous rows")
+    ck.i32("has_initial_state", has_initial_state, numel=S)
+    ck.f32("chunk_states_out", chunk_states_out, numel=Cn * H * P * N)
+    ck.f32("dA_cumsum_out", dA_cumsum_out, numel=H * T)
+    ck.f32("cb_out", cb_out, numel=Cn * G * chunk_size * chunk_size)
+    ck.f32("chunk_local_states_out", chunk_local_states_out, numel=Cn * H * P * N)
+    ck.i32("num_computed", num_computed, numel=S)
+    ck.i32("block_idx_last_computed", block_idx_last_computed, numel=S)
+    ck.i32("block_idx_last_scheduled", block_idx_last_scheduled, numel=S)
+    ck.i32("device_error_flag", device_error_flag, min_numel=1)
+    ck.gpu("x", x)     # every other tensor is on x's device
+    device_error_flag = _flag_for(ck, device_error_flag)
     a = PrefillArgs()
     a.T, a.H, a.P, a.G, a.N = T, H, P, G, N
     a.chunk_size = int(chunk_size)
-    a.num_seqs = cu_seqlens.numel() - 1
-    a.num_chunks = seq_idx.numel()
+    a.num_seqs = S
+    a.num_chunks = Cn
     a.in_dtype = _dtype_code(x)
-    a.a_kind = _abi.SSD_A_SCALAR if A.dim() == 1 else _abi.SSD_A_DIAG
+    a.a_kind = _abi.SSD_A_DIAG if diag else _abi.SSD_A_SCALAR
     a.x, a.x_stride_t = x.data_ptr(), x.stride(0)
     a.dt, a.dt_stride_t = dt.data_ptr(), dt.stride(0)
     a.B, a.C, a.bc_stride_t = B.data_ptr(), C.data_ptr(), B.stride(0)
@@ -178,16 +331,46 @@ def decode_args(x, dt, A, B, C, y, state_pool, state_indices, num_accepted_token
                 block_idx_last_computed=None, block_idx_last_scheduled=None) -> DecodeArgs:
     """Fill an ssd_decode_args.  Passing the two block index tensors selects the all cache
     mode: state_indices is then [B_pad, max_blocks] and ntok must be 1."""
+    import torch
+    ck = _Checker("ssd_state_update", x)
+    if x.dim() != 4 or B.dim() != 4 or C.dim() != 4 or dt.dim() != 3 or y.dim() != 4:
+        ck.fail("x, y must be [B_pad, ntok, H, P], dt [B_pad, ntok, H], B and C "
+                "[B_pad, ntok, G, N]")
     B_pad, ntok, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
+    ck.t("x", x, _float_dtypes())
+    for name, t in (("dt", dt), ("B", B), ("C", C), ("y", y)):
+        ck.t(name, t, (x.dtype,))
+    if tuple(dt.shape) != (B_pad, ntok, H) or tuple(y.shape) != tuple(x.shape) or \
+            tuple(B.shape[:2]) != (B_pad, ntok) or tuple(C.shape) != tuple(B.shape):
+        ck.fail("dt, B, C and y must match x's rows, tokens and heads")
     for name, t in (("x", x), ("dt", dt), ("B", B), ("C", C), ("y", y),
                     ("state_indices", state_indices)):
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
+    diag = A.dim() == 2
+    ck.f32("A", A, numel=H * N if diag else H)
+    ck.f32("D", D, numel=H)
+    ck.f32("dt_bias", dt_bias, numel=H)
+    ck.t("state_pool", state_pool, _float_dtypes())
+    if state_pool.dim() != 4 or tuple(state_pool.shape[1:]) != (H, P, N) or \
+            tuple(state_pool.stride()[1:]) != (P * N, N, 1):
+        ck.fail("state_pool must be [slots, H, P, N] with contiguous slots")
+    ck.t("state_indices", state_indices, (torch.int32,))
+    if state_indices.dim() != 2 or state_indices.shape[0] != B_pad or \
+            (block_idx_last_scheduled is None and state_indices.shape[1] != ntok):
+        ck.fail("state_indices must be [B_pad, ntok] (or [B_pad, max_blocks] in the all "
+                "cache mode)")
+    ck.i32("num_accepted_tokens", num_accepted_tokens, numel=B_pad)
+    ck.i32("block_idx_last_computed", block_idx_last_computed, numel=B_pad)
+    ck.i32("block_idx_last_scheduled", block_idx_last_scheduled, numel=B_pad)
+    ck.i32("device_error_flag", device_error_flag, min_numel=1)
+    ck.gpu("x", x)     # every other tensor is on x's device
+    device_error_flag = _flag_for(ck, device_error_flag)
     a = DecodeArgs()
     a.B_pad, a.ntok, a.H, a.P, a.G, a.N = B_pad, ntok, H, P, G, N
     a.in_dtype = _dtype_code(x)
-    a.a_kind = _abi.SSD_A_SCALAR if A.dim() == 1 else _abi.SSD_A_DIAG
+    a.a_kind = _abi.SSD_A_DIAG if diag else _abi.SSD_A_SCALAR
     a.x, a.dt, a.B, a.C, a.y = x.data_ptr(), dt.data_ptr(), B.data_ptr(), C.data_ptr(), y.data_ptr()
     a.A, a.D, a.dt_bias = A.data_ptr(), _dptr(D), _dptr(dt_bias)
     a.dt_softplus = 1 if dt_softplus else 0
@@ -223,12 +406,35 @@ def conv1d_args(x, weight, bias, out, cu_seqlens, cu_chunk_seqlens, seq_idx,
                 device_error_flag=None) -> _abi.Conv1dArgs:
     """Fill an ssd_conv1d_args.  x, out [T, D] (rows contiguous); weight [D, W] fp32;
     conv_states [slots, W-1, D] ("sd") or [slots, D, W-1] ("ds") in x's dtype."""
+    ck = _Checker("ssd_conv1d_prefill", x)
+    if x.dim() != 2 or out.dim() != 2 or weight.dim() != 2:
+        ck.fail("x and out must be [T, D], weight [D, W]")
     T, D = x.shape
+    ck.t("x", x, _float_dtypes())
+    ck.t("out", out, (x.dtype,))
+    if tuple(out.shape) != (T, D) or weight.shape[0] != D:
+        ck.fail("out must match x, weight must have D rows")
     for name, t in (("x", x), ("out", out)):
         if t.stride(1) != 1:
             raise ValueError(f"{name}: each token row must be contiguous")
     if not weight.is_contiguous():
         raise ValueError("weight must be contiguous")
+    S = cu_seqlens.numel() - 1
+    ck.f32("weight", weight)
+    ck.f32("bias", bias, numel=D)
+    ck.i32("cu_seqlens", cu_seqlens)
+    ck.i32("cu_chunk_seqlens", cu_chunk_seqlens, numel=seq_idx.numel() + 1)
+    ck.i32("seq_idx", seq_idx)
+    if conv_states is not None:
+        ck.t("conv_states", conv_states, (x.dtype,))
+        if conv_states.dim() != 3 or not conv_states[0].is_contiguous():
+            ck.fail("conv_states must be [slots, W-1, D] or [slots, D, W-1] with contiguous "
+                    "slots")
+    ck.i32("state_indices", state_indices, numel=S)
+    ck.i32("has_initial_state", has_initial_state, numel=S)
+    ck.i32("device_error_flag", device_error_flag, min_numel=1)
+    ck.gpu("x", x)     # every other tensor is on x's device
+    device_error_flag = _flag_for(ck, device_error_flag)
     a = _abi.Conv1dArgs()
     a.T, a.D, a.W = T, D, weight.shape[1]
     a.num_seqs = cu_seqlens.numel() - 1
@@ -268,11 +474,27 @@ def conv1d_update_args(x, weight, bias, out, conv_states, state_indices,
                        activation: bool = False, null_block_id: int = 0,
                        state_layout: str = "sd", device_error_flag=None) -> _abi.Conv1dUpdateArgs:
     """Fill an ssd_conv1d_update_args.  x, out [B_pad, ntok, D] contiguous."""
+    ck = _Checker("ssd_conv1d_update", x)
+    if x.dim() != 3 or out.dim() != 3 or weight.dim() != 2:
+        ck.fail("x and out must be [B_pad, ntok, D], weight [D, W]")
     B_pad, ntok, D = x.shape
+    ck.t("x", x, _float_dtypes())
+    ck.t("out", out, (x.dtype,))
+    if tuple(out.shape) != tuple(x.shape) or weight.shape[0] != D:
+        ck.fail("out must match x, weight must have D rows")
     for name, t in (("x", x), ("out", out), ("weight", weight),
                     ("state_indices", state_indices)):
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
+    ck.f32("weight", weight)
+    ck.f32("bias", bias, numel=D)
+    ck.t("conv_states", conv_states, (x.dtype,))
+    if conv_states.dim() != 3 or not conv_states[0].is_contiguous():
+        ck.fail("conv_states must be [slots, W-1, D] or [slots, D, W-1] with contiguous slots")
+    ck.i32("state_indices", state_indices, numel=B_pad)
+    ck.i32("device_error_flag", device_error_flag, min_numel=1)
+    ck.gpu("x", x)     # every other tensor is on x's device
+    device_error_flag = _flag_for(ck, device_error_flag)
     a = _abi.Conv1dUpdateArgs()
     a.B_pad, a.ntok, a.D, a.W = B_pad, ntok, D, weight.shape[1]
     a.in_dtype = _dtype_code(x)

@@ -21,7 +21,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libssd.so")
 
 HIP_SOURCES = ["ssd_entry.hip", "ssd_prefill.hip", "ssd_decode.hip", "ssd_diag.hip", "ssd_conv.hip",
-               "ssd_debug.hip"]
+               "ssd_debug.hip", "ssd_probe.hip"]
 HOST_SOURCES = ["ssd_host.cpp"]
 ARCH = "gfx950"
 HIP_FLAGS = [

@@ -1,18 +1,21 @@
-// ssd_diag.hip -- Mamba1-style selective scan with a per-(channel, state) diagonal A.
+// ssd_diag.hip -- sequential selective scan with a one-element head: Mamba1's per-(channel,
+// state) diagonal A, and Mamba2's scalar A per head at head_dim 1.
 //
 // The S6 model of "[vLLM] Mamba (SSM)" (paper key content) with A[channel, state]:
 //   h[c,n] = exp(delta[t,c] A[c,n]) h[c,n] + delta[t,c] x[t,c] B[t,n];  y[t,c] = sum_n C[t,n] h[c,n] + D[c] x[t,c]
 // Mamba1 has no chunk notion of its own, so the chunk size only sets where state
 // checkpoints are written ("vLLM Mamba2 SSD kernel warm-up", config/model.py section).
+// The Mamba2 recurrence with head_dim 1 is the same scan with A[c, n] = A[c] for every n
+// (one decay per (token, head), so one exponential instead of N) and B/C taken from the
+// head's group g = c / (H / G): its MFMA form would contract over a single column.
 //
-// This path is bound by the exponential (one per (token, channel, state)) and VALU work,
-// not by a contraction, so it runs on the vector ALUs: one workgroup owns 64 channels of
-// one sequence and walks its tokens in order; each channel's 16 states are spread over 4
-// adjacent lanes (4 states each) and y is a 4-lane reduction.  Token tiles of delta, x,
-// B and C are staged through LDS with coalesced loads (64 channels = 128 B per token for
-// bf16), delta is prepared once per (token, channel) while staging, and y leaves through
-// an LDS tile as coalesced rows.  Checkpoints are written at the chunk ends listed by the
-// chunk metadata.
+// This path is bound by the exponential and VALU work, not by a contraction, so it runs on
+// the vector ALUs: one workgroup owns CH channels of one group of one sequence and walks
+// its tokens in order; each channel's N states are spread over LPC adjacent lanes (SPL
+// states each) and y is an LPC-lane reduction.  Token tiles of delta, x, B and C are staged
+// through LDS with coalesced loads (64 channels = 128 B per token for bf16), delta is
+// prepared once per (token, channel) while staging, and y leaves through an LDS tile as
+// coalesced rows.  Checkpoints are written at the chunk ends listed by the chunk metadata.
 #include <cstdint>
 #include <type_traits>
 
@@ -27,33 +30,48 @@ namespace ssd {
 #define SSD_DIAG_SPL 4
 #endif
 
-// SPL states per lane: a channel's 16 states sit on 16/SPL adjacent lanes and a
-// workgroup owns CH = 256 / (16/SPL) channels.
-template <typename T, int SPL>
+// NS states per channel, SPL per lane: a channel's states sit on LPC = NS/SPL adjacent
+// lanes and a workgroup owns CH = 256 / LPC channels.
+template <int NS, int SPL>
 struct DiagCfg {
-  static_assert(SPL % 4 == 0, "states move to and from the pool four at a time");
-  static constexpr int N = kDiagN, LPC = N / SPL, CH = 256 / LPC;
+  static_assert(SPL % 4 == 0 && NS % SPL == 0, "states move to and from the pool four at a time");
+  static constexpr int N = NS, LPC = N / SPL, CH = 256 / LPC;
 };
 
-// Sum of v over the aligned group of LPC (2 or 4) lanes, on every lane of the group: DPP
-// quad permutations (lane ^ 1, then lane ^ 2) feed the adds directly, with no LDS trip.
+// Sum of v over the aligned group of LPC (2, 4, 8 or 16) lanes, on every lane of the
+// group: DPP quad permutations (lane ^ 1, then lane ^ 2), then rotations by 4 and 8 lanes
+// inside the 16-lane row, feed the adds directly, with no LDS trip.
 template <int LPC>
 __device__ __forceinline__ float group_sum(float v) {
-  static_assert(LPC == 1 || LPC == 2 || LPC == 4, "lanes per channel within a quad");
+  static_assert(LPC == 1 || LPC == 2 || LPC == 4 || LPC == 16, "lanes per channel within a row");
   if constexpr (LPC >= 2)
     v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
   if constexpr (LPC >= 4)
     v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
+  if constexpr (LPC >= 16) {
+    // quad sums q0..q3 of the row: + row_ror:4 gives q_i + q_(i+1), + row_ror:8 the total
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x124, 0xF, 0xF, true));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x128, 0xF, 0xF, true));
+  }
   return v;
 }
 
-template <typename T, int SPL>
+// Workgroups of one sequence: G groups x ceil(H/G / CH) channel blocks, so the channels of
+// a workgroup share one B/C group.
+__host__ __device__ __forceinline__ int diag_blocks_per_group(int H, int G, int CH) {
+  return (H / G + CH - 1) / CH;
+}
+
+// kScalarA: A is [H] (Mamba2 at head_dim 1), else [H, NS] (Mamba1).
+template <typename T, int NS, int SPL, bool kScalarA>
 __global__ __launch_bounds__(256) void k_diag_scan(PrefillParams p) {
-  constexpr int N = kDiagN;    // 16 states per channel
-  constexpr int LPC = DiagCfg<T, SPL>::LPC;   // lanes per channel
-  constexpr int CH = DiagCfg<T, SPL>::CH;     // channels per workgroup
-  constexpr int TT = 32;       // tokens per LDS tile
+  using Cfg = DiagCfg<NS, SPL>;
+  constexpr int N = NS;                // states per channel
+  constexpr int LPC = Cfg::LPC;        // lanes per channel
+  constexpr int CH = Cfg::CH;          // channels per workgroup
+  constexpr int TT = 32;               // tokens per LDS tile
   constexpr int U = SSD_DIAG_UNROLL;   // tokens per step of the scan (divides TT)
+  constexpr int NA = kScalarA ? 1 : SPL;   // decay factors per lane and token
   static_assert(TT % U == 0, "unroll");
   __shared__ __attribute__((aligned(16))) float s_d[TT][CH];
   __shared__ __attribute__((aligned(16))) float s_x[TT][CH];
@@ -62,36 +80,41 @@ __global__ __launch_bounds__(256) void k_diag_scan(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) float s_c[TT][N];
 
   const int tid = threadIdx.x;
-  const int cb = blockIdx.x, r = blockIdx.y;
+  const int r = blockIdx.y;
+  const int H = p.H, HPG = p.H / p.G;
+  const int nb = diag_blocks_per_group(H, p.G, CH);
+  const int g = blockIdx.x / nb, jb = blockIdx.x % nb;
+  const int c0 = g * HPG + jb * CH;               // first channel of the workgroup
+  const int nch = min(CH, HPG - jb * CH);         // channels of the workgroup (all one group)
   const int cl = tid / LPC, ng = tid % LPC;
-  const int H = p.H;
-  const int c = cb * CH + cl;
-  const bool valid = c < H;
+  const int c = c0 + cl;
+  const bool valid = cl < nch;
 
   const int t0 = p.cu_seqlens[r], t1 = p.cu_seqlens[r + 1];
   int k = r == 0 ? 0 : p.last_chunk[r - 1] + 1;
   const int klast = p.last_chunk[r];
+  const bool first_wg = blockIdx.x == 0;
   if (t0 < 0 || t1 > p.T || t1 <= t0 || k < 0 || klast < k || klast >= p.C || p.cu_chunk[k] != t0 ||
       p.cu_chunk[klast + 1] != t1) {
-    if (tid == 0 && cb == 0) raise_flag(p.flag, SSD_DEVERR_CHUNK_RANGE);
+    if (tid == 0 && first_wg) raise_flag(p.flag, SSD_DEVERR_CHUNK_RANGE);
     return;
   }
   int next_end = p.cu_chunk[k + 1];
 
-  float A2[SPL];
+  float A2[NA];
   float h[SPL];
 #pragma unroll
   for (int i = 0; i < SPL; ++i) h[i] = 0.f;
   // pool entries: the initial state (read only with has_initial_state) and the final
   // state (written only with write_final); in the all cache mode the block_idx_last_computed
   // and block_idx_last_scheduled entries, plus one entry per block end below
-  const bool report = tid == 0 && cb == 0;
+  const bool report = tid == 0 && first_wg;
   const SeqSlots ss = seq_slots(p, r, true, true, report);
   const int src = (ss.src >= 0 && p.has_init && p.has_init[r]) ? ss.src : -1;
   const int fin = p.write_final ? ss.fin : -1;
   if (valid) {
 #pragma unroll
-    for (int i = 0; i < SPL; ++i) A2[i] = p.A[c * N + ng * SPL + i] * kLog2e;
+    for (int i = 0; i < NA; ++i) A2[i] = (kScalarA ? p.A[c] : p.A[c * N + ng * SPL + i]) * kLog2e;
     if (src >= 0) {
       const int64_t e = int64_t(src) * p.slot_stride + int64_t(c) * N + ng * SPL;
 #pragma unroll
@@ -102,36 +125,38 @@ __global__ __launch_bounds__(256) void k_diag_scan(PrefillParams p) {
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < SPL; ++i) A2[i] = 0.f;
+    for (int i = 0; i < NA; ++i) A2[i] = 0.f;
   }
   const float Dc = (valid && p.D) ? p.D[c] : 0.f;
 
   const T* xg = static_cast<const T*>(p.x);
   const T* dg = static_cast<const T*>(p.dt);
-  const T* bg = static_cast<const T*>(p.B);
-  const T* cg = static_cast<const T*>(p.Cm);
+  const T* bg = static_cast<const T*>(p.B) + int64_t(g) * N;
+  const T* cg = static_cast<const T*>(p.Cm) + int64_t(g) * N;
   T* yg = static_cast<T*>(p.y);
 
   // A tile's inputs are fetched into registers one tile ahead (raw values; positions past
   // the sequence end read as zero) and written to LDS at the top of the tile's turn.
   constexpr int NE = TT * CH / 256;              // delta / x elements per thread
   constexpr int NBC = TT * 2 * (N / 4);          // B / C float4 items per tile
+  constexpr int NBCI = (NBC + 255) / 256;        // ... per thread
   T rd[NE], rx[NE];
-  float4_v rbc;
+  float4_v rbc[NBCI];
   // Vector path (bf16, 8 channels per thread): thread t owns channels 8*(t % 8) .. +7 of
   // tile row t / 8, moved as one 16-byte access per tensor; it needs whole 8-channel
-  // groups (H % 8 == 0) and 16-byte aligned rows.  Otherwise one element per access.
+  // groups (H/G % 8 == 0) and 16-byte aligned rows.  Otherwise one element per access.
   constexpr bool kVecT = std::is_same<T, bf16_t>::value && NE == 8 && CH == 64;
-  const bool vec = kVecT && H % 8 == 0 && p.x_st % 8 == 0 && p.dt_st % 8 == 0 &&
+  const bool vec = kVecT && HPG % 8 == 0 && p.x_st % 8 == 0 && p.dt_st % 8 == 0 &&
                    p.y_st % 8 == 0 &&
                    ((reinterpret_cast<uintptr_t>(p.x) | reinterpret_cast<uintptr_t>(p.dt) |
                      reinterpret_cast<uintptr_t>(p.y)) & 15) == 0;
-  const int vtt = tid / 8, vc8 = (tid % 8) * 8, vch = cb * CH + vc8;
+  const int vtt = tid / 8, vc8 = (tid % 8) * 8, vch = c0 + vc8;
+  const bool vin = vc8 < nch;
   u32x4_v vd = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
   auto fetch = [&](int tb) {
     const int nt = min(TT, t1 - tb);
     if (vec) {
-      const bool in = vtt < nt && vch < H;
+      const bool in = vtt < nt && vin;
       vd = in ? *reinterpret_cast<const u32x4_v*>(dg + int64_t(tb + vtt) * p.dt_st + vch)
               : u32x4_v{0u, 0u, 0u, 0u};
       vx = in ? *reinterpret_cast<const u32x4_v*>(xg + int64_t(tb + vtt) * p.x_st + vch)
@@ -139,22 +164,24 @@ __global__ __launch_bounds__(256) void k_diag_scan(PrefillParams p) {
     } else {
 #pragma unroll
       for (int u = 0; u < NE; ++u) {
-        const int e = u * 256 + tid, tt = e / CH, ch = cb * CH + e % CH;
-        const bool in = tt < nt && ch < H;
+        const int e = u * 256 + tid, tt = e / CH, cc = e % CH;
+        const bool in = tt < nt && cc < nch;
         const int64_t t = in ? tb + tt : t0;
-        const int chc = in ? ch : 0;
+        const int chc = in ? c0 + cc : 0;
         rd[u] = in ? dg[t * p.dt_st + chc] : T(0);
         rx[u] = in ? xg[t * p.x_st + chc] : T(0);
       }
     }
-    rbc = float4_v{0.f, 0.f, 0.f, 0.f};
-    if (tid < NBC) {
-      const int tt = tid / (2 * (N / 4)), q = tid % (2 * (N / 4));
+#pragma unroll
+    for (int u = 0; u < NBCI; ++u) {
+      const int e = u * 256 + tid;
+      rbc[u] = float4_v{0.f, 0.f, 0.f, 0.f};
+      const int tt = e / (2 * (N / 4)), q = e % (2 * (N / 4));
       const int which = q / (N / 4), n4 = q % (N / 4);
-      if (tt < nt) {
+      if (e < NBC && tt < nt) {
         const T* src = (which ? cg : bg) + int64_t(tb + tt) * p.bc_st + n4 * 4;
-        rbc = float4_v{Elem<T>::load(src), Elem<T>::load(src + 1), Elem<T>::load(src + 2),
-                       Elem<T>::load(src + 3)};
+        rbc[u] = float4_v{Elem<T>::load(src), Elem<T>::load(src + 1), Elem<T>::load(src + 2),
+                          Elem<T>::load(src + 3)};
       }
     }
   };
@@ -162,7 +189,7 @@ __global__ __launch_bounds__(256) void k_diag_scan(PrefillParams p) {
   for (int tb = t0; tb < t1; tb += TT) {
     const int nt = min(TT, t1 - tb);
     if (vec) {
-      const bool in = vtt < nt && vch < H;
+      const bool in = vtt < nt && vin;
       float dv8[8], xv8[8];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -178,16 +205,19 @@ __global__ __launch_bounds__(256) void k_diag_scan(PrefillParams p) {
     } else {
 #pragma unroll
       for (int u = 0; u < NE; ++u) {
-        const int e = u * 256 + tid, tt = e / CH, cc = e % CH, ch = cb * CH + cc;
-        const bool in = tt < nt && ch < H;
-        s_d[tt][cc] = in ? p.prep(to_f32(rd[u]), ch) : 0.f;
+        const int e = u * 256 + tid, tt = e / CH, cc = e % CH;
+        const bool in = tt < nt && cc < nch;
+        s_d[tt][cc] = in ? p.prep(to_f32(rd[u]), c0 + cc) : 0.f;
         s_x[tt][cc] = to_f32(rx[u]);
       }
     }
-    if (tid < NBC) {
-      const int tt = tid / (2 * (N / 4)), q = tid % (2 * (N / 4));
+#pragma unroll
+    for (int u = 0; u < NBCI; ++u) {
+      const int e = u * 256 + tid;
+      const int tt = e / (2 * (N / 4)), q = e % (2 * (N / 4));
       const int which = q / (N / 4), n4 = q % (N / 4);
-      *reinterpret_cast<float4_v*>(which ? &s_c[tt][4 * n4] : &s_b[tt][4 * n4]) = rbc;
+      if (e < NBC)
+        *reinterpret_cast<float4_v*>(which ? &s_c[tt][4 * n4] : &s_b[tt][4 * n4]) = rbc[u];
     }
     __syncthreads();
     if (tb + TT < t1) fetch(tb + TT);
@@ -201,7 +231,7 @@ __global__ __launch_bounds__(256) void k_diag_scan(PrefillParams p) {
     // of U.
     auto steps = [&](int tt, auto ucount) {
       constexpr int V = decltype(ucount)::value;
-      float dv[V], xv[V], a[V][SPL], bb[V][SPL], cc4[V][SPL];
+      float dv[V], xv[V], a[V][NA], bb[V][SPL], cc4[V][SPL];
 #pragma unroll
       for (int u = 0; u < V; ++u) {
         dv[u] = s_d[tt + u][cl];
@@ -210,8 +240,9 @@ __global__ __launch_bounds__(256) void k_diag_scan(PrefillParams p) {
         for (int i = 0; i < SPL; ++i) {
           bb[u][i] = s_b[tt + u][ng * SPL + i];
           cc4[u][i] = s_c[tt + u][ng * SPL + i];
-          a[u][i] = __builtin_amdgcn_exp2f(dv[u] * A2[i]);
         }
+#pragma unroll
+        for (int i = 0; i < NA; ++i) a[u][i] = __builtin_amdgcn_exp2f(dv[u] * A2[i]);
       }
       float acc[V];
 #pragma unroll
@@ -220,7 +251,7 @@ __global__ __launch_bounds__(256) void k_diag_scan(PrefillParams p) {
         acc[u] = 0.f;
 #pragma unroll
         for (int i = 0; i < SPL; ++i) {
-          h[i] = a[u][i] * h[i] + dx * bb[u][i];
+          h[i] = a[u][kScalarA ? 0 : i] * h[i] + dx * bb[u][i];
           acc[u] += cc4[u][i] * h[i];
         }
       }
@@ -243,7 +274,8 @@ __global__ __launch_bounds__(256) void k_diag_scan(PrefillParams p) {
         if (valid && p.states) {   // end of chunk k: checkpoint
           float* dst = p.states + (int64_t(k) * H + c) * N + ng * SPL;
 #pragma unroll
-          for (int i = 0; i < SPL; ++i) dst[i] = h[i];
+          for (int i = 0; i < SPL; i += 4)
+            *reinterpret_cast<float4_v*>(dst + i) = float4_v{h[i], h[i + 1], h[i + 2], h[i + 3]};
         }
         if (valid && p.block_size > 0) {   // the all cache mode: a block ends here
           const int col = block_end_col(p, r, t0, p.cu_chunk[k], next_end, report);
@@ -268,7 +300,7 @@ __global__ __launch_bounds__(256) void k_diag_scan(PrefillParams p) {
     }
     __syncthreads();
     if (vec) {
-      if (vtt < nt && vch < H) {
+      if (vtt < nt && vin) {
         const float4_v a = *reinterpret_cast<const float4_v*>(&s_y[vtt][vc8]);
         const float4_v b = *reinterpret_cast<const float4_v*>(&s_y[vtt][vc8 + 4]);
         *reinterpret_cast<u32x4_v*>(yg + int64_t(tb + vtt) * p.y_st + vch) =
@@ -277,13 +309,13 @@ __global__ __launch_bounds__(256) void k_diag_scan(PrefillParams p) {
       }
     } else {
       for (int e = tid; e < nt * CH; e += 256) {
-        const int tt = e / CH, cc = e % CH, ch = cb * CH + cc;
-        if (ch < H) Elem<T>::store(yg + int64_t(tb + tt) * p.y_st + ch, s_y[tt][cc]);
+        const int tt = e / CH, cc = e % CH;
+        if (cc < nch) Elem<T>::store(yg + int64_t(tb + tt) * p.y_st + c0 + cc, s_y[tt][cc]);
       }
     }
     __syncthreads();
   }
-  if (k != klast + 1 && tid == 0 && cb == 0) raise_flag(p.flag, SSD_DEVERR_CHUNK_RANGE);
+  if (k != klast + 1 && tid == 0 && first_wg) raise_flag(p.flag, SSD_DEVERR_CHUNK_RANGE);
   if (valid && fin >= 0) {
     const int64_t e = int64_t(fin) * p.slot_stride + int64_t(c) * N + ng * SPL;
 #pragma unroll
@@ -292,13 +324,28 @@ __global__ __launch_bounds__(256) void k_diag_scan(PrefillParams p) {
   }
 }
 
-hipError_t launch_diag_prefill(int in_dtype, const PrefillParams& p, hipStream_t s,
+template <typename T, int NS, int SPL, bool kScalarA>
+static void launch_diag(const PrefillParams& p, hipStream_t s) {
+  constexpr int CH = DiagCfg<NS, SPL>::CH;
+  const dim3 grid(p.G * diag_blocks_per_group(p.H, p.G, CH), p.S);
+  hipLaunchKernelGGL((k_diag_scan<T, NS, SPL, kScalarA>), grid, dim3(256), 0, s, p);
+}
+
+template <typename T>
+static hipError_t launch_diag_t(const PrefillParams& p, bool scalar_a, hipStream_t s) {
+  if (!scalar_a && p.N == kDiagN) launch_diag<T, 16, SSD_DIAG_SPL, false>(p, s);
+  else if (scalar_a && p.N == 16) launch_diag<T, 16, 4, true>(p, s);
+  else if (scalar_a && p.N == 128) launch_diag<T, 128, 8, true>(p, s);
+  else return hipErrorInvalidValue;   // the plan admits no other dstate
+  return hipSuccess;
+}
+
+hipError_t launch_diag_prefill(int in_dtype, bool scalar_a, const PrefillParams& p, hipStream_t s,
                                void* const* events) {
-  constexpr int SPL = SSD_DIAG_SPL, CH = DiagCfg<float, SPL>::CH;
-  const dim3 grid((p.H + CH - 1) / CH, p.S);
   record_event(events, 0, s);
-  if (in_dtype == SSD_BF16) hipLaunchKernelGGL((k_diag_scan<bf16_t, SPL>), grid, dim3(256), 0, s, p);
-  else hipLaunchKernelGGL((k_diag_scan<float, SPL>), grid, dim3(256), 0, s, p);
+  const hipError_t e = in_dtype == SSD_BF16 ? launch_diag_t<bf16_t>(p, scalar_a, s)
+                                            : launch_diag_t<float>(p, scalar_a, s);
+  if (e != hipSuccess) return e;
   record_event(events, 1, s);
   return hipGetLastError();
 }

@@ -20,6 +20,8 @@ ssd_status check_vector_access(const ssd_prefill_args* a) {
   if (a->state_pool && (!aligned(a->state_pool, 16) || a->slot_stride % 4))
     return SSD_ERR_UNSUPPORTED;
   if (a->chunk_states_out && !aligned(a->chunk_states_out, 16)) return SSD_ERR_UNSUPPORTED;
+  if (a->chunk_local_states_out && !aligned(a->chunk_local_states_out, 16))
+    return SSD_ERR_UNSUPPORTED;
   return SSD_OK;
 }
 
@@ -97,7 +99,8 @@ ssd_status ssd_prefill(const ssd_prefill_args* a, void* workspace, size_t worksp
     return SSD_ERR_HIP;
   const hipError_t e = plan.kind == ssd::PrefillKind::kChunked
                            ? ssd::launch_chunked_prefill(plan.variant, p, s, a->profile_events)
-                           : ssd::launch_diag_prefill(a->in_dtype, p, s, a->profile_events);
+                           : ssd::launch_diag_prefill(a->in_dtype, a->a_kind == SSD_A_SCALAR, p,
+                                                      s, a->profile_events);
   return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
 }
 

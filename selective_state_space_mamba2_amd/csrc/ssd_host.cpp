@@ -15,6 +15,9 @@ const ChunkedShape kChunkedShapes[] = {
     {SSD_BF16, 64, 128, 256}, {SSD_BF16, 64, 128, 128}, {SSD_BF16, 64, 128, 64},
     {SSD_BF16, 16, 16, 64},   {SSD_F32, 16, 16, 64},    {SSD_F32, 64, 128, 64},
     {SSD_BF16, 16, 16, 256},  {SSD_F32, 16, 16, 256},   {SSD_F32, 64, 128, 256},
+    {SSD_BF16, 16, 128, 64},  {SSD_BF16, 16, 128, 256}, {SSD_BF16, 64, 16, 64},
+    {SSD_BF16, 64, 16, 256},  {SSD_F32, 16, 128, 64},   {SSD_F32, 16, 128, 256},
+    {SSD_F32, 64, 16, 64},    {SSD_F32, 64, 16, 256},
 };
 const int kNumChunkedShapes = sizeof(kChunkedShapes) / sizeof(kChunkedShapes[0]);
 
@@ -72,6 +75,16 @@ ssd_status plan_prefill(const ssd_prefill_args* a, PrefillPlan* plan) {
   if (a->a_kind == SSD_A_DIAG) {
     if (a->P != 1 || a->G != 1) return SSD_ERR_BAD_SHAPE;
     if (a->N != kDiagN) return SSD_ERR_UNSUPPORTED;
+    if (a->dA_cumsum_out || a->cb_out || a->chunk_local_states_out) return SSD_ERR_UNSUPPORTED;
+    plan->kind = PrefillKind::kDiag;
+    plan->ws_bytes = 0;
+    return SSD_OK;
+  }
+
+  if (a->P == 1) {
+    // head_dim 1: the sequential scan with A[h] on every state (the MFMA form would contract
+    // over one column); any chunk size, the per-step debug outputs are not produced
+    if (!scalar_p1_supports_n(a->N)) return SSD_ERR_UNSUPPORTED;
     if (a->dA_cumsum_out || a->cb_out || a->chunk_local_states_out) return SSD_ERR_UNSUPPORTED;
     plan->kind = PrefillKind::kDiag;
     plan->ws_bytes = 0;

@@ -131,7 +131,9 @@ struct DecodeParams {
 // last one (the timing hook of the C ABI).
 hipError_t launch_chunked_prefill(int variant, const PrefillParams& p, hipStream_t s,
                                   void* const* events);
-hipError_t launch_diag_prefill(int in_dtype, const PrefillParams& p, hipStream_t s,
+// The sequential scan of a one-element head: scalar_a selects A [H] (head_dim 1) over the
+// per-(channel, state) A [H, N].
+hipError_t launch_diag_prefill(int in_dtype, bool scalar_a, const PrefillParams& p, hipStream_t s,
                                void* const* events);
 hipError_t launch_state_update(int in_dtype, const DecodeParams& p, hipStream_t s,
                                void* const* events);

@@ -10,6 +10,7 @@
 namespace ssd {
 
 // Which prefill implementation runs.
+// kDiag: the sequential scan of a one-element head (SSD_A_DIAG, or SSD_A_SCALAR with P == 1).
 enum class PrefillKind { kNone = 0, kChunked = 1, kDiag = 2 };
 
 // Workspace carve-up of one prefill call (byte offsets into the caller's workspace).
@@ -33,14 +34,15 @@ struct PrefillPlan {
                              // end state, -1 for none (0 bytes when the mode is off)
 };
 
-// Shapes that run the chunk-chain kernel (bf16, head dim 64, dstate and chunk size
-// multiples of 128); the others run the march kernel.
-constexpr bool chain_supported(int dtype, int P, int N, int CS) {
-  return dtype == SSD_BF16 && P == 64 && N % 128 == 0 && CS % 128 == 0;
-}
 // Wavefronts per chunk-chain workgroup; each publishes its share of the state under a
 // flag of its own, so there are kChainWaves flags per (chunk, head).
 constexpr int kChainWaves = 4;
+// Shapes that run the chunk-chain kernel (bf16, head dim 64, dstate and chunk size
+// multiples of 128, at most one token per thread of the workgroup); the others run the
+// march kernel.
+constexpr bool chain_supported(int dtype, int P, int N, int CS) {
+  return dtype == SSD_BF16 && P == 64 && N % 128 == 0 && CS % 128 == 0 && CS <= 64 * kChainWaves;
+}
 
 // C.B^T fragments of the 16-row tiles 0..i-1 of a chunk: tile i needs the 32-token blocks
 // 0..i/2 (one fragment each).
@@ -78,8 +80,10 @@ constexpr int kDecodeMaxTokens = 16;
 constexpr int kDecodeMaxStateElems = 16384;   // P * N per head
 bool decode_supports_n(int N);
 
-// Diagonal (Mamba1) scan: the one instantiated dstate.
+// Diagonal (Mamba1) scan: the one instantiated dstate.  The same sequential scan runs
+// the scalar-A recurrence at head_dim 1 with these dstates:
 constexpr int kDiagN = 16;
+constexpr bool scalar_p1_supports_n(int N) { return N == 16 || N == 128; }
 
 ssd_status plan_prefill(const ssd_prefill_args* a, PrefillPlan* plan);
 ssd_status check_decode(const ssd_decode_args* a);

@@ -1003,8 +1003,8 @@ void k_chunk_march(PrefillParams p) {
 //
 // Hand-off: each wave publishes its columns of H_k under a flag of its own (the successor's
 // wave w reads exactly those columns), so the chain needs no workgroup barrier.  The
-// checkpoint stores and the successor's loads use the device-coherent cache policy (see
-// kCohDev); the publisher waits for its stores to complete, then sets the flag.
+// publisher waits for its state stores to complete, then sets the flag; the cache policy of
+// the stores and of the successor's loads is chosen as described at kCohDev.
 //
 // Dispatch order: rows of the grid are chunks in the order of k_chunk_prep's chunk_ord (by
 // position inside the sequence, then sequences longest first), so a workgroup's
@@ -1035,6 +1035,8 @@ struct ChainCfg {
   static constexpr int NG = P / 8, NITEM = NG * CS / 4, NI = NITEM / NTH;
   static constexpr int NF = cb_frag_base(NT);
   static_assert(TN % NW == 0 && N % 32 == 0 && NT % NW == 0 && NITEM % NTH == 0, "shape");
+  // delta and the cumsum are formed for one token per thread (token 64 * wave + lane)
+  static_assert(CS <= 64 * NW, "one token per thread");
 };
 
 // The chunk's x rows.  Work item `it`: columns 8*g8 .. 8*g8+7, tokens 4*sg .. 4*sg+3.
@@ -1060,16 +1062,25 @@ __device__ __forceinline__ void chain_load_x(Frag8 (&x)[NI][4], const PrefillPar
 
 constexpr long long kChainWaitTicks = 100000000;   // ~1 s of the 100 MHz wall clock
 // Cache policies of the published-state accesses.  Device-scope coherent (sc1) is the
-// policy of device-scope relaxed atomics: a store with it is performed for every CU once it
-// completes, and a load with it observes such stores.  Within one XCD the L2 is shared, so
-// there a plain store (complete once it is in L2) and an L1-bypassing load (sc0) suffice
-// and keep the state in L2.  The publisher picks the L2 form only when it runs on the XCD
-// its workgroup id maps to (id mod 8, where a successor's id also maps), and records its
-// XCD and the form in the flag value; a successor on that same XCD reads through L2, any
-// other reads device-coherent, and a state left in another XCD's L2 is reported
-// (SSD_DEVERR_CHAIN_WAIT).  Neither side needs a cache flush or invalidate: the publisher
-// waits for its stores to complete before the flag store, the successor issues its loads
-// after it has seen the flag.
+// policy of device-scope relaxed atomics (the flags themselves use it): a store with it is
+// performed for every CU once it completes, and a load with it observes such stores, in
+// whichever L1 or L2 an older copy of the line may sit.
+// Within one XCD the L2 is shared, so a plain store (complete once it is in L2) followed by
+// a workgroup-scope load (sc0) also works, and keeps the state in L2, provided no L1 of the
+// XCD can hold an older copy of the line.  A workgroup-scope load may be served by the
+// CU's L1, so that form is used only when the state goes to the checkpoint output, whose
+// rows are written once and read once per launch: their lines cannot be in any L1 before
+// the successor reads them (L1s start each launch invalidated).  The two-deep workspace
+// ring reuses its entries within a launch (chunk j+3 reads the entry chunk j+1 read, on
+// the same XCD), and an all-cache-mode pool entry may be the one the sequence's first
+// chunk read its initial state from, so both always go device-coherent.
+// The publisher picks the L2 form only for the checkpoint output, and only when
+// it runs on the XCD its workgroup id maps to (id mod 8, where a successor's id also
+// maps); it records its XCD and the form in the flag value.  A successor reads through L2
+// only when the flag says the L2 form on its own XCD, device-coherent otherwise, and a
+// state left in another XCD's L2 is reported (SSD_DEVERR_CHAIN_WAIT).  Neither side needs
+// a cache flush or invalidate: the publisher waits for its stores to complete before the
+// flag store, the successor issues its loads after it has seen the flag.
 constexpr int kCohDev = 16;
 constexpr int kCohWg = 1;
 constexpr int kFlagLocal = 16;   // flag value - 1 = XCD id | kFlagLocal when kept in L2
@@ -1308,7 +1319,7 @@ void k_chunk_chain(PrefillParams p) {
     }
     asm volatile("" ::: "memory");
     const int e = __builtin_amdgcn_readfirstlane(fv) - 1;
-    via_l2 = (e & 15) == my_xcd;
+    via_l2 = (e & kFlagLocal) && (e & 15) == my_xcd;
     if (!via_l2 && (e & kFlagLocal) && lane == 0) raise_flag(p.flag, SSD_DEVERR_CHAIN_WAIT);
     hin = chain_state(p, k - 1, h, r, k - 1 - k0);
   }
@@ -1369,7 +1380,8 @@ void k_chunk_chain(PrefillParams p) {
     const BufRes hb(chain_state(p, k, h, r, k - k0));
 
     // kept in this XCD's L2 when the successor maps here too (the last chunk has none)
-    const bool keep_l2 = !last && my_xcd == int(blockIdx.x % kXcds);
+    // and the state goes to the checkpoint output (no line of it can sit in an L1)
+    const bool keep_l2 = !last && p.states && my_xcd == int(blockIdx.x % kXcds);
     f32x4_v hn[TNW][TP];
 #pragma unroll
     for (int q = 0; q < TNW; ++q)
@@ -1523,6 +1535,10 @@ static const RunFn kRun[] = {
     run_chunked<float, 16, 16, 64>,    run_chunked<float, 64, 128, 64>,
     run_chunked<bf16_t, 16, 16, 256>,  run_chunked<float, 16, 16, 256>,
     run_chunked<float, 64, 128, 256>,
+    run_chunked<bf16_t, 16, 128, 64>,  run_chunked<bf16_t, 16, 128, 256>,
+    run_chunked<bf16_t, 64, 16, 64>,   run_chunked<bf16_t, 64, 16, 256>,
+    run_chunked<float, 16, 128, 64>,   run_chunked<float, 16, 128, 256>,
+    run_chunked<float, 64, 16, 64>,    run_chunked<float, 64, 16, 256>,
 };
 
 hipError_t launch_chunked_prefill(int variant, const PrefillParams& p, hipStream_t s,

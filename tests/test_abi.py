@@ -13,13 +13,16 @@ from selective_state_space_mamba2_amd import _abi
 from selective_state_space_mamba2_amd._abi import DecodeArgs, PrefillArgs, lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "ssd.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(ssd_[a-z0-9_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names.update(re.findall(r"\b(ssd_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_every_declared_function_is_exported():
@@ -245,6 +248,27 @@ def test_diag_host_checks():
     assert _ws(_good_prefill(**base, dA_cumsum_out=FAKE))[0] == _abi.SSD_ERR_UNSUPPORTED
 
 
+@pytest.mark.parametrize("in_dtype", [_abi.SSD_BF16, _abi.SSD_F32])
+@pytest.mark.parametrize("P", [1, 16, 64])
+@pytest.mark.parametrize("N", [16, 128])
+@pytest.mark.parametrize("cs", [64, 256])
+def test_minimum_instantiation_set_plans(in_dtype, P, N, cs):
+    """Every (dtype, head_dim, dstate, chunk_size) of the minimum instantiation set has a
+    kernel: head_dim 1 runs the sequential scan, the others the chunked kernels."""
+    H, G = 8, 2
+    a = _good_prefill(in_dtype=in_dtype, H=H, P=P, G=G, N=N, chunk_size=cs, x_stride_t=H * P,
+                      y_stride_t=H * P, dt_stride_t=H, bc_stride_t=G * N)
+    st, need = _ws(a)
+    assert st == 0, (in_dtype, P, N, cs, st)
+    n = ctypes.c_int32(-1)
+    names = (ctypes.c_char_p * _abi.SSD_PREFILL_MAX_KERNELS)()
+    assert lib().ssd_prefill_kernel_count(ctypes.byref(a), ctypes.byref(n), names) == 0
+    if P == 1:
+        assert need == 0 and n.value == 1 and names[0] == b"k_diag_scan"
+    else:
+        assert n.value == 2 and names[0] == b"k_chunk_prep"
+
+
 def _good_decode(**over):
     a = DecodeArgs()
     a.B_pad, a.ntok, a.H, a.P, a.G, a.N = 8, 4, 48, 64, 4, 128
@@ -359,3 +383,13 @@ def _good_conv_update(**over):
 ])
 def test_conv1d_update_host_checks(over, status):
     assert lib().ssd_conv1d_update(ctypes.byref(_good_conv_update(**over)), None) == status
+
+
+def test_probe_stream_host_checks():
+    f = lib().ssd_probe_stream
+    assert f(FAKE, 16, FAKE, 16, None, None) == _abi.SSD_ERR_NULL_POINTER      # no sink
+    assert f(None, 16, FAKE, 0, FAKE, None) == _abi.SSD_ERR_NULL_POINTER
+    assert f(FAKE, 15, FAKE, 16, FAKE, None) == _abi.SSD_ERR_BAD_SHAPE
+    assert f(FAKE + 4, 16, FAKE, 16, FAKE, None) == _abi.SSD_ERR_UNSUPPORTED
+    assert f(FAKE, (1 << 35) + 16, FAKE, 0, FAKE, None) == _abi.SSD_ERR_BAD_SHAPE
+    assert f(None, 0, None, 0, FAKE, None) == 0                               # nothing to move

@@ -26,11 +26,12 @@ def test_bench_prints_one_json_line_with_the_contract_keys():
         assert k in d, k
     assert d["n_gpus"] == 1 and d["steps"] == 4 and d["warmup"] == 2
     assert d["unit"] == "tokens/s" and d["value"] > 0 and d["higher_is_better"] is True
-    assert d["config"]["workload"] == "mamba2_2.7b_prefill"
+    assert d["config"]["workload"] == "nemotron_h_prefix_cache"
     r = d["roofline"]
     assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
     assert 0 < r["frac"] < 1 and abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-3
     assert d["graph"]["ms_per_step"] > 0
+    assert r["read_frac"] > 0 and "traffic_source" in r
 
 
 def test_bench_refuses_more_than_one_gpu():

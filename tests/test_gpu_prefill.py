@@ -23,7 +23,15 @@ def _case(seed, in_dtype, P, N, cs, lengths, nc, H=8, G=2, init="pool", slots=16
 
 VARIANTS = [("bf16", 64, 128, 256), ("bf16", 64, 128, 128), ("bf16", 64, 128, 64),
             ("bf16", 16, 16, 64), ("f32", 16, 16, 64), ("f32", 64, 128, 64),
-            ("bf16", 16, 16, 256), ("f32", 16, 16, 256), ("f32", 64, 128, 256)]
+            ("bf16", 16, 16, 256), ("f32", 16, 16, 256), ("f32", 64, 128, 256),
+            # the rest of the minimum instantiation set: head_dim 16 with dstate 128, head_dim
+            # 64 with dstate 16 (chunked kernels), head_dim 1 (the sequential scan)
+            ("bf16", 16, 128, 64), ("bf16", 16, 128, 256), ("bf16", 64, 16, 64),
+            ("bf16", 64, 16, 256), ("f32", 16, 128, 64), ("f32", 16, 128, 256),
+            ("f32", 64, 16, 64), ("f32", 64, 16, 256),
+            ("bf16", 1, 16, 64), ("bf16", 1, 16, 256), ("bf16", 1, 128, 64),
+            ("bf16", 1, 128, 256), ("f32", 1, 16, 64), ("f32", 1, 16, 256),
+            ("f32", 1, 128, 64), ("f32", 1, 128, 256)]
 
 
 @pytest.mark.parametrize("dtype,P,N,cs", VARIANTS)
@@ -76,6 +84,21 @@ def test_long_memory_and_zero_decay(dtype):
     check_prefill(inp, run_prefill(inp), oracle_prefill(inp))
     inp0 = _case(10, dtype, 64, 128, 64, [500], [0], A_zero=True, init="none")
     check_prefill(inp0, run_prefill(inp0), oracle_prefill(inp0))
+
+
+@pytest.mark.parametrize("dtype,N", [("bf16", 128), ("f32", 16)])
+def test_head_dim_one(dtype, N):
+    """head_dim 1 (the sequential scan with A per head): heads whose group spans several
+    workgroups (80 heads, 2 groups), long memory and A = 0, softplus with bias and limit."""
+    inp = _case(21, dtype, 1, N, 64, [300, 1, 130], [0, 63, 5], H=80, G=2, slots=8,
+                A_range=(1e-3, 1e-2))
+    check_prefill(inp, run_prefill(inp), oracle_prefill(inp))
+    inp0 = _case(22, dtype, 1, N, 256, [500], [0], H=8, G=4, A_zero=True, init="none")
+    check_prefill(inp0, run_prefill(inp0), oracle_prefill(inp0))
+    bias = np.linspace(-1.5, 0.5, 80).astype(np.float32).astype(np.float64)
+    got = run_prefill(inp, dt_bias=bias, softplus=True, dt_limit=(0.01, 0.5), write_final=False)
+    ref = oracle_prefill(inp, dt_bias=bias, softplus=True, dt_limit=(0.01, 0.5))
+    check_prefill(inp, got, ref, check_pool=False)
 
 
 def test_dt_zero_keeps_the_state():
@@ -240,6 +263,27 @@ def test_out_of_range_slot_raises_the_device_flag():
     ref = oracle_prefill(inp, seqs=[0, 1])
     check_prefill(inp, got, {0: ref[0]})
     assert_close(got["y"][100:150], ref[1]["y"], TOL["bf16"], "y of the flagged sequence")
+
+
+def test_default_error_word_keeps_device_errors():
+    """A call given no device_error_flag reports into the GPU's persistent error word,
+    which check_device_errors turns into an exception (and clears)."""
+    from gpu_helpers import dev_f32, dev_i32, dev_token, prefill_metadata
+    from selective_state_space_mamba2_amd import api
+    inp = _case(16, "bf16", 64, 128, 256, [100, 50], [0, 0])
+    inp.state_indices[1] = inp.pool.shape[0]          # outside [0, num_slots)
+    api.ssd_device_errors()                           # start from a clear word
+    cuc, sidx, last = prefill_metadata(inp)
+    import torch
+    pool = torch.from_numpy(inp.pool).cuda()
+    api.ssd_prefill(*(dev_token(inp, n) for n in ("x", "dt")), dev_f32(inp.A),
+                    *(dev_token(inp, n) for n in ("B", "C")), inp.chunk_size,
+                    dev_i32(inp.cu_seqlens), dev_i32(cuc), dev_i32(sidx), dev_i32(last),
+                    state_pool=pool, state_indices=dev_i32(inp.state_indices),
+                    has_initial_state=dev_i32(inp.has_initial_state), write_final_to_pool=True)
+    with pytest.raises(RuntimeError, match="SLOT_RANGE"):
+        api.check_device_errors()
+    assert api.ssd_device_errors() == 0               # cleared by the check
 
 
 # ----------------------------------------------------------------------------------------
