@@ -393,3 +393,4 @@ def test_probe_stream_host_checks():
     assert f(FAKE + 4, 16, FAKE, 16, FAKE, None) == _abi.SSD_ERR_UNSUPPORTED
     assert f(FAKE, (1 << 35) + 16, FAKE, 0, FAKE, None) == _abi.SSD_ERR_BAD_SHAPE
     assert f(None, 0, None, 0, FAKE, None) == 0                               # nothing to move
+
