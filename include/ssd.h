@@ -270,6 +270,21 @@ ssd_status ssd_prefill_workspace_size(const ssd_prefill_args* args, size_t* byte
 ssd_status ssd_prefill(const ssd_prefill_args* args, void* workspace,
                        size_t workspace_bytes, ssd_stream_t stream);
 
+/* Allocation-free variant of ssd_prefill, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * same kernels run with their workspace in a static device array of
+ * SSD_NOALLOC_SCRATCH_BYTES (256 MiB) that the library holds on every GPU it runs on until
+ * the process ends; the call itself allocates and frees nothing.  The caller still passes
+ * every input and output.  Every ssd_prefill_noalloc call on one GPU shares that GPU's
+ * array: calls that overlap in time on one GPU (different streams, or host threads) race
+ * and give undefined results; calls in stream order are safe (each call's kernels set up
+ * everything they read from the array, nothing needs clearing in between).
+ * Errors: as ssd_prefill, plus SSD_ERR_WORKSPACE when the workspace these arguments need
+ * (ssd_prefill_workspace_size) exceeds SSD_NOALLOC_SCRATCH_BYTES, and SSD_ERR_HIP when the
+ * array's device address cannot be obtained. */
+#define SSD_NOALLOC_SCRATCH_BYTES (256u << 20)
+ssd_status ssd_prefill_noalloc(const ssd_prefill_args* args, ssd_stream_t stream);
+
 /* ---------------------------------------------------------------------------------------
  * Decode state update
  *

@@ -62,6 +62,7 @@ class PrefillArgs(ctypes.Structure):
 
 
 SSD_PREFILL_MAX_KERNELS = 2
+SSD_NOALLOC_SCRATCH_BYTES = 256 << 20
 
 
 class DecodeArgs(ctypes.Structure):
@@ -116,6 +117,7 @@ EXPORTS = {
     "ssd_prefill_workspace_size": (ctypes.c_int, [ctypes.POINTER(PrefillArgs),
                                                   ctypes.POINTER(ctypes.c_size_t)]),
     "ssd_prefill": (ctypes.c_int, [ctypes.POINTER(PrefillArgs), _vp, ctypes.c_size_t, _vp]),
+    "ssd_prefill_noalloc": (ctypes.c_int, [ctypes.POINTER(PrefillArgs), _vp]),
     "ssd_prefill_kernel_count": (ctypes.c_int, [ctypes.POINTER(PrefillArgs),
                                                 ctypes.POINTER(ctypes.c_int32),
                                                 ctypes.POINTER(ctypes.c_char_p)]),

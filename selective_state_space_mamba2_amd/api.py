@@ -31,7 +31,7 @@ __all__ = [
     "ssd_abi_version", "ssd_status_string", "ssd_chunk_metadata_count",
     "ssd_build_chunk_metadata", "ssd_prefill_workspace_size", "ssd_prefill",
     "ssd_state_update", "prefill_args", "ssd_conv1d_prefill", "ssd_conv1d_update",
-    "ssd_device_errors", "check_device_errors", "device_error_names",
+    "ssd_device_errors", "check_device_errors", "device_error_names", "ssd_prefill_noalloc",
 ]
 
 
@@ -322,6 +322,18 @@ def ssd_prefill(x, dt, A, B, C, chunk_size: int, cu_seqlens, cu_chunk_seqlens, s
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     check("ssd_prefill", lib().ssd_prefill(ctypes.byref(args), ws_ptr, ws_bytes,
                                            _stream_ptr(stream)))
+    return y
+
+
+def ssd_prefill_noalloc(x, dt, A, B, C, chunk_size: int, cu_seqlens, cu_chunk_seqlens, seq_idx,
+                        last_chunk_indices, y, stream=None, **kw):
+    """The prefill with its workspace in the library's static per-GPU array: this call and
+    the library allocate nothing (``y`` and every other tensor come from the caller).
+    Calls that overlap on one GPU race (see include/ssd.h).  Returns y."""
+    args = prefill_args(x, dt, A, B, C, chunk_size, cu_seqlens, cu_chunk_seqlens, seq_idx,
+                        last_chunk_indices, y, **kw)
+    check("ssd_prefill_noalloc", lib().ssd_prefill_noalloc(ctypes.byref(args),
+                                                           _stream_ptr(stream)))
     return y
 
 

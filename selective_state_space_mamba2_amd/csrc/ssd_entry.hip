@@ -1,10 +1,32 @@
 // ssd_entry.hip -- C-ABI entry points that launch kernels: argument resolution, the
 // device-facing checks (alignment of vector accesses, workspace), and the launch sequence.
+#include <atomic>
 #include <cstdint>
 
 #include "ssd_params.h"
 
+// The workspace of ssd_prefill_noalloc: one copy per GPU, in the code object's device
+// memory, shared by every such call on that GPU (see include/ssd.h).
+static __device__ __align__(256) unsigned char scratch[SSD_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+// Device address of this GPU's `scratch` (the host-side name is only a stand-in), looked
+// up once per device with that device current and kept; NULL if the lookup failed.
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    // racing first calls on one device both find the same address
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+  }
+  return ptr;
+}
 
 bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
 
@@ -38,15 +60,15 @@ ssd_status ssd_prefill_workspace_size(const ssd_prefill_args* a, size_t* bytes) 
   return SSD_OK;
 }
 
-ssd_status ssd_prefill(const ssd_prefill_args* a, void* workspace, size_t workspace_bytes,
-                       ssd_stream_t stream) {
-  ssd::PrefillPlan plan;
-  ssd_status st = ssd::plan_prefill(a, &plan);
-  if (st != SSD_OK) return st;
-  if (a->num_seqs == 0) return SSD_OK;
-  if (plan.ws_bytes > 0 &&
-      (!workspace || workspace_bytes < plan.ws_bytes || !aligned(workspace, 256)))
-    return SSD_ERR_WORKSPACE;
+}  // extern "C"
+
+namespace {
+
+// ssd_prefill after planning and the workspace check: the device-facing checks, argument
+// resolution and the launches.
+ssd_status prefill_launch(const ssd_prefill_args* a, const ssd::PrefillPlan& plan, void* workspace,
+                          ssd_stream_t stream) {
+  ssd_status st = SSD_OK;
   if (plan.kind == ssd::PrefillKind::kChunked) {
     st = check_vector_access(a);
     if (st != SSD_OK) return st;
@@ -102,6 +124,36 @@ ssd_status ssd_prefill(const ssd_prefill_args* a, void* workspace, size_t worksp
                            : ssd::launch_diag_prefill(a->in_dtype, a->a_kind == SSD_A_SCALAR, p,
                                                       s, a->profile_events);
   return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+ssd_status ssd_prefill(const ssd_prefill_args* a, void* workspace, size_t workspace_bytes,
+                       ssd_stream_t stream) {
+  ssd::PrefillPlan plan;
+  const ssd_status st = ssd::plan_prefill(a, &plan);
+  if (st != SSD_OK) return st;
+  if (a->num_seqs == 0) return SSD_OK;
+  if (plan.ws_bytes > 0 &&
+      (!workspace || workspace_bytes < plan.ws_bytes || !aligned(workspace, 256)))
+    return SSD_ERR_WORKSPACE;
+  return prefill_launch(a, plan, workspace, stream);
+}
+
+ssd_status ssd_prefill_noalloc(const ssd_prefill_args* a, ssd_stream_t stream) {
+  ssd::PrefillPlan plan;
+  const ssd_status st = ssd::plan_prefill(a, &plan);
+  if (st != SSD_OK) return st;
+  if (a->num_seqs == 0) return SSD_OK;
+  if (plan.ws_bytes > SSD_NOALLOC_SCRATCH_BYTES) return SSD_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (plan.ws_bytes > 0) {
+    ws = scratch_ptr();
+    if (!ws) return SSD_ERR_HIP;
+  }
+  return prefill_launch(a, plan, ws, stream);
 }
 
 ssd_status ssd_prefill_kernel_count(const ssd_prefill_args* a, int32_t* count,

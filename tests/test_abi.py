@@ -394,3 +394,17 @@ def test_probe_stream_host_checks():
     assert f(FAKE, (1 << 35) + 16, FAKE, 0, FAKE, None) == _abi.SSD_ERR_BAD_SHAPE
     assert f(None, 0, None, 0, FAKE, None) == 0                               # nothing to move
 
+
+def test_prefill_noalloc_host_checks():
+    """The allocation-free prefill returns the same host-check statuses as ssd_prefill, and
+    SSD_ERR_WORKSPACE when the workspace needed exceeds the static array (before any device
+    call)."""
+    f = lib().ssd_prefill_noalloc
+    assert f(None, None) == _abi.SSD_ERR_NULL_POINTER
+    assert f(ctypes.byref(_good_prefill(P=32)), None) == _abi.SSD_ERR_UNSUPPORTED
+    assert f(ctypes.byref(_good_prefill(x=None)), None) == _abi.SSD_ERR_NULL_POINTER
+    big = _good_prefill(T=1 << 19, num_chunks=2048)
+    st, need = _ws(big)
+    assert st == 0 and need > _abi.SSD_NOALLOC_SCRATCH_BYTES
+    assert f(ctypes.byref(big), None) == _abi.SSD_ERR_WORKSPACE
+    assert f(ctypes.byref(_good_prefill(T=0, num_seqs=0, num_chunks=0)), None) == 0
