@@ -111,7 +111,8 @@ ssd_status prefill_launch(const ssd_prefill_args* a, const ssd::PrefillPlan& pla
     p.blk_slot = a->block_size > 0 ? reinterpret_cast<int*>(ws + plan.off_blk) : nullptr;
     if (plan.chain) {
       p.chain_flag = reinterpret_cast<int*>(ws + plan.off_flag);
-      p.chunk_ord = reinterpret_cast<int*>(ws + plan.off_cord);
+      p.items = plan.off_items ? reinterpret_cast<int*>(ws + plan.off_items) : nullptr;
+      p.chain_grid = plan.chain_grid;
       p.hring = a->chunk_states_out ? nullptr : reinterpret_cast<float*>(ws + plan.off_ring);
     }
   }

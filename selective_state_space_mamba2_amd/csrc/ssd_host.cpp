@@ -123,8 +123,16 @@ ssd_status plan_prefill(const ssd_prefill_args* a, PrefillPlan* plan) {
   if (plan->chain) {
     plan->off_flag = off;
     off = align_up(off + size_t(C) * a->H * kChainWaves * sizeof(int32_t), 256);
-    plan->off_cord = off;
-    off = align_up(off + size_t(C) * sizeof(int32_t), 256);
+    // the work-item table: C * H items, each XCD's run at most total / 8 + one chain of
+    // at most C - S + 1 chunks (rounding: + 1), padded to 8 per row
+    if (chain_ordered(a->num_seqs, C, a->H)) {
+      plan->chain_grid = int(C * a->H + kXcds * (C - a->num_seqs + 2));
+      plan->off_items = off;
+      off = align_up(off + size_t(plan->chain_grid) * sizeof(int32_t), 256);
+    } else {
+      plan->chain_grid = int(C * kXcds * ((a->H + kXcds - 1) / kXcds));
+      plan->off_items = 0;
+    }
     plan->off_ring = off;
     if (!a->chunk_states_out)
       off = align_up(off + size_t(a->num_seqs) * a->H * 2 * size_t(state / a->H) * sizeof(float), 256);

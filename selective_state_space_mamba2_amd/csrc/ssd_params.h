@@ -42,7 +42,9 @@ struct PrefillParams {
   void* cfw;           // workspace, input dtype: C fragments per chunk and group
   int* seq_ord;        // workspace [S]: sequences in march dispatch order
   int* chain_flag;     // workspace [C, H, kChainWaves]: chain publication flags (NULL: march)
-  int* chunk_ord;      // workspace [C]: chunks in chain dispatch order
+  int* items;          // workspace [chain_grid]: the chain kernel's (chunk * H + head) per
+                       // workgroup, -1 for none (NULL: chunks in index order)
+  int chain_grid;      // workgroups of the chain kernel
   float* hring;        // workspace [S, H, 2, P, N] when states is NULL: published states
   int* blk_slot;       // workspace [C], all cache mode: pool slot of each chunk's end state
                        // (-1: none), set by k_chunk_prep; NULL when the mode is off

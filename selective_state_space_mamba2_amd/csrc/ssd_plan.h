@@ -27,7 +27,9 @@ struct PrefillPlan {
   size_t off_ord = 0;        // int32 [S]: sequence dispatch order of the march kernel
   bool chain = false;        // the chunk-chain kernel runs (else a march kernel)
   size_t off_flag = 0;       // int32 [C, H, kChainWaves]: chain publication flags
-  size_t off_cord = 0;       // int32 [C]: chain dispatch order of the chunks
+  size_t off_items = 0;      // int32 [chain_grid]: the chain kernel's work items (0 bytes
+                             // when the batch is too large to order)
+  int chain_grid = 0;        // workgroups of the chain kernel
   size_t off_ring = 0;       // fp32 [S, H, 2, P, N]: published states when no chunk-state
                              // output is given (0 bytes otherwise)
   size_t off_blk = 0;        // int32 [C]: the all cache mode's pool slot for every chunk's
@@ -37,6 +39,13 @@ struct PrefillPlan {
 // Wavefronts per chunk-chain workgroup; each publishes its share of the state under a
 // flag of its own, so there are kChainWaves flags per (chunk, head).
 constexpr int kChainWaves = 4;
+// The prep kernel orders the chain's work items (one workgroup, with every sequence and
+// chunk in LDS, so the batch is bounded); larger batches run the chunks in index order.
+constexpr int kChainOrderMaxSeqs = 1024;
+constexpr int kChainOrderMaxChunks = 6144;
+constexpr bool chain_ordered(int64_t S, int64_t C, int64_t H) {
+  return S <= kChainOrderMaxSeqs && C <= kChainOrderMaxChunks && C * H <= (int64_t(1) << 22);
+}
 // Shapes that run the chunk-chain kernel (bf16, head dim 64, dstate and chunk size
 // multiples of 128, at most one token per thread of the workgroup); the others run the
 // march kernel.

@@ -224,14 +224,7 @@ __device__ __forceinline__ int xsw(int p, int s) { return s ^ (((p >> 3) & 3) <<
 // starts at once and shorter sequences fill the remaining slots.  The order is computed by
 // one workgroup of k_chunk_prep (a rank count over at most kOrderMaxSeqs sequences;
 // larger batches keep the given order).  `nch` is kOrderMaxSeqs ints of LDS.
-constexpr int kOrderMaxSeqs = 1024;
-
-// Whether k_chunk_prep writes the chain kernel's chunk order (a count over all sequences
-// per chunk, so it is bounded); otherwise the chain kernel takes chunks in index order,
-// which also puts every predecessor first.
-__device__ __forceinline__ bool chain_ordered(const PrefillParams& p) {
-  return p.S <= kOrderMaxSeqs && int64_t(p.S) * p.C <= (int64_t(1) << 20);
-}
+constexpr int kOrderMaxSeqs = kChainOrderMaxSeqs;
 
 __device__ __forceinline__ void sequence_order(const PrefillParams& p, int* nch, int* rank_of) {
   const int S = p.S;
@@ -253,23 +246,111 @@ __device__ __forceinline__ void sequence_order(const PrefillParams& p, int* nch,
   __syncthreads();
 }
 
-// The chain kernel's row order: chunk j of sequence r (ranked q longest first) goes to row
-// sum_r' min(nch_r', j) + q, i.e. by position inside the sequence, then by rank.  The
-// sequences with more than j chunks are exactly ranks 0 .. cnt_j - 1, so rows are dense
-// and every chunk's predecessor has a smaller row.  Rows no chunk claims (bad metadata)
-// hold -1.
-__device__ __forceinline__ void chain_chunk_order(const PrefillParams& p, const int* nch,
-                                                  const int* rank_of) {
-  for (int i = threadIdx.x; i < p.C; i += blockDim.x) p.chunk_ord[i] = -1;
-  __syncthreads();
-  for (int k = threadIdx.x; k < p.C; k += blockDim.x) {
+// The chain kernel's work items: (chunk k, head h) runs as workgroup 8 * slot + x, i.e. on
+// XCD x (workgroups are dispatched round-robin over the 8 XCDs).  The chains (sequence
+// rank q, head h), taken in the order c = q * H + h (longest sequences first), are cut into
+// 8 contiguous runs of equal work (chunks), one per XCD, and every run is laid out row by
+// row: row j holds the run's chains with more than j chunks, which are a prefix of the run
+// since lengths do not increase along it.  So all chunks of a chain share one XCD (the
+// hand-off can stay in its L2), the heads of a (sequence, group) share one XCD except at
+// the cuts (their operand fragments are fetched into one L2 rather than into every one),
+// and every predecessor sits in an earlier row of the same XCD.  Slot of chain c at row j:
+// sum over the run of min(length, j), plus c minus the run's first chain; entries no chunk
+// claims (bad metadata, the padding of the last rows) hold -1.
+// `len_q` and `wq` are kOrderMaxSeqs + 1 ints of LDS each, `kinfo` C ints of LDS.
+__device__ void chain_items(const PrefillParams& p, const int* nch, const int* rank_of, int* len_q,
+                            int* wq, int* kinfo) {
+  const int S = p.S, H = p.H, tid = threadIdx.x, nt = blockDim.x;
+  __shared__ int cut[kXcds + 1];
+  __shared__ int part[256];
+  for (int i = tid; i < p.chain_grid; i += nt) p.items[i] = -1;
+  for (int q = tid; q < S; q += nt) len_q[q] = nch[p.seq_ord[q]];
+  // every chunk's sequence rank and position in the sequence (-1: bad metadata)
+  for (int k = tid; k < p.C; k += nt) {
     const int r = p.seq_idx[k];
-    if (r < 0 || r >= p.S) continue;
-    const int j = k - (r == 0 ? 0 : p.last_chunk[r - 1] + 1);
-    if (j < 0 || j >= nch[r]) continue;
-    int row = rank_of[r];
-    for (int q = 0; q < p.S; ++q) row += min(nch[q], j);
-    if (row < p.C) p.chunk_ord[row] = k;
+    int info = -1;
+    if (r >= 0 && r < S) {
+      const int j = k - (r == 0 ? 0 : p.last_chunk[r - 1] + 1);
+      if (j >= 0 && j < nch[r]) info = rank_of[r] | (j << 10);
+    }
+    kinfo[k] = info;
+  }
+  __syncthreads();
+  // wq[q] = work of the chains of ranks < q (exclusive prefix of len_q * H); S <= 4 * 256
+  {
+    int v[4], sum = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int q = 4 * tid + u;
+      v[u] = q < S ? len_q[q] * H : 0;
+      sum += v[u];
+    }
+    part[tid] = sum;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      const int o = tid >= off ? part[tid - off] : 0;
+      __syncthreads();
+      part[tid] += o;
+      __syncthreads();
+    }
+    int run = part[tid] - sum;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int q = 4 * tid + u;
+      if (q < S) wq[q] = run;
+      run += v[u];
+    }
+    if (tid == 255) wq[S] = part[255];
+    __syncthreads();
+  }
+  const int total = wq[S], nchain = S * H;
+  __shared__ int wcut[kXcds + 1];
+  if (tid <= kXcds) {
+    // run x starts at the first chain whose work-before reaches x * total / 8
+    const int target = int((int64_t(tid) * total + kXcds - 1) / kXcds);
+    int lo = 0, hi = S;   // last rank with wq <= target
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (wq[mid] <= target) lo = mid;
+      else hi = mid - 1;
+    }
+    int c = nchain, w = total;   // the chain and the work before it
+    if (lo < S) {
+      const int t = len_q[lo] > 0 ? min(H, (target - wq[lo] + len_q[lo] - 1) / len_q[lo]) : 0;
+      c = lo * H + t;
+      w = wq[lo] + t * len_q[lo];
+    }
+    if (tid == 0) c = 0, w = 0;
+    if (tid == kXcds) c = nchain, w = total;
+    cut[tid] = c;
+    wcut[tid] = w;
+  }
+  __syncthreads();
+  // one (chunk, head) item per thread and step
+  const int nitem = p.C * H;
+  for (int idx = tid; idx < nitem; idx += nt) {
+    const int k = idx / H, h = idx - k * H;
+    const int info = kinfo[k];
+    if (info < 0) continue;
+    const int j = info >> 10;
+    const int c = (info & 1023) * H + h;
+    int x = 0;
+    while (x + 1 < kXcds && c >= cut[x + 1]) ++x;
+    const int a = cut[x], b = cut[x + 1];
+    // first rank whose chains have fewer than j chunks: chains a .. e-1 have at least j
+    int lo = 0, hi = S;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (len_q[mid] >= j) lo = mid + 1;
+      else hi = mid;
+    }
+    int e = lo * H, we = wq[lo];
+    if (e <= a) e = a, we = wcut[x];
+    if (e >= b) e = b, we = wcut[x + 1];
+    // row j of the run starts at sum over the run of min(length, j)
+    const int64_t slot = int64_t(j) * (e - a) + (wcut[x + 1] - we) + (c - a);
+    const int64_t id = slot * kXcds + x;
+    if (id < p.chain_grid) p.items[id] = k * H + h;
   }
 }
 
@@ -359,7 +440,12 @@ __global__ __launch_bounds__(256) void k_chunk_prep(PrefillParams p) {
     static_assert(sizeof(tl) >= 2 * kOrderMaxSeqs * sizeof(int), "order scratch");
     int* nch = reinterpret_cast<int*>(&tl[0][0]);
     sequence_order(p, nch, nch + kOrderMaxSeqs);
-    if (p.chunk_ord && chain_ordered(p)) chain_chunk_order(p, nch, nch + kOrderMaxSeqs);
+    // the chain shapes' work items, with the B tile (staged only after this) as scratch
+    if constexpr (sizeof(Bs) >= (2 * (kOrderMaxSeqs + 1) + kChainOrderMaxChunks) * sizeof(int)) {
+      int* scratch = reinterpret_cast<int*>(Bs);
+      if (p.items) chain_items(p, nch, nch + kOrderMaxSeqs, scratch, scratch + kOrderMaxSeqs + 1,
+                               scratch + 2 * (kOrderMaxSeqs + 1));
+    }
     __syncthreads();
   }
   // the chain kernel's publication flags of this chunk start cleared
@@ -1006,10 +1092,8 @@ void k_chunk_march(PrefillParams p) {
 // publisher waits for its state stores to complete, then sets the flag; the cache policy of
 // the stores and of the successor's loads is chosen as described at kCohDev.
 //
-// Dispatch order: rows of the grid are chunks in the order of k_chunk_prep's chunk_ord (by
-// position inside the sequence, then sequences longest first), so a workgroup's
-// predecessor sits in an earlier row; inside a row, head h runs on XCD h / ceil(H / 8),
-// so the heads of one group share an L2 for the fragments.  Workgroups are dispatched in
+// Dispatch order: k_chunk_prep's item table (chain_items) places every chain on one XCD and
+// a workgroup's predecessor in an earlier row of that XCD.  Workgroups are dispatched in
 // id order, so a waiting workgroup's predecessor is already resident or done; the wait is
 // also bounded in time (about a second, then SSD_DEVERR_CHAIN_WAIT is raised and the
 // workgroup goes on), so no metadata error can stall the device.
@@ -1145,13 +1229,23 @@ void k_chunk_chain(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) float s_w[CS];        // chunk-end weight
   __shared__ float s_tot[NW];                                    // per-wave delta*A sums
 
-  // (chunk, head) of this workgroup
+  // (chunk, head) of this workgroup: from k_chunk_prep's item table, or (batches too large
+  // to order) chunks in index order, which also puts every predecessor first, with the
+  // heads spread over the XCDs
   const int tid = threadIdx.x;
-  const int hx = (p.H + kXcds - 1) / kXcds;                    // heads per XCD and row
-  const int row = blockIdx.x / (kXcds * hx), sl = blockIdx.x % (kXcds * hx);
-  const int h = (sl % kXcds) * hx + sl / kXcds;
-  if (h >= p.H || row >= p.C) return;
-  const int k = chain_ordered(p) ? ld_meta(p.chunk_ord, row) : row;
+  int k, h;
+  if (p.items) {
+    const int item = ld_meta(p.items, blockIdx.x);
+    if (item < 0) return;
+    k = item / p.H;
+    h = item - k * p.H;
+  } else {
+    const int hx = (p.H + kXcds - 1) / kXcds;                  // heads per XCD and row
+    const int row = blockIdx.x / (kXcds * hx), sl = blockIdx.x % (kXcds * hx);
+    h = (sl % kXcds) * hx + sl / kXcds;
+    if (h >= p.H || row >= p.C) return;
+    k = row;
+  }
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, li = lane & 15, kg = lane >> 4;
   const uint32_t lane_b = uint32_t(lane) * 8 * sizeof(T);
@@ -1516,9 +1610,7 @@ static hipError_t run_chunked(const PrefillParams& p, hipStream_t s, void* const
                      s, p);
   record_event(ev, 1, s);
   if constexpr (kChain) {
-    const int hx = (p.H + kXcds - 1) / kXcds;
-    hipLaunchKernelGGL((k_chunk_chain<N, CS>), dim3(p.C * kXcds * hx), dim3(64 * kChainWaves), 0,
-                       s, p);
+    hipLaunchKernelGGL((k_chunk_chain<N, CS>), dim3(p.chain_grid), dim3(64 * kChainWaves), 0, s, p);
   } else {
     const MarchGrid mg = march_grid(p.S, p.G, p.H, P / PW);
     hipLaunchKernelGGL((k_chunk_march<T, P, PW, N, CS>), dim3(mg.nblocks * mg.bsize), dim3(256), 0,

@@ -144,7 +144,7 @@ static void plan_sweep() {
               if (st == SSD_OK) {
                 ++ok;
                 const size_t offs[] = {plan.off_cb, plan.off_bt, plan.off_dc, plan.off_cf,
-                                       plan.off_ord, plan.off_flag, plan.off_cord, plan.off_ring,
+                                       plan.off_ord, plan.off_flag, plan.off_items, plan.off_ring,
                                        plan.off_blk};
                 for (size_t o : offs) CHECK(o <= plan.ws_bytes);
                 CHECK(plan.ws_bytes % 256 == 0);
