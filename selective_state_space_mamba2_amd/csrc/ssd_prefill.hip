@@ -436,17 +436,20 @@ __global__ __launch_bounds__(256) void k_chunk_prep(PrefillParams p) {
   const int k = blockIdx.x, g = blockIdx.y, z = blockIdx.z, tid = threadIdx.x;
   const int zs = gridDim.z;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  if (k == 0 && g == 0 && z == 0 && p.S <= kOrderMaxSeqs) {
-    static_assert(sizeof(tl) >= 2 * kOrderMaxSeqs * sizeof(int), "order scratch");
-    int* nch = reinterpret_cast<int*>(&tl[0][0]);
-    sequence_order(p, nch, nch + kOrderMaxSeqs);
-    // the chain shapes' work items, with the B tile (staged only after this) as scratch
-    if constexpr (sizeof(Bs) >= (2 * (kOrderMaxSeqs + 1) + kChainOrderMaxChunks) * sizeof(int)) {
-      int* scratch = reinterpret_cast<int*>(Bs);
-      if (p.items) chain_items(p, nch, nch + kOrderMaxSeqs, scratch, scratch + kOrderMaxSeqs + 1,
-                               scratch + 2 * (kOrderMaxSeqs + 1));
+  if (k == p.C) {
+    // the grid's extra column: one workgroup orders the sequences (and the chain's work
+    // items) beside the chunks' workgroups, with its B tile as scratch
+    if (g == 0 && z == 0 && p.S <= kOrderMaxSeqs) {
+      static_assert(sizeof(tl) >= 2 * kOrderMaxSeqs * sizeof(int), "order scratch");
+      int* nch = reinterpret_cast<int*>(&tl[0][0]);
+      sequence_order(p, nch, nch + kOrderMaxSeqs);
+      if constexpr (sizeof(Bs) >= (2 * (kOrderMaxSeqs + 1) + kChainOrderMaxChunks) * sizeof(int)) {
+        int* scratch = reinterpret_cast<int*>(Bs);
+        if (p.items) chain_items(p, nch, nch + kOrderMaxSeqs, scratch, scratch + kOrderMaxSeqs + 1,
+                                 scratch + 2 * (kOrderMaxSeqs + 1));
+      }
     }
-    __syncthreads();
+    return;
   }
   // the chain kernel's publication flags of this chunk start cleared
   if (p.chain_flag && z == 0) {
@@ -1606,8 +1609,8 @@ static hipError_t run_chunked(const PrefillParams& p, hipStream_t s, void* const
   constexpr bool kChain = chain_supported(sizeof(T) == 2 ? SSD_BF16 : SSD_F32, P, N, CS);
   if (kChain && !p.chain_flag) return hipErrorInvalidValue;   // the plan gives it the buffers
   record_event(ev, 0, s);
-  hipLaunchKernelGGL((k_chunk_prep<T, N, CS>), dim3(p.C, p.G, prep_split(p.C * p.G)), dim3(256), 0,
-                     s, p);
+  hipLaunchKernelGGL((k_chunk_prep<T, N, CS>), dim3(p.C + 1, p.G, prep_split(p.C * p.G)), dim3(256),
+                     0, s, p);
   record_event(ev, 1, s);
   if constexpr (kChain) {
     hipLaunchKernelGGL((k_chunk_chain<N, CS>), dim3(p.chain_grid), dim3(64 * kChainWaves), 0, s, p);
