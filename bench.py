@@ -200,10 +200,15 @@ def _kernel_spread(evs_per_step, n_kernels):
 
 
 def _source_digest(*names):
+    """Digest of kernel sources with comments and blank lines left out (a comment edit keeps
+    a stored counter record valid; any code change invalidates it)."""
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "selective_state_space_mamba2_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "selective_state_space_mamba2_amd", "csrc", n)) as f:
+            for line in f:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 
