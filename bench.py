@@ -214,8 +214,9 @@ def _source_digest(*names):
 
 def _counter_traffic(kernel, workload, digest):
     """HBM bytes per launch measured with rocprofv3 PMC counters (FETCH_SIZE + WRITE_SIZE,
-    scaled by a copy-kernel calibration), as recorded under profiles/.  None when no record
-    exists or the kernel source changed since the counters were taken."""
+    each scaled by what it reads for the probe's pure-read / pure-write launches of known
+    size in the same run), as recorded under profiles/.  None when no record exists or the
+    kernel code changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "counters.json")
     if not os.path.exists(path):
         return None
@@ -229,8 +230,9 @@ def _counter_traffic(kernel, workload, digest):
 
 
 TRAFFIC_SOURCE = ("stored record (profiles/counters.json): rocprofv3 FETCH_SIZE and WRITE_SIZE "
-                  "of this kernel on this workload, scaled by a copy-kernel calibration, keyed "
-                  "by a digest of the kernel sources (null once they changed)")
+                  "of this kernel on this workload, each scaled by what it reads for the "
+                  "library probe's pure-read / pure-write launches of known size in the same "
+                  "run, keyed by a digest of the kernel code (null once it changed)")
 
 
 def _roofline(bound, achieved, peak, unit, traffic=None, kernel=None, work=None):
@@ -834,16 +836,6 @@ def _add_measured_frac(obj, peaks):
                 _add_measured_frac(v, peaks)
 
 
-def copy_calibration(torch, mib=1024, reps=3):
-    """A plain device copy of known size (for scaling the HBM byte counters)."""
-    a = torch.empty(mib * (1 << 20) // 4, dtype=torch.float32, device="cuda").normal_()
-    b = torch.empty_like(a)
-    for _ in range(reps):
-        b.copy_(a)
-    torch.cuda.synchronize()
-    _log(f"copy calibration: {reps} copies of {mib} MiB")
-
-
 def _prefill_config(inp, C):
     lens = [int(v) for v in (inp.cu_seqlens[1:] - inp.cu_seqlens[:-1])]
     nc = [int(v) for v in inp.num_computed]
@@ -891,7 +883,6 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--primary-only", action="store_true")
-    ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle time per sampled baseline")
     ap.add_argument("--legs", default="",
@@ -907,8 +898,6 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    if args.copy_calibration:
-        copy_calibration(torch)
     cpu = not args.no_cpu_baseline
 
     name = "nemotron_h_prefix_cache"

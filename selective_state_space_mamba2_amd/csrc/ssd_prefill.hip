@@ -252,11 +252,11 @@ __device__ __forceinline__ void sequence_order(const PrefillParams& p, int* nch,
 // 8 contiguous runs of equal work (chunks), one per XCD, and every run is laid out row by
 // row: row j holds the run's chains with more than j chunks, which are a prefix of the run
 // since lengths do not increase along it.  So all chunks of a chain share one XCD (the
-// hand-off can stay in its L2), the heads of a (sequence, group) share one XCD except at
-// the cuts (their operand fragments are fetched into one L2 rather than into every one),
-// and every predecessor sits in an earlier row of the same XCD.  Slot of chain c at row j:
-// sum over the run of min(length, j), plus c minus the run's first chain; entries no chunk
-// claims (bad metadata, the padding of the last rows) hold -1.
+// publisher can leave the state in its L2), the heads of a (sequence, group) share one XCD
+// except at the cuts (their operand fragments are fetched into one L2 rather than into
+// every one), and every predecessor sits in an earlier row of the same XCD.  Slot of chain
+// c at row j: sum over the run of min(length, j), plus c minus the run's first chain;
+// entries no chunk claims (bad metadata, the padding of the last rows) hold -1.
 // `len_q` and `wq` are kOrderMaxSeqs + 1 ints of LDS each, `kinfo` C ints of LDS.
 __device__ void chain_items(const PrefillParams& p, const int* nch, const int* rank_of, int* len_q,
                             int* wq, int* kinfo) {
