@@ -1423,6 +1423,14 @@ void k_chunk_chain(PrefillParams p) {
     if (!via_l2 && (e & kFlagLocal) && lane == 0) raise_flag(p.flag, SSD_DEVERR_CHAIN_WAIT);
     hin = chain_state(p, k - 1, h, r, k - 1 - k0);
   }
+  // The state's rows move in the row layout: in the access (q, pt) of wave w, lane L holds
+  // row pt*16 + L/4, columns (w*TNW + q)*16 + 4*(L%4) .. +3, so each four consecutive lanes
+  // cover one contiguous 64-byte row segment (one address-unit pass per quad; the MFMA
+  // accumulator layout, lane (li, kg) = row li, columns 4*kg.., takes four).
+  const int rrow = lane >> 2, rcol = 4 * (lane & 3);
+  auto roff = [&](int q, int pt) {   // element offset of this lane's four states
+    return (pt * 16 + rrow) * N + (wave * TNW + q) * 16 + rcol;
+  };
   f32x4_v hreg[TNW][TP];
   if (from_pool) {
     // a pool slot (fp32 or bf16), written before this launch
@@ -1430,8 +1438,7 @@ void k_chunk_chain(PrefillParams p) {
     for (int q = 0; q < TNW; ++q)
 #pragma unroll
       for (int pt = 0; pt < TP; ++pt) {
-        const float4_v v = pool_ld4(p.pool, p.pool_bf16,
-                                    src_e + (pt * 16 + li) * N + (wave * TNW + q) * 16 + 4 * kg);
+        const float4_v v = pool_ld4(p.pool, p.pool_bf16, src_e + roff(q, pt));
         hreg[q][pt] = f32x4_v{v.x, v.y, v.z, v.w};
       }
   } else if (hin) {
@@ -1443,15 +1450,13 @@ void k_chunk_chain(PrefillParams p) {
       for (int q = 0; q < TNW; ++q)
 #pragma unroll
         for (int pt = 0; pt < TP; ++pt)
-          hv[q][pt] = __builtin_amdgcn_raw_buffer_load_b128(
-              hb.r, uint32_t((pt * 16 + li) * N + (wave * TNW + q) * 16 + 4 * kg) * 4, 0, kCohWg);
+          hv[q][pt] = __builtin_amdgcn_raw_buffer_load_b128(hb.r, uint32_t(roff(q, pt)) * 4, 0, kCohWg);
     } else {
 #pragma unroll
       for (int q = 0; q < TNW; ++q)
 #pragma unroll
         for (int pt = 0; pt < TP; ++pt)
-          hv[q][pt] = __builtin_amdgcn_raw_buffer_load_b128(
-              hb.r, uint32_t((pt * 16 + li) * N + (wave * TNW + q) * 16 + 4 * kg) * 4, 0, kCohDev);
+          hv[q][pt] = __builtin_amdgcn_raw_buffer_load_b128(hb.r, uint32_t(roff(q, pt)) * 4, 0, kCohDev);
     }
 #pragma unroll
     for (int q = 0; q < TNW; ++q)
@@ -1474,7 +1479,7 @@ void k_chunk_chain(PrefillParams p) {
   for (int q = 0; q < TNW; ++q)
 #pragma unroll
     for (int pt = 0; pt < TP; ++pt)
-      O::st4lds(&Hs[(pt * 16 + li) * RSB + chain_hs(li, (wave * TNW + q) * 16 + 4 * kg)], hreg[q][pt]);
+      O::st4lds(&Hs[(pt * 16 + rrow) * RSB + chain_hs(rrow, (wave * TNW + q) * 16 + rcol)], hreg[q][pt]);
   {
     const float dec = fast_exp(s_c[CS - 1]);
     const BufRes hb(chain_state(p, k, h, r, k - k0));
@@ -1482,14 +1487,20 @@ void k_chunk_chain(PrefillParams p) {
     // kept in this XCD's L2 when the successor maps here too (the last chunk has none)
     // and the state goes to the checkpoint output (no line of it can sit in an L1)
     const bool keep_l2 = !last && p.states && my_xcd == int(blockIdx.x % kXcds);
+    // S_k into the row layout: lane L takes the accumulator values of lane (L%4)*16 + L/4
+    const int src_b = ((lane & 3) * 16 + (lane >> 2)) * 4;
     f32x4_v hn[TNW][TP];
 #pragma unroll
     for (int q = 0; q < TNW; ++q)
 #pragma unroll
-      for (int pt = 0; pt < TP; ++pt) hn[q][pt] = dec * hreg[q][pt] + sacc[q][pt];
-    auto hoff = [&](int q, int pt) {
-      return uint32_t((pt * 16 + li) * N + (wave * TNW + q) * 16 + 4 * kg) * 4;
-    };
+      for (int pt = 0; pt < TP; ++pt) {
+        f32x4_v sr;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          sr[e] = __int_as_float(__builtin_amdgcn_ds_bpermute(src_b, __float_as_int(sacc[q][pt][e])));
+        hn[q][pt] = dec * hreg[q][pt] + sr;
+      }
+    auto hoff = [&](int q, int pt) { return uint32_t(roff(q, pt)) * 4; };
     auto hbits = [&](const f32x4_v& v) {
       return u32x4_v{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
                      __float_as_uint(v[3])};
