@@ -1442,7 +1442,8 @@ void k_chunk_chain(PrefillParams p) {
         hreg[q][pt] = f32x4_v{v.x, v.y, v.z, v.w};
       }
   } else if (hin) {
-    // the predecessor's state through this XCD's L2, else device-coherent
+    // the predecessor's state: workgroup-scope loads after an L2-form publication on this
+    // XCD, device-coherent ones otherwise
     const BufRes hb(hin);
     u32x4_v hv[TNW][TP];
     if (via_l2) {
@@ -1484,8 +1485,9 @@ void k_chunk_chain(PrefillParams p) {
     const float dec = fast_exp(s_c[CS - 1]);
     const BufRes hb(chain_state(p, k, h, r, k - k0));
 
-    // kept in this XCD's L2 when the successor maps here too (the last chunk has none)
-    // and the state goes to the checkpoint output (no line of it can sit in an L1)
+    // the L2 form (plain stores, no wait for a write-through) when the successor maps to
+    // this XCD too (the last chunk has none) and the state goes to the checkpoint output (no
+    // line of it can sit in an L1)
     const bool keep_l2 = !last && p.states && my_xcd == int(blockIdx.x % kXcds);
     // S_k into the row layout: lane L takes the accumulator values of lane (L%4)*16 + L/4
     const int src_b = ((lane & 3) * 16 + (lane >> 2)) * 4;
