@@ -73,7 +73,7 @@ typedef enum ssd_status {
                                       environment variable SSD_DEBUG is set (not "0"),
                                       by an extra kernel each call launches first        */
 
-typedef enum ssd_dtype { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
+typedef enum ssd_dtype { SSD_F32 = 0, SSD_BF16 = 1, SSD_F16 = 2 } ssd_dtype;
 
 typedef enum ssd_a_kind {
   SSD_A_SCALAR = 0,  /* Mamba2: A[H], one decay per head                                 */
@@ -162,7 +162,7 @@ typedef struct ssd_prefill_args {
   int32_t chunk_size;   /* cs                                                           */
   int32_t num_seqs;     /* S                                                            */
   int32_t num_chunks;   /* C, as returned by ssd_build_chunk_metadata                   */
-  int32_t in_dtype;     /* ssd_dtype of x, dt, B, C and y                                */
+  int32_t in_dtype;     /* ssd_dtype of x, dt, B, C and y: SSD_F32 or SSD_BF16            */
   int32_t a_kind;       /* ssd_a_kind                                                   */
 
   /* token tensors (device).  Within one token the layout is contiguous ([H,P] / [H] /
@@ -215,11 +215,12 @@ typedef struct ssd_prefill_args {
    * of kernels launched is reported by ssd_prefill_kernel_count. */
   void* const* profile_events;
 
-  /* ssd_dtype of state_pool: SSD_F32 (0, so a zero-initialised struct keeps fp32) or
-   * SSD_BF16 (a bf16 pool, the reduced-precision SSM state dtype of "vLLM Mamba2 SSD kernel
-   * warm-up", mamba_mixer2.py section): states are read from and written to the pool in
-   * that dtype (round to nearest even) and carried in fp32 everywhere else; chunk_states_out
-   * stays fp32. */
+  /* ssd_dtype of state_pool: SSD_F32 (0, so a zero-initialised struct keeps fp32), SSD_BF16
+   * or SSD_F16 (a bf16 or IEEE fp16 pool, the reduced-precision SSM state dtypes of "vLLM
+   * Mamba2 SSD kernel warm-up", mamba_mixer2.py section): states are read from and written
+   * to the pool in that dtype (round to nearest even; an fp16 state beyond 65504 in
+   * magnitude becomes infinite) and carried in fp32 everywhere else; chunk_states_out stays
+   * fp32.  Any other value: SSD_ERR_BAD_SHAPE. */
   int32_t state_dtype;
 
   /* "all" cache mode: prefix caching with one state entry per cache block ("[vLLM] Mamba
@@ -311,7 +312,7 @@ typedef struct ssd_decode_args {
   int32_t B_pad;        /* rows, including padding rows                                 */
   int32_t ntok;         /* tokens per row = 1 + speculative tokens, >= 1                */
   int32_t H, P, G, N;
-  int32_t in_dtype;     /* ssd_dtype of x, dt, B, C and y                                */
+  int32_t in_dtype;     /* ssd_dtype of x, dt, B, C and y: SSD_F32 or SSD_BF16            */
   int32_t a_kind;       /* SSD_A_SCALAR, or SSD_A_DIAG (Mamba1: P == 1, G == 1, N == 16) */
 
   /* token tensors (device, contiguous) */
@@ -336,8 +337,10 @@ typedef struct ssd_decode_args {
   int32_t* device_error_flag;         /* NULL or an int32 receiving SSD_DEVERR_* bits */
   void* const* profile_events;        /* NULL or 2 hipEvent_t recorded before and after
                                          the update kernel (timing hook)              */
-  int32_t state_dtype;                /* ssd_dtype of state_pool: SSD_F32 (0) or SSD_BF16;
-                                         the state is carried in fp32 inside the step  */
+  int32_t state_dtype;                /* ssd_dtype of state_pool: SSD_F32 (0), SSD_BF16
+                                         or SSD_F16 (a 2-byte pool with a dense A needs
+                                         slot_stride % 8 == 0); the state is carried in
+                                         fp32 inside the step                          */
 
   /* "all" cache mode (one state entry per cache block, as for the prefill): idx_stride ==
    * 0 keeps state_indices [B_pad, ntok] as described above.  With idx_stride > 0,
@@ -389,7 +392,7 @@ typedef struct ssd_conv1d_args {
   int32_t num_seqs;     /* S                                                            */
   int32_t num_chunks;   /* C of the chunk metadata (ssd_build_chunk_metadata, any
                            chunk_size): the unit of work, never two sequences           */
-  int32_t in_dtype;     /* ssd_dtype of x, out and the conv state                        */
+  int32_t in_dtype;     /* ssd_dtype of x, out and the conv state: SSD_F32 or SSD_BF16    */
   const void* x;   int64_t x_stride_t;    /* [T, D] (device), stride >= D               */
   void* out;       int64_t out_stride_t;  /* [T, D] out (device), stride >= D           */
   const float* weight;  /* [D, W] (device, fp32)                                          */

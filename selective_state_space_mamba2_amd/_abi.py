@@ -28,6 +28,7 @@ SSD_DEVERR_DUPLICATE_SLOT = 16
 
 SSD_F32 = 0
 SSD_BF16 = 1
+SSD_F16 = 2
 SSD_A_SCALAR = 0
 SSD_A_DIAG = 1
 

@@ -92,6 +92,8 @@ def _dtype_code(t) -> int:
         return _abi.SSD_BF16
     if t.dtype == torch.float32:
         return _abi.SSD_F32
+    if t.dtype == torch.float16:
+        return _abi.SSD_F16
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
@@ -193,6 +195,11 @@ def _float_dtypes():
     return (torch.bfloat16, torch.float32)
 
 
+def _pool_dtypes():
+    import torch
+    return (torch.bfloat16, torch.float32, torch.float16)
+
+
 def _flag_for(ck: _Checker, device_error_flag):
     """The caller's error flag, or the GPU's persistent error word."""
     return _error_word(ck.device) if device_error_flag is None else device_error_flag
@@ -237,7 +244,7 @@ def prefill_args(x, dt, A, B, C, chunk_size: int, cu_seqlens, cu_chunk_seqlens, 
     ck.i32("seq_idx", seq_idx)
     ck.i32("last_chunk_indices", last_chunk_indices, numel=S)
     if state_pool is not None:
-        ck.t("state_pool", state_pool, _float_dtypes())
+        ck.t("state_pool", state_pool, _pool_dtypes())
         if state_pool.dim() != 4 or tuple(state_pool.shape[1:]) != (H, P, N) or \
                 tuple(state_pool.stride()[1:]) != (P * N, N, 1):
             ck.fail("state_pool must be [slots, H, P, N] with contiguous slots")
@@ -364,7 +371,7 @@ def decode_args(x, dt, A, B, C, y, state_pool, state_indices, num_accepted_token
     ck.f32("A", A, numel=H * N if diag else H)
     ck.f32("D", D, numel=H)
     ck.f32("dt_bias", dt_bias, numel=H)
-    ck.t("state_pool", state_pool, _float_dtypes())
+    ck.t("state_pool", state_pool, _pool_dtypes())
     if state_pool.dim() != 4 or tuple(state_pool.shape[1:]) != (H, P, N) or \
             tuple(state_pool.stride()[1:]) != (P * N, N, 1):
         ck.fail("state_pool must be [slots, H, P, N] with contiguous slots")

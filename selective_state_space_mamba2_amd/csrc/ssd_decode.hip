@@ -310,9 +310,14 @@ static hipError_t launch_t(const DecodeParams& p, hipStream_t s, void* const* ev
 
 hipError_t launch_state_update(int in_dtype, const DecodeParams& p, hipStream_t s,
                                void* const* events) {
-  if (in_dtype == SSD_BF16)
-    return p.pool_bf16 ? launch_t<bf16_t, bf16_t>(p, s, events) : launch_t<bf16_t, float>(p, s, events);
-  return p.pool_bf16 ? launch_t<float, bf16_t>(p, s, events) : launch_t<float, float>(p, s, events);
+  if (in_dtype == SSD_BF16) {
+    if (p.pool_kind == SSD_BF16) return launch_t<bf16_t, bf16_t>(p, s, events);
+    if (p.pool_kind == SSD_F16) return launch_t<bf16_t, f16_t>(p, s, events);
+    return launch_t<bf16_t, float>(p, s, events);
+  }
+  if (p.pool_kind == SSD_BF16) return launch_t<float, bf16_t>(p, s, events);
+  if (p.pool_kind == SSD_F16) return launch_t<float, f16_t>(p, s, events);
+  return launch_t<float, float>(p, s, events);
 }
 
 }  // namespace ssd

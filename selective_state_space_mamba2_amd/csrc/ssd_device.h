@@ -57,7 +57,8 @@ template <> struct Elem<bf16_t> {
   static __device__ __forceinline__ void store(bf16_t* p, float v) { *p = f32_to_bf16(v); }
 };
 
-// Four consecutive pool states: fp32 in memory, or bf16 (round to nearest even on store).
+// Four consecutive pool states: fp32 in memory, or bf16 / fp16 (round to nearest even on
+// store).
 template <typename S> struct PoolIO;
 template <> struct PoolIO<float> {
   static __device__ __forceinline__ float4_v ld4(const void* base, int64_t e) {
@@ -100,14 +101,54 @@ template <> struct PoolIO<bf16_t> {
                                 reinterpret_cast<u32x4_v*>(static_cast<bf16_t*>(base) + e));
   }
 };
+// fp16 pool states: IEEE binary16, converted with round to nearest even.
+typedef _Float16 f16_t;
+__device__ __forceinline__ float f16_to_f32(uint32_t bits) {
+  return float(__builtin_bit_cast(_Float16, uint16_t(bits & 0xffffu)));
+}
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  return uint32_t(__builtin_bit_cast(uint16_t, _Float16(a))) |
+         (uint32_t(__builtin_bit_cast(uint16_t, _Float16(b))) << 16);
+}
+template <> struct PoolIO<f16_t> {
+  static __device__ __forceinline__ float4_v ld4(const void* base, int64_t e) {
+    const u32x2_v v = *reinterpret_cast<const u32x2_v*>(static_cast<const uint16_t*>(base) + e);
+    return float4_v{f16_to_f32(v.x), f16_to_f32(v.x >> 16), f16_to_f32(v.y), f16_to_f32(v.y >> 16)};
+  }
+  static __device__ __forceinline__ void st4(void* base, int64_t e, float4_v v) {
+    *reinterpret_cast<u32x2_v*>(static_cast<uint16_t*>(base) + e) =
+        u32x2_v{pack_f16x2(v.x, v.y), pack_f16x2(v.z, v.w)};
+  }
+  static __device__ __forceinline__ void st4_nt(void* base, int64_t e, float4_v v) {
+    __builtin_nontemporal_store(u32x2_v{pack_f16x2(v.x, v.y), pack_f16x2(v.z, v.w)},
+                                reinterpret_cast<u32x2_v*>(static_cast<uint16_t*>(base) + e));
+  }
+  static __device__ __forceinline__ void ld8(const void* base, int64_t e, float* v) {
+    const u32x4_v w = *reinterpret_cast<const u32x4_v*>(static_cast<const uint16_t*>(base) + e);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = f16_to_f32(ws[i]);
+      v[2 * i + 1] = f16_to_f32(ws[i] >> 16);
+    }
+  }
+  static __device__ __forceinline__ void st8_nt(void* base, int64_t e, const float* v) {
+    __builtin_nontemporal_store(u32x4_v{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3]),
+                                        pack_f16x2(v[4], v[5]), pack_f16x2(v[6], v[7])},
+                                reinterpret_cast<u32x4_v*>(static_cast<uint16_t*>(base) + e));
+  }
+};
 __device__ __forceinline__ float4_v as_float4(f32x4_v v) { return float4_v{v[0], v[1], v[2], v[3]}; }
 // The same with the pool dtype chosen at run time (kernels that touch the pool only at a
-// sequence's first and last chunk).
-__device__ __forceinline__ float4_v pool_ld4(const void* base, int bf16, int64_t e) {
-  return bf16 ? PoolIO<bf16_t>::ld4(base, e) : PoolIO<float>::ld4(base, e);
+// sequence's first and last chunk); `kind` is the ABI's state_dtype (0 fp32, 1 bf16, 2 fp16).
+__device__ __forceinline__ float4_v pool_ld4(const void* base, int kind, int64_t e) {
+  if (kind == 1) return PoolIO<bf16_t>::ld4(base, e);
+  if (kind == 2) return PoolIO<f16_t>::ld4(base, e);
+  return PoolIO<float>::ld4(base, e);
 }
-__device__ __forceinline__ void pool_st4(void* base, int bf16, int64_t e, float4_v v) {
-  if (bf16) PoolIO<bf16_t>::st4(base, e, v);
+__device__ __forceinline__ void pool_st4(void* base, int kind, int64_t e, float4_v v) {
+  if (kind == 1) PoolIO<bf16_t>::st4(base, e, v);
+  else if (kind == 2) PoolIO<f16_t>::st4(base, e, v);
   else PoolIO<float>::st4(base, e, v);
 }
 

@@ -119,7 +119,7 @@ __global__ __launch_bounds__(256) void k_diag_scan(PrefillParams p) {
       const int64_t e = int64_t(src) * p.slot_stride + int64_t(c) * N + ng * SPL;
 #pragma unroll
       for (int i = 0; i < SPL; i += 4) {
-        const float4_v v = pool_ld4(p.pool, p.pool_bf16, e + i);
+        const float4_v v = pool_ld4(p.pool, p.pool_kind, e + i);
         h[i] = v.x; h[i + 1] = v.y; h[i + 2] = v.z; h[i + 3] = v.w;
       }
     }
@@ -284,7 +284,7 @@ __global__ __launch_bounds__(256) void k_diag_scan(PrefillParams p) {
             const int64_t e = int64_t(bslot) * p.slot_stride + int64_t(c) * N + ng * SPL;
 #pragma unroll
             for (int i = 0; i < SPL; i += 4)
-              pool_st4(p.pool, p.pool_bf16, e + i, float4_v{h[i], h[i + 1], h[i + 2], h[i + 3]});
+              pool_st4(p.pool, p.pool_kind, e + i, float4_v{h[i], h[i + 1], h[i + 2], h[i + 3]});
           }
         }
         ++k;
@@ -320,7 +320,7 @@ __global__ __launch_bounds__(256) void k_diag_scan(PrefillParams p) {
     const int64_t e = int64_t(fin) * p.slot_stride + int64_t(c) * N + ng * SPL;
 #pragma unroll
     for (int i = 0; i < SPL; i += 4)
-      pool_st4(p.pool, p.pool_bf16, e + i, float4_v{h[i], h[i + 1], h[i + 2], h[i + 3]});
+      pool_st4(p.pool, p.pool_kind, e + i, float4_v{h[i], h[i + 1], h[i + 2], h[i + 3]});
   }
 }
 

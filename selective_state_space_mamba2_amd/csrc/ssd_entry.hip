@@ -90,7 +90,7 @@ ssd_status prefill_launch(const ssd_prefill_args* a, const ssd::PrefillPlan& pla
   p.cu_seqlens = a->cu_seqlens; p.cu_chunk = a->cu_chunk_seqlens;
   p.seq_idx = a->seq_idx; p.last_chunk = a->last_chunk_indices;
   p.pool = a->state_pool; p.slot_stride = a->slot_stride; p.num_slots = a->num_slots;
-  p.pool_bf16 = a->state_dtype == SSD_BF16 ? 1 : 0;
+  p.pool_kind = a->state_dtype;
   p.state_idx = a->state_indices; p.has_init = a->has_initial_state;
   p.write_final = (a->write_final_to_pool && a->state_pool) ? 1 : 0;
   p.block_size = a->block_size; p.idx_stride = a->block_size > 0 ? a->idx_stride : 1;
@@ -182,8 +182,8 @@ ssd_status ssd_state_update(const ssd_decode_args* a, ssd_stream_t stream) {
   if (a->B_pad == 0) return SSD_OK;
   if (ssd::decode_lds_bytes(a->ntok, a->P, a->N) > 64 * 1024) return SSD_ERR_UNSUPPORTED;
   if (!aligned(a->state_pool, 16) || a->slot_stride % 4) return SSD_ERR_UNSUPPORTED;
-  // A bf16 pool is moved 8 states (16 bytes) per lane by the dense-A kernel.
-  if (a->state_dtype == SSD_BF16 && a->a_kind == SSD_A_SCALAR && a->slot_stride % 8)
+  // A 2-byte pool (bf16, fp16) is moved 8 states (16 bytes) per lane by the dense-A kernel.
+  if (a->state_dtype != SSD_F32 && a->a_kind == SSD_A_SCALAR && a->slot_stride % 8)
     return SSD_ERR_UNSUPPORTED;
   ssd::DecodeParams p{};
   p.B_pad = a->B_pad; p.ntok = a->ntok; p.H = a->H; p.P = a->P; p.G = a->G; p.N = a->N;
@@ -192,7 +192,7 @@ ssd_status ssd_state_update(const ssd_decode_args* a, ssd_stream_t stream) {
   p.A = a->A; p.D = a->D;
   p.prep = ssd::DtPrep{a->dt_bias, a->dt_softplus ? 1 : 0, a->dt_min, a->dt_max};
   p.pool = a->state_pool; p.slot_stride = a->slot_stride; p.num_slots = a->num_slots;
-  p.pool_bf16 = a->state_dtype == SSD_BF16 ? 1 : 0;
+  p.pool_kind = a->state_dtype;
   p.idx = a->state_indices; p.num_acc = a->num_accepted_tokens;
   p.null_id = a->null_block_id; p.flag = a->device_error_flag;
   p.idx_stride = a->idx_stride;

@@ -26,6 +26,7 @@ bool decode_supports_n(int N) {
 }
 
 static bool valid_dtype(int32_t d) { return d == SSD_F32 || d == SSD_BF16; }
+static bool valid_state_dtype(int32_t d) { return valid_dtype(d) || d == SSD_F16; }
 
 ssd_status plan_prefill(const ssd_prefill_args* a, PrefillPlan* plan) {
   if (!a || !plan) return SSD_ERR_NULL_POINTER;
@@ -61,7 +62,7 @@ ssd_status plan_prefill(const ssd_prefill_args* a, PrefillPlan* plan) {
   }
   if (std::isnan(a->dt_min) || std::isnan(a->dt_max) || a->dt_min > a->dt_max)
     return SSD_ERR_BAD_SHAPE;
-  if (!valid_dtype(a->state_dtype)) return SSD_ERR_BAD_SHAPE;
+  if (!valid_state_dtype(a->state_dtype)) return SSD_ERR_BAD_SHAPE;
   // the all cache mode: one pool entry per cache block of block_size tokens
   if (a->block_size < 0) return SSD_ERR_BAD_SHAPE;
   if (a->block_size > 0) {
@@ -150,7 +151,7 @@ ssd_status check_decode(const ssd_decode_args* a) {
   if (a->H % a->G != 0) return SSD_ERR_BAD_SHAPE;
   if (!valid_dtype(a->in_dtype)) return SSD_ERR_BAD_SHAPE;
   if (a->a_kind != SSD_A_SCALAR && a->a_kind != SSD_A_DIAG) return SSD_ERR_BAD_SHAPE;
-  if (!valid_dtype(a->state_dtype)) return SSD_ERR_BAD_SHAPE;
+  if (!valid_state_dtype(a->state_dtype)) return SSD_ERR_BAD_SHAPE;
   if (a->ntok > kDecodeMaxTokens) return SSD_ERR_UNSUPPORTED;
   if (a->a_kind == SSD_A_DIAG) {
     // Mamba1: one channel per head position, one B/C group, dstate 16

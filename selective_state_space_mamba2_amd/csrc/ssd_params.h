@@ -26,7 +26,7 @@ struct PrefillParams {
   const int* seq_idx;
   const int* last_chunk;
   void* pool; int64_t slot_stride; int num_slots;
-  int pool_bf16;       // the pool holds bf16 states (else fp32)
+  int pool_kind;       // dtype of the pool states: 0 fp32, 1 bf16, 2 fp16 (state_dtype)
   const int* state_idx;
   const int* has_init;
   int write_final;
@@ -119,7 +119,7 @@ struct DecodeParams {
   const float* D;
   DtPrep prep;
   void* pool; int64_t slot_stride; int num_slots;
-  int pool_bf16;       // the pool holds bf16 states (else fp32)
+  int pool_kind;       // dtype of the pool states: 0 fp32, 1 bf16, 2 fp16 (state_dtype)
   const int* idx;
   const int* num_acc;
   int null_id;

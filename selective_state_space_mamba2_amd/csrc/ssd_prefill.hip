@@ -644,7 +644,7 @@ __device__ __forceinline__ void march_pool_store(const PrefillParams& p, int64_t
                                                  int wave, int li, int kg) {
   constexpr int TN = N / 16, TNW = (TN + 3) / 4, TPW = PW / 16;
   // buffer stores: the slot in a descriptor, one lane offset, the tile offset in soffset
-  const int esz = p.pool_bf16 ? 2 : 4;
+  const int esz = p.pool_kind ? 2 : 4;
   const BufRes b(static_cast<char*>(p.pool) + e * esz);
   const uint32_t lane_e = uint32_t(li * N + 4 * kg);
 #pragma unroll
@@ -655,8 +655,11 @@ __device__ __forceinline__ void march_pool_store(const PrefillParams& p, int64_t
     for (int pt = 0; pt < TPW; ++pt) {
       const f32x4_v v = hreg[q][pt];
       const uint32_t tile_e = uint32_t(pt * 16 * N + nt * 16);
-      if (p.pool_bf16)
+      if (p.pool_kind == SSD_BF16)
         __builtin_amdgcn_raw_buffer_store_b64(u32x2_v{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])},
+                                              b.r, lane_e * 2, tile_e * 2, 0);
+      else if (p.pool_kind == SSD_F16)
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2_v{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])},
                                               b.r, lane_e * 2, tile_e * 2, 0);
       else
         __builtin_amdgcn_raw_buffer_store_b128(u32x4_v{__float_as_uint(v[0]), __float_as_uint(v[1]),
@@ -783,7 +786,7 @@ void k_chunk_march(PrefillParams p) {
       const int nt = wave * TNW + q;
       hreg[q][pt] = f32x4_v{0.f, 0.f, 0.f, 0.f};
       if (init && nt < TN) {
-        const float4_v v = pool_ld4(p.pool, p.pool_bf16, src_e + (pt * 16 + li) * N + nt * 16 + 4 * kg);
+        const float4_v v = pool_ld4(p.pool, p.pool_kind, src_e + (pt * 16 + li) * N + nt * 16 + 4 * kg);
         hreg[q][pt] = f32x4_v{v.x, v.y, v.z, v.w};
       }
     }
@@ -1193,7 +1196,7 @@ __device__ __forceinline__ int chain_hs(int pl, int n) { return n ^ ((pl & 15) <
 // two-deep ring per (sequence, head) in the workspace (chunk j of a sequence uses entry
 // j & 1; entry reuse is safe because chunk j+2 publishes only after chunk j+1 has read H_j).
 __device__ __forceinline__ int chain_pool_pub(const PrefillParams& p, int k) {
-  if (p.states || !p.blk_slot || p.pool_bf16) return -1;
+  if (p.states || !p.blk_slot || p.pool_kind != SSD_F32) return -1;
   const int s = ld_meta(p.blk_slot, k);
   return s < p.num_slots ? s : -1;
 }
@@ -1438,7 +1441,7 @@ void k_chunk_chain(PrefillParams p) {
     for (int q = 0; q < TNW; ++q)
 #pragma unroll
       for (int pt = 0; pt < TP; ++pt) {
-        const float4_v v = pool_ld4(p.pool, p.pool_bf16, src_e + roff(q, pt));
+        const float4_v v = pool_ld4(p.pool, p.pool_kind, src_e + roff(q, pt));
         hreg[q][pt] = f32x4_v{v.x, v.y, v.z, v.w};
       }
   } else if (hin) {
@@ -1525,7 +1528,7 @@ void k_chunk_chain(PrefillParams p) {
       for (int q = 0; q < TNW; ++q)
 #pragma unroll
         for (int pt = 0; pt < TP; ++pt)
-          pool_st4(p.pool, p.pool_bf16, e + hoff(q, pt) / 4, as_float4(hn[q][pt]));
+          pool_st4(p.pool, p.pool_kind, e + hoff(q, pt) / 4, as_float4(hn[q][pt]));
     };
     if (fin_e >= 0) to_pool(fin_e);
     // the block entry, unless the publication above already went there

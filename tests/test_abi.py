@@ -189,7 +189,8 @@ def test_kernel_count():
     (dict(chunk_size=0), _abi.SSD_ERR_BAD_SHAPE),
     (dict(in_dtype=7), _abi.SSD_ERR_BAD_SHAPE),
     (dict(a_kind=5), _abi.SSD_ERR_BAD_SHAPE),
-    (dict(state_dtype=2), _abi.SSD_ERR_BAD_SHAPE),
+    (dict(state_dtype=3), _abi.SSD_ERR_BAD_SHAPE),
+    (dict(in_dtype=_abi.SSD_F16), _abi.SSD_ERR_BAD_SHAPE),       # fp16 is a pool type only
     (dict(num_chunks=1), _abi.SSD_ERR_BAD_SHAPE),         # fewer chunks than sequences
     (dict(num_chunks=600), _abi.SSD_ERR_BAD_SHAPE),       # more chunks than tokens
     (dict(T=1), _abi.SSD_ERR_BAD_SHAPE),                  # fewer tokens than sequences
@@ -299,6 +300,8 @@ def _good_decode(**over):
     (dict(dt_min=2.0, dt_max=1.0), _abi.SSD_ERR_BAD_SHAPE),
     (dict(state_pool=FAKE + 4), _abi.SSD_ERR_UNSUPPORTED),
     (dict(state_dtype=_abi.SSD_BF16, slot_stride=48 * 64 * 128 + 4), _abi.SSD_ERR_UNSUPPORTED),
+    (dict(state_dtype=_abi.SSD_F16, slot_stride=48 * 64 * 128 + 4), _abi.SSD_ERR_UNSUPPORTED),
+    (dict(in_dtype=_abi.SSD_F16), _abi.SSD_ERR_BAD_SHAPE),       # fp16 is a pool type only
     (dict(idx_stride=-1), _abi.SSD_ERR_BAD_SHAPE),
     (dict(idx_stride=5), _abi.SSD_ERR_BAD_SHAPE),                # all cache mode needs ntok 1
     (dict(idx_stride=5, ntok=1, num_accepted_tokens=FAKE), _abi.SSD_ERR_BAD_SHAPE),

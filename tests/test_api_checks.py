@@ -93,7 +93,7 @@ def test_decode_stops_at_the_gpu_check():
     (dict(state_indices=torch.zeros(4, 3, dtype=torch.int32)), "state_indices must be"),
     (dict(A=torch.zeros(H, dtype=torch.float64)), "A has dtype"),
     (dict(C=torch.zeros(4, 2, G, N)), "C has dtype"),
-    (dict(state_pool=torch.zeros(9, H, P, N, dtype=torch.float16)), "state_pool has dtype"),
+    (dict(state_pool=torch.zeros(9, H, P, N, dtype=torch.float64)), "state_pool has dtype"),
     (dict(D=torch.zeros(H, device="meta")), "D is on meta"),
 ])
 def test_decode_argument_checks(over, match):

@@ -8,7 +8,8 @@ import math
 import numpy as np
 import pytest
 
-from gpu_helpers import TOL, assert_close, bf16_pool, host64, oracle_decode, run_decode
+from gpu_helpers import (TOL, assert_close, host64, oracle_decode, pool_tol, rounded_pool,
+                         run_decode)
 from selective_state_space_mamba2_amd.inputs import make_decode, workload
 
 pytestmark = pytest.mark.gpu
@@ -163,22 +164,47 @@ def test_full_mamba1_decode_workload():
 
 
 # ----------------------------------------------------------------------------------------
-# bf16 state pool: states are read from and written to the pool in bf16, carried in fp32
-# inside the step; y keeps the input dtype's tolerance (the bf16 initial states are exact
-# inputs), the written slots the bf16 one.
+# 2-byte state pool (bf16 or fp16): states are read from and written to the pool in that
+# type, carried in fp32 inside the step; y keeps the input dtype's tolerance (the rounded
+# initial states are exact inputs), the written slots the pool type's where that is looser.
 
 @pytest.mark.parametrize("dtype,P,N,G,ntok,a_kind", [("bf16", 64, 128, 2, 4, "scalar"),
                                                      ("f32", 32, 64, 1, 3, "scalar"),
-                                                     # the bf16 pool's halving y reduction
+                                                     # the 2-byte pool's halving y reduction
                                                      # with 2 and 8 rows per lane
                                                      ("f32", 64, 64, 2, 3, "scalar"),
                                                      ("bf16", 64, 256, 1, 2, "scalar"),
                                                      ("bf16", 1, 16, 1, 4, "diag"),
                                                      ("f32", 1, 16, 1, 2, "diag")])
-def test_bf16_state_pool(dtype, P, N, G, ntok, a_kind):
+@pytest.mark.parametrize("pool", ["bf16", "f16"])
+def test_2byte_state_pool(pool, dtype, P, N, G, ntok, a_kind):
     H = 8 if a_kind == "scalar" else 300
-    inp = bf16_pool(make_decode(50 + P + ntok, in_dtype=dtype, B_pad=12, n_live=7, ntok=ntok,
-                                H=H, P=P, G=G, N=N, pool_slots=64, a_kind=a_kind))
+    inp = rounded_pool(make_decode(50 + P + ntok, in_dtype=dtype, B_pad=12, n_live=7,
+                                   ntok=ntok, H=H, P=P, G=G, N=N, pool_slots=64,
+                                   a_kind=a_kind), pool)
     got = run_decode(inp)
     assert got["flag"] == 0
-    _check(inp, got, pool_tol=TOL["bf16"])
+    _check(inp, got, pool_tol=pool_tol(inp))
+
+
+def test_f16_pool_saturates_to_inf():
+    """A state beyond fp16's range is stored as an infinity of its sign (round to nearest
+    even: magnitudes from 65520 up); the other written elements are the fp16 rounding of the
+    exact state, within one fp16 ulp plus the fp32 arithmetic's error."""
+    inp = rounded_pool(make_decode(61, in_dtype="f32", B_pad=8, n_live=6, ntok=1, H=8, P=16,
+                                   G=1, N=16, pool_slots=32), "f16")
+    inp.x = inp.x * 2.0 ** 18                  # exact in fp32; states reach ~1e5
+    got = run_decode(inp)
+    assert got["flag"] == 0
+    _, writes = oracle_decode(inp)
+    n_inf = 0
+    for slot, st in writes.items():
+        g = got["pool"][slot]
+        scale = np.abs(st).max()
+        over = np.abs(st) >= 65520.0 * (1 + 1e-4)
+        under = np.abs(st) <= 65520.0 * (1 - 1e-4)
+        n_inf += int(over.sum())
+        np.testing.assert_array_equal(g[over], np.copysign(np.inf, st[over]))
+        err = np.abs(g[under] - st[under])
+        assert np.all(err <= 2.0 ** -10 * np.abs(st[under]) + 1e-6 * scale), f"slot {slot}"
+    assert n_inf > 0, "the case must overflow fp16 somewhere"

@@ -25,16 +25,17 @@ def test_small_diag_with_pool_and_checkpoints(dtype):
             np.testing.assert_array_equal(got["pool"][s], inp.pool[s])
 
 
+@pytest.mark.parametrize("pool", ["bf16", "f16"])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_diag_bf16_state_pool(dtype):
-    """The Mamba1 scan gathering from and writing back to a bf16 pool."""
-    from gpu_helpers import TOL, bf16_pool
-    inp = bf16_pool(make_prefill(43, in_dtype=dtype, H=200, P=1, G=1, N=16, chunk_size=128,
-                                 lengths=[300, 77], num_computed=[0, 5], a_kind="diag",
-                                 init="pool", pool_slots=8))
+def test_diag_2byte_state_pool(dtype, pool):
+    """The Mamba1 scan gathering from and writing back to a bf16 or fp16 pool."""
+    from gpu_helpers import pool_tol, rounded_pool
+    inp = rounded_pool(make_prefill(43, in_dtype=dtype, H=200, P=1, G=1, N=16, chunk_size=128,
+                                    lengths=[300, 77], num_computed=[0, 5], a_kind="diag",
+                                    init="pool", pool_slots=8), pool)
     got = run_prefill(inp)
     assert got["flag"] == 0
-    check_prefill(inp, got, oracle_prefill(inp), pool_tol=TOL["bf16"])
+    check_prefill(inp, got, oracle_prefill(inp), pool_tol=pool_tol(inp))
     owned = set(int(v) for v in inp.state_indices)
     for s in range(8):
         if s not in owned:

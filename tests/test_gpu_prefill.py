@@ -8,8 +8,8 @@ import math
 import numpy as np
 import pytest
 
-from gpu_helpers import (TOL, assert_close, bf16_pool, check_prefill, oracle_prefill,
-                         run_prefill)
+from gpu_helpers import (TOL, assert_close, check_prefill, oracle_prefill, pool_tol,
+                         rounded_pool, run_prefill)
 from oracle import transform_dt
 from selective_state_space_mamba2_amd.inputs import make_prefill, workload
 
@@ -155,16 +155,19 @@ def test_many_short_sequences_take_chunks_in_index_order():
     check_prefill(inp, got, oracle_prefill(inp, seqs=[0, 5, 6, 700, 1099]))
 
 
+@pytest.mark.parametrize("pool", ["bf16", "f16"])
 @pytest.mark.parametrize("dtype,P,N,cs", [("bf16", 64, 128, 256), ("bf16", 64, 128, 64),
-                                          ("f32", 64, 128, 64)])
-def test_bf16_state_pool(dtype, P, N, cs):
-    """Initial states gathered from, and final states written to, a bf16 pool (chain and
-    march kernels); y and the fp32 chunk states keep the input dtype's tolerance, the
-    written pool slots the bf16 one, untouched slots stay bit-identical."""
-    inp = bf16_pool(_case(36, dtype, P, N, cs, [2 * cs + 40, cs - 3, 70], [0, 5, cs - 1]))
+                                          ("f32", 64, 128, 64), ("f32", 64, 128, 256)])
+def test_2byte_state_pool(pool, dtype, P, N, cs):
+    """Initial states gathered from, and final states written to, a bf16 or fp16 pool (chain
+    and march kernels); y and the fp32 chunk states keep the input dtype's tolerance, the
+    written pool slots the pool type's where that is looser, untouched slots stay
+    bit-identical."""
+    inp = rounded_pool(_case(36, dtype, P, N, cs, [2 * cs + 40, cs - 3, 70], [0, 5, cs - 1]),
+                       pool)
     got = run_prefill(inp)
     assert got["flag"] == 0
-    check_prefill(inp, got, oracle_prefill(inp), pool_tol=TOL["bf16"])
+    check_prefill(inp, got, oracle_prefill(inp), pool_tol=pool_tol(inp))
     owned = set(int(v) for v in inp.state_indices)
     untouched = [s for s in range(inp.pool.shape[0]) if s not in owned]
     np.testing.assert_array_equal(got["pool"][untouched], inp.pool[untouched])

@@ -10,8 +10,8 @@ pool dtype's, and every other slot bit-identical.
 import numpy as np
 import pytest
 
-from gpu_helpers import (TOL, _vals, assert_close, dev_f32, dev_i32, dev_token, host64,
-                         prefill_metadata, torch)
+from gpu_helpers import (TOL, _dev_pool, _vals, assert_close, dev_f32, dev_i32, dev_token,
+                         host64, pool_tol, prefill_metadata, rounded_pool, torch)
 from oracle import block_indices, scan_decode, scan_prefill
 from selective_state_space_mamba2_amd import _abi, api
 from selective_state_space_mamba2_amd.inputs import make_decode, make_prefill
@@ -48,15 +48,13 @@ def _case(seed, dtype, P, N, cs, bs, lengths, nc, H=4, G=2, max_blocks=4, a_kind
     return inp, table, lc, ls
 
 
-def _run(inp, table, bs, lc, ls, *, write_final=True, want_states=True, pool_bf16=False,
+def _run(inp, table, bs, lc, ls, *, write_final=True, want_states=True,
          nc_dev=None):
     t = torch()
     cuc, sidx, last = prefill_metadata(inp)
     x, dt, B, C = (dev_token(inp, n) for n in ("x", "dt", "B", "C"))
     y = t.full_like(x, float("nan"))
-    pool = t.from_numpy(inp.pool).to("cuda")
-    if pool_bf16:
-        pool = pool.to(t.bfloat16)
+    pool = _dev_pool(inp)
     has_init = (inp.num_computed > 0).astype(np.int32)
     states = (t.full((len(sidx), inp.H, inp.P, inp.N), float("nan"), device="cuda")
               if want_states else None)
@@ -96,7 +94,7 @@ def _expected(inp, table, bs, lc, ls, write_final=True):
     return refs, writes
 
 
-def _check(inp, got, refs, writes, pool_tol):
+def _check(inp, got, refs, writes, entry_tol):
     tol = TOL[inp.in_dtype]
     assert got["flag"] == 0
     for r, o in refs.items():
@@ -106,7 +104,7 @@ def _check(inp, got, refs, writes, pool_tol):
             ks = np.flatnonzero(got["sidx"] == r)
             assert_close(got["states"][ks], o["boundary_states"], tol, f"chunk states seq {r}")
     for slot, h in writes.items():
-        assert_close(got["pool"][slot], h, pool_tol, f"pool slot {slot}")
+        assert_close(got["pool"][slot], h, entry_tol, f"pool slot {slot}")
     untouched = [s for s in range(inp.pool.shape[0]) if s not in writes]
     np.testing.assert_array_equal(got["pool"][untouched], inp.pool[untouched])
 
@@ -149,28 +147,32 @@ def test_prefill_diag_writes_every_block_entry(dtype, write_final):
     _check(inp, got, refs, writes, TOL[dtype])
 
 
-def test_prefill_diag_bf16_pool():
-    """The same through a bf16 pool (entries at the bf16 tolerance)."""
+@pytest.mark.parametrize("pool", ["bf16", "f16"])
+def test_prefill_diag_2byte_pool(pool):
+    """The same through a bf16 or fp16 pool (entries at the looser of the input's and the
+    pool type's tolerance)."""
     cs, bs = 64, 192
     lengths, nc = _lengths(cs, bs)
     inp, table, lc, ls = _case(56, "bf16", 1, 16, cs, bs, lengths, nc, H=72, G=1,
                                a_kind="diag")
-    inp.pool = torch().from_numpy(inp.pool).to(torch().bfloat16).float().numpy()
-    got = _run(inp, table, bs, lc, ls, pool_bf16=True)
+    rounded_pool(inp, pool)
+    got = _run(inp, table, bs, lc, ls)
     refs, writes = _expected(inp, table, bs, lc, ls)
-    _check(inp, got, refs, writes, TOL["bf16"])
+    _check(inp, got, refs, writes, pool_tol(inp))
 
 
+@pytest.mark.parametrize("pool", ["bf16", "f16"])
 @pytest.mark.parametrize("dtype,P,N,cs,bs", [SHAPES[0], SHAPES[2]])
-def test_prefill_bf16_pool_and_no_chunk_state_output(dtype, P, N, cs, bs):
-    """A bf16 pool (entries at the bf16 tolerance) and no chunk_states_out (the chain kernel
-    hands states over through its workspace ring)."""
+def test_prefill_2byte_pool_and_no_chunk_state_output(dtype, P, N, cs, bs, pool):
+    """A bf16 or fp16 pool (entries at the looser of the input's and the pool type's
+    tolerance) and no chunk_states_out (the chain kernel hands states over through its
+    workspace ring)."""
     lengths, nc = _lengths(cs, bs)
     inp, table, lc, ls = _case(52, dtype, P, N, cs, bs, lengths, nc)
-    inp.pool = torch().from_numpy(inp.pool).to(torch().bfloat16).float().numpy()
-    got = _run(inp, table, bs, lc, ls, want_states=False, pool_bf16=True)
+    rounded_pool(inp, pool)
+    got = _run(inp, table, bs, lc, ls, want_states=False)
     refs, writes = _expected(inp, table, bs, lc, ls)
-    _check(inp, got, refs, writes, TOL["bf16"])
+    _check(inp, got, refs, writes, pool_tol(inp))
 
 
 def test_prefill_resumes_from_its_own_entries():
@@ -218,7 +220,7 @@ def test_prefill_flags_inconsistent_columns():
 
 
 @pytest.mark.parametrize("kind", ["scalar", "diag"])
-@pytest.mark.parametrize("pool_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("pool_dtype", ["f32", "bf16", "f16"])
 def test_decode_reads_last_computed_writes_last_scheduled(kind, pool_dtype):
     t = torch()
     if kind == "scalar":
@@ -227,8 +229,8 @@ def test_decode_reads_last_computed_writes_last_scheduled(kind, pool_dtype):
     else:
         inp = make_decode(57, in_dtype="bf16", B_pad=12, n_live=9, ntok=1, H=200, P=1, G=1,
                           N=16, pool_slots=64, a_kind="diag")
-    if pool_dtype == "bf16":
-        inp.pool = t.from_numpy(inp.pool).to(t.bfloat16).float().numpy()
+    if pool_dtype != "f32":
+        rounded_pool(inp, pool_dtype)
     rng = np.random.default_rng(58)
     table = _block_table(59, 12, 3, 64)
     table[9:] = inp.null_block_id                          # padding rows
@@ -236,9 +238,7 @@ def test_decode_reads_last_computed_writes_last_scheduled(kind, pool_dtype):
     ls = np.minimum(lc + rng.integers(0, 2, size=12), 2).astype(np.int32)
     x, dt, B, C = (dev_token(inp, n) for n in ("x", "dt", "B", "C"))
     y = t.full_like(x, 7.0)
-    pool = t.from_numpy(inp.pool).to("cuda")
-    if pool_dtype == "bf16":
-        pool = pool.to(t.bfloat16)
+    pool = _dev_pool(inp)
     flag = t.zeros(1, dtype=t.int32, device="cuda")
     api.ssd_state_update(x, dt, dev_f32(inp.A), B, C, pool, dev_i32(table), y=y,
                          null_block_id=inp.null_block_id, D=dev_f32(inp.D),
