@@ -489,7 +489,8 @@ def cpu_baseline_prefill(inp, budget_s=None, min_s=0.5):
 # ----------------------------------------------------------------------------------------
 # decode
 # ----------------------------------------------------------------------------------------
-def bench_decode(torch, steps, warmup, with_cpu=True, name="decode_spec", pool_bf16=False):
+def bench_decode(torch, steps, warmup, with_cpu=True, name="decode_spec", pool="f32"):
+    """One decode leg; ``pool`` is the state pool's dtype: "f32", "bf16" or "f16"."""
     import ctypes
     from selective_state_space_mamba2_amd import api
     from selective_state_space_mamba2_amd._abi import check, lib
@@ -497,15 +498,15 @@ def bench_decode(torch, steps, warmup, with_cpu=True, name="decode_spec", pool_b
     inp = workload(name)
     x, dt, B, C = (_dev_token(torch, inp, n) for n in ("x", "dt", "B", "C"))
     y = torch.empty_like(x)
-    pool = torch.from_numpy(inp.pool).cuda()
-    if pool_bf16:
-        pool = pool.to(torch.bfloat16)
+    state_pool = torch.from_numpy(inp.pool).cuda()
+    if pool != "f32":
+        state_pool = state_pool.to({"bf16": torch.bfloat16, "f16": torch.float16}[pool])
     idx = torch.from_numpy(inp.state_indices).cuda()
     acc = torch.from_numpy(inp.num_accepted).cuda()
     A = torch.tensor(inp.A, dtype=torch.float32).cuda()
     D = torch.tensor(inp.D, dtype=torch.float32).cuda()
     flag = _error_flag(torch)
-    a = api.decode_args(x, dt, A, B, C, y, pool, idx, num_accepted_tokens=acc,
+    a = api.decode_args(x, dt, A, B, C, y, state_pool, idx, num_accepted_tokens=acc,
                         null_block_id=inp.null_block_id, D=D, device_error_flag=flag)
     sp = torch.cuda.current_stream().cuda_stream
     for _ in range(warmup):
@@ -525,14 +526,14 @@ def bench_decode(torch, steps, warmup, with_cpu=True, name="decode_spec", pool_b
     ms = start.elapsed_time(end) / steps
     _assert_no_device_error(flag, f"decode {name}")
     kms = _kernel_times(ev_sets, 1)[0]
-    w = decode_work(inp, 2 if pool_bf16 else 4)
+    w = decode_work(inp, 4 if pool == "f32" else 2)
     kname = "k_state_update_diag" if inp.A.ndim == 2 else "k_state_update"
-    out = {"workload": name + (" (bf16 state pool)" if pool_bf16 else ""),
+    out = {"workload": name + ("" if pool == "f32" else f" ({pool} state pool)"),
            "metric": "state-updates/s",
            "value": round(w["updates"] / (ms * 1e-3), 1), "unit": "state-updates/s",
            "ms_per_step": round(ms, 5),
            "roofline": _roofline("hbm", w["bytes"] / (kms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s",
-                                 _counter_traffic(kname, name + ("/bf16_pool" if pool_bf16 else ""),
+                                 _counter_traffic(kname, name + ("" if pool == "f32" else f"/{pool}_pool"),
                                                   _source_digest("ssd_decode.hip", "ssd_device.h")),
                                  kname, w),
            "kernel_ms": round(kms, 5), "kernel_ms_spread": _kernel_spread(ev_sets, 1)[0],
@@ -553,7 +554,7 @@ def bench_decode(torch, steps, warmup, with_cpu=True, name="decode_spec", pool_b
                                          f"fp64 sequential updates with the restore and every "
                                          f"checkpoint; {wall:.1f} s wall",
                                **_cpu_info()}
-    del pool
+    del state_pool
     return out
 
 
@@ -879,7 +880,7 @@ def prefill_leg(torch, name, steps, warmup, graph=False, with_cpu=True, cpu_budg
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--primary-only", action="store_true")
@@ -940,7 +941,10 @@ def main():
                                   name="mamba1_decode_spec")),
             ("decode_bf16_pool", "decode_spec, bf16 state pool",
              lambda: bench_decode(torch, args.steps, args.warmup, with_cpu=False,
-                                  pool_bf16=True)),
+                                  pool="bf16")),
+            ("decode_f16_pool", "decode_spec, fp16 state pool",
+             lambda: bench_decode(torch, args.steps, args.warmup, with_cpu=False,
+                                  pool="f16")),
             ("conv1d_prefill", "conv1d prefill",
              lambda: bench_conv_prefill(torch, args.steps, args.warmup)),
             ("conv1d_update", "conv1d update",
