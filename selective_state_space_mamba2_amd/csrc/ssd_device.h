@@ -103,12 +103,15 @@ template <> struct PoolIO<bf16_t> {
 };
 // fp16 pool states: IEEE binary16, converted with round to nearest even.
 typedef _Float16 f16_t;
+typedef _Float16 f16x2_v __attribute__((ext_vector_type(2)));
+typedef float f32x2_v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float f16_to_f32(uint32_t bits) {
   return float(__builtin_bit_cast(_Float16, uint16_t(bits & 0xffffu)));
 }
+// Two fp32 -> packed pair of fp16 (low half = a), round to nearest even, magnitudes past
+// the fp16 range to infinity: one v_cvt_pk_f16_f32 on gfx950.
 __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
-  return uint32_t(__builtin_bit_cast(uint16_t, _Float16(a))) |
-         (uint32_t(__builtin_bit_cast(uint16_t, _Float16(b))) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_v{a, b}, f16x2_v));
 }
 template <> struct PoolIO<f16_t> {
   static __device__ __forceinline__ float4_v ld4(const void* base, int64_t e) {
