@@ -15,8 +15,8 @@ carries, each with its own roofline and oracle baseline, the Mamba2-2.7B-like la
 prefill (4 x 2048 tokens, 80 heads), the tiny fp32 prefill, the decode state update (256
 live requests of a 512-row padded batch, 1+3 tokens, [2048,48,64,128] fp32 pool) and the
 Mamba1 long-context diagonal scan, and as further objects the prefix-cache prefill in the
-all cache mode, the Mamba1 decode, the decode with a bf16 state pool and the causal conv1d
-prefill and decode update.
+all cache mode, the Mamba1 decode, the decode with a bf16 and with an fp16 state pool and the
+causal conv1d prefill and decode update.
 
 Roofline: each kernel's duration comes from HIP events the library records around its
 own launches on the launch stream (the C ABI's timing hook), averaged over the timed

@@ -359,8 +359,8 @@ typedef struct ssd_decode_args {
  * SSD_ERR_BAD_SHAPE (also an unknown a_kind, SSD_A_DIAG with P != 1 or G != 1, or the all
  * cache mode with ntok != 1 or num_accepted_tokens set), SSD_ERR_UNSUPPORTED (N, ntok or
  * P*N outside the instantiated range; state_pool not 16-byte aligned or slot_stride not a
- * multiple of 4, or of 8 for a bf16 pool with SSD_A_SCALAR), SSD_ERR_HIP.  B_pad == 0 is a
- * no-op. */
+ * multiple of 4, or of 8 for a bf16 or fp16 pool with SSD_A_SCALAR), SSD_ERR_HIP.
+ * B_pad == 0 is a no-op. */
 ssd_status ssd_state_update(const ssd_decode_args* args, ssd_stream_t stream);
 
 /* ---------------------------------------------------------------------------------------

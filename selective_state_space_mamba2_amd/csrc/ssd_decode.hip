@@ -144,7 +144,7 @@ __global__ __launch_bounds__(256) void k_state_update(DecodeParams p) {
     }
     const int64_t dst = int64_t(row.dst(j)) * p.slot_stride + head_off;
     if constexpr (V == 8 && ITERS > 1 && ITERS <= NQ) {
-      // bf16 pool: the state rows first, each stored as soon as it is updated, then y[p]
+      // 2-byte pool: the state rows first, each stored as soon as it is updated, then y[p]
       // = sum over the NQ lanes of a row group for all ITERS rows at once: halving
       // exchanges (lane bit NQ/2 picks the upper or lower half of the rows, then NQ/4 ...)
       // leave lane q with one row, i = q / (NQ / ITERS); plain exchanges finish its sum.

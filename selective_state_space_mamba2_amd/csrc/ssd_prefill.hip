@@ -1436,7 +1436,7 @@ void k_chunk_chain(PrefillParams p) {
   };
   f32x4_v hreg[TNW][TP];
   if (from_pool) {
-    // a pool slot (fp32 or bf16), written before this launch
+    // a pool slot (fp32, bf16 or fp16), written before this launch
 #pragma unroll
     for (int q = 0; q < TNW; ++q)
 #pragma unroll
