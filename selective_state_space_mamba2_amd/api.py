@@ -155,6 +155,13 @@ class _Checker:
     def __init__(self, fn: str, ref):
         self.fn = fn
         self.device = ref.device
+        self.refs = []      # every tensor the argument struct will point into
+
+    def keep(self, a):
+        """Attach the checked tensors to the argument struct ``a``: the struct holds raw
+        device addresses, so the tensors behind them must live as long as it does."""
+        a._tensors = tuple(self.refs)
+        return a
 
     def fail(self, msg):
         raise ValueError(f"{self.fn}: {msg}")
@@ -176,6 +183,7 @@ class _Checker:
         if t.device != self.device:
             self.fail(f"{name} is on {t.device}, expected {self.device} (the device of the "
                       f"token tensors)")
+        self.refs.append(t)
 
     def i32(self, name, t, numel=None, min_numel=None):
         import torch
@@ -214,7 +222,9 @@ def prefill_args(x, dt, A, B, C, chunk_size: int, cu_seqlens, cu_chunk_seqlens, 
                  num_computed=None, block_idx_last_computed=None,
                  block_idx_last_scheduled=None) -> PrefillArgs:
     """Fill an ssd_prefill_args from tensors (no device work).  block_size > 0 selects the
-    all cache mode: state_indices is then [S, max_blocks] (row stride taken from it)."""
+    all cache mode: state_indices is then [S, max_blocks] (row stride taken from it).  The
+    returned struct holds the tensors it points into (``_tensors``), so they live as long
+    as it does; the same holds for the other argument builders below."""
     import torch
     ck = _Checker("ssd_prefill", x)
     if x.dim() != 3 or B.dim() != 3 or C.dim() != 3 or dt.dim() != 2 or y.dim() != 3:
@@ -303,7 +313,7 @@ def prefill_args(x, dt, A, B, C, chunk_size: int, cu_seqlens, cu_chunk_seqlens, 
     a.num_computed = _dptr(num_computed)
     a.block_idx_last_computed = _dptr(block_idx_last_computed)
     a.block_idx_last_scheduled = _dptr(block_idx_last_scheduled)
-    return a
+    return ck.keep(a)
 
 
 def ssd_prefill_workspace_size(args: PrefillArgs) -> int:
@@ -406,7 +416,7 @@ def decode_args(x, dt, A, B, C, y, state_pool, state_indices, num_accepted_token
         a.idx_stride = state_indices.shape[1]
         a.block_idx_last_computed = _dptr(block_idx_last_computed)
         a.block_idx_last_scheduled = _dptr(block_idx_last_scheduled)
-    return a
+    return ck.keep(a)
 
 
 def ssd_state_update(x, dt, A, B, C, state_pool, state_indices, y=None, stream=None, **kw):
@@ -473,7 +483,7 @@ def conv1d_args(x, weight, bias, out, cu_seqlens, cu_chunk_seqlens, seq_idx,
     a.state_indices = _dptr(state_indices)
     a.has_initial_state = _dptr(has_initial_state)
     a.device_error_flag = _dptr(device_error_flag)
-    return a
+    return ck.keep(a)
 
 
 def ssd_conv1d_prefill(x, weight, bias, cu_seqlens, cu_chunk_seqlens, seq_idx, out=None,
@@ -526,7 +536,7 @@ def conv1d_update_args(x, weight, bias, out, conv_states, state_indices,
     a.state_indices = state_indices.data_ptr()
     a.null_block_id = int(null_block_id)
     a.device_error_flag = _dptr(device_error_flag)
-    return a
+    return ck.keep(a)
 
 
 def ssd_conv1d_update(x, weight, bias, conv_states, state_indices, out=None, stream=None,

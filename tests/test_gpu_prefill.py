@@ -311,3 +311,44 @@ def test_full_nemotron_prefix_cache():
     owned = set(int(v) for v in inp.state_indices)
     untouched = [s for s in range(inp.pool.shape[0]) if s not in owned]
     np.testing.assert_array_equal(got["pool"][untouched], inp.pool[untouched])
+
+
+def test_argument_struct_keeps_its_tensors_alive():
+    """An argument struct built from temporaries (every token, metadata and index tensor
+    dropped by the caller) still runs correctly after a garbage collection and a burst of
+    allocations that would reuse freed blocks: the struct holds the tensors it points into."""
+    import ctypes
+    import gc
+
+    from gpu_helpers import dev_f32, dev_i32, dev_token, prefill_metadata, torch
+    from selective_state_space_mamba2_amd import api
+    from selective_state_space_mamba2_amd._abi import check, lib
+    t = torch()
+    inp = _case(71, "bf16", 64, 128, 256, [600, 257, 90], [0, 40, 255])
+    cuc, sidx, last = prefill_metadata(inp)
+    y = t.full((inp.T, inp.H, inp.P), float("nan"), dtype=t.bfloat16, device="cuda")
+    pool = t.from_numpy(inp.pool).cuda()
+    states = t.full((len(sidx), inp.H, inp.P, inp.N), float("nan"), device="cuda")
+    flag = t.zeros(1, dtype=t.int32, device="cuda")
+
+    def build():
+        return api.prefill_args(
+            dev_token(inp, "x"), dev_token(inp, "dt"), dev_f32(inp.A), dev_token(inp, "B"),
+            dev_token(inp, "C"), inp.chunk_size, dev_i32(inp.cu_seqlens), dev_i32(cuc),
+            dev_i32(sidx), dev_i32(last), y, D=dev_f32(inp.D), state_pool=pool,
+            state_indices=dev_i32(inp.state_indices),
+            has_initial_state=dev_i32(inp.has_initial_state), write_final_to_pool=True,
+            chunk_states_out=states, device_error_flag=flag)
+
+    a = build()
+    gc.collect()
+    junk = [t.full((n,), -7, dtype=t.int32, device="cuda") for n in (1, 4, 17, 256, 4096) * 8]
+    ws = t.empty(max(api.ssd_prefill_workspace_size(a), 256), dtype=t.uint8, device="cuda")
+    check("ssd_prefill", lib().ssd_prefill(ctypes.byref(a), ws.data_ptr(), ws.numel(),
+                                           t.cuda.current_stream().cuda_stream))
+    t.cuda.synchronize()
+    assert int(flag.item()) == 0
+    got = dict(y=y.float().cpu().numpy().astype(np.float64), metadata=(cuc, sidx, last),
+               states=states.cpu().numpy().astype(np.float64), pool=pool.cpu().numpy())
+    check_prefill(inp, got, oracle_prefill(inp))
+    del junk
