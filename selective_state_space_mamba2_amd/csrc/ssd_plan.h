@@ -59,8 +59,9 @@ constexpr int cb_frag_base(int i) { return (i / 2) * (i / 2 + 1) + (i % 2) * (i 
 
 // Placement of the march kernel's work items on the 8 XCDs of the device.  Items (one per
 // sequence, head and head-dim slice, in sequence dispatch order) are cut into nblocks =
-// 8 * ceil(S*G / 8) contiguous blocks of bsize items; block j runs on XCD j % 8, which
-// receives workgroup ids w with w % 8 == j % 8.  The workgroups that read the same
+// 8 * ceil(S*G / 8) contiguous blocks of bsize items; block j runs on the XCD that
+// receives the workgroup ids w with w % 8 == j % 8 (one XCD per residue: the round-robin
+// dispatch starts at an XCD that varies between launches).  The workgroups that read the same
 // chunk's C.B^T / B^T / C fragments (one sequence and group) thus share an L2.  The grid
 // has nblocks * bsize workgroups; ids past the last item exit at once.
 struct MarchGrid {

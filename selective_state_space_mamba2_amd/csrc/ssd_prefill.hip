@@ -247,16 +247,17 @@ __device__ __forceinline__ void sequence_order(const PrefillParams& p, int* nch,
 }
 
 // The chain kernel's work items: (chunk k, head h) runs as workgroup 8 * slot + x, i.e. on
-// XCD x (workgroups are dispatched round-robin over the 8 XCDs).  The chains (sequence
-// rank q, head h), taken in the order c = q * H + h (longest sequences first), are cut into
-// 8 contiguous runs of equal work (chunks), one per XCD, and every run is laid out row by
-// row: row j holds the run's chains with more than j chunks, which are a prefix of the run
-// since lengths do not increase along it.  So all chunks of a chain share one XCD (the
-// publisher can leave the state in its L2), the heads of a (sequence, group) share one XCD
-// except at the cuts (their operand fragments are fetched into one L2 rather than into
-// every one), and every predecessor sits in an earlier row of the same XCD.  Slot of chain
-// c at row j: sum over the run of min(length, j), plus c minus the run's first chain;
-// entries no chunk claims (bad metadata, the padding of the last rows) hold -1.
+// the XCD of run x (workgroups are dispatched round-robin over the 8 XCDs, starting at an
+// XCD that varies from launch to launch, so the ids of one residue mod 8 share an XCD).
+// The chains (sequence rank q, head h), taken in the order c = q * H + h (longest sequences
+// first), are cut into 8 contiguous runs of equal work (chunks), one per XCD, and every run
+// is laid out row by row: row j holds the run's chains with more than j chunks, which are a
+// prefix of the run since lengths do not increase along it.  So all chunks of a chain share
+// one XCD (the publisher can leave the state in its L2), the heads of a (sequence, group)
+// share one XCD except at the cuts (their operand fragments are fetched into one L2 rather
+// than into every one), and every predecessor sits in an earlier row of the same XCD.  Slot
+// of chain c at row j: sum over the run of min(length, j), plus c minus the run's first
+// chain; entries no chunk claims (bad metadata, the padding of the last rows) hold -1.
 // `len_q` and `wq` are kOrderMaxSeqs + 1 ints of LDS each, `kinfo` C ints of LDS.
 __device__ void chain_items(const PrefillParams& p, const int* nch, const int* rank_of, int* len_q,
                             int* wq, int* kinfo) {
@@ -1167,10 +1168,12 @@ constexpr long long kChainWaitTicks = 100000000;   // ~1 s of the 100 MHz wall c
 // ring reuses its entries within a launch (chunk j+3 reads the entry chunk j+1 read, on
 // the same XCD), and an all-cache-mode pool entry may be the one the sequence's first
 // chunk read its initial state from, so both always go device-coherent.
-// The publisher picks the L2 form only for the checkpoint output, and only when
-// it runs on the XCD its workgroup id maps to (id mod 8, where a successor's id also
-// maps); it records its XCD and the form in the flag value.  A successor reads through L2
-// only when the flag says the L2 form on its own XCD, device-coherent otherwise, and a
+// The publisher picks the L2 form for the checkpoint output: its successor's workgroup id
+// is the same mod 8, and the XCD of workgroup id w is (w + rot) mod 8 with one rotation rot
+// for the whole launch (measured: the rotation changes from launch to launch, 0 or 7 in
+// eager launches and in graph replays, but never within one), so the two share an XCD.
+// The publisher records its XCD and the form in the flag value.  A successor reads through
+// L2 only when the flag says the L2 form on its own XCD, device-coherent otherwise, and a
 // state left in another XCD's L2 is reported (SSD_DEVERR_CHAIN_WAIT).  Neither side needs
 // a cache flush or invalidate: the publisher waits for its stores to complete before the
 // flag store, the successor issues its loads after it has seen the flag.
@@ -1488,10 +1491,10 @@ void k_chunk_chain(PrefillParams p) {
     const float dec = fast_exp(s_c[CS - 1]);
     const BufRes hb(chain_state(p, k, h, r, k - k0));
 
-    // the L2 form (plain stores, no wait for a write-through) when the successor maps to
-    // this XCD too (the last chunk has none) and the state goes to the checkpoint output (no
-    // line of it can sit in an L1)
-    const bool keep_l2 = !last && p.states && my_xcd == int(blockIdx.x % kXcds);
+    // the L2 form (plain stores, no wait for a write-through) when there is a successor
+    // (on this XCD: same id mod 8, one rotation per launch) and the state goes to the
+    // checkpoint output (no line of it can sit in an L1)
+    const bool keep_l2 = !last && p.states;
     // S_k into the row layout: lane L takes the accumulator values of lane (L%4)*16 + L/4
     const int src_b = ((lane & 3) * 16 + (lane >> 2)) * 4;
     f32x4_v hn[TNW][TP];
