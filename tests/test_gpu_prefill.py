@@ -313,6 +313,60 @@ def test_full_nemotron_prefix_cache():
     np.testing.assert_array_equal(got["pool"][untouched], inp.pool[untouched])
 
 
+
+def test_two_streams_at_once():
+    """Two independent chain-kernel prefills issued on two streams at the same time, several
+    times over: each gives exactly the outputs it gives alone and raises no device error
+    (the hand-off assumes that a predecessor and its successor, whose workgroup ids are
+    equal mod 8, run on one XCD also while another launch shares the device)."""
+    import torch
+    from gpu_helpers import dev_f32, dev_i32, dev_token, prefill_metadata
+    from selective_state_space_mamba2_amd import api
+    calls = []
+    for seed in (37, 38):
+        inp = _case(seed, "bf16", 64, 128, 256, [1500, 900, 2300, 400], [0, 300, 77, 255],
+                    H=16, G=2)
+        cuc, sidx, last = prefill_metadata(inp)
+        x, dt, B, C = (dev_token(inp, n) for n in ("x", "dt", "B", "C"))
+        md = [dev_i32(inp.cu_seqlens), dev_i32(cuc), dev_i32(sidx), dev_i32(last)]
+        pool0 = torch.from_numpy(inp.pool).cuda()
+        out = dict(y=torch.zeros_like(x), pool=pool0.clone(),
+                   states=torch.zeros(len(sidx), inp.H, 64, 128, device="cuda"),
+                   flag=torch.zeros(1, dtype=torch.int32, device="cuda"))
+        kw = dict(y=out["y"], D=dev_f32(inp.D), state_pool=out["pool"],
+                  state_indices=dev_i32(inp.state_indices),
+                  has_initial_state=dev_i32(inp.has_initial_state), write_final_to_pool=True,
+                  chunk_states_out=out["states"], device_error_flag=out["flag"])
+        a = api.prefill_args(x, dt, dev_f32(inp.A), B, C, 256, *md, **kw)
+        ws = torch.empty(max(api.ssd_prefill_workspace_size(a), 256), dtype=torch.uint8,
+                         device="cuda")
+        run = (lambda st, x=x, dt=dt, A=dev_f32(inp.A), B=B, C=C, md=md, kw=kw, ws=ws:
+               api.ssd_prefill(x, dt, A, B, C, 256, *md, workspace=ws, stream=st, **kw))
+        calls.append((run, out, pool0))
+    main = torch.cuda.current_stream()
+    ref = []
+    for run, out, pool0 in calls:
+        run(main)
+        torch.cuda.synchronize()
+        assert int(out["flag"].item()) == 0
+        ref.append({k: out[k].clone() for k in ("y", "states", "pool")})
+    side = torch.cuda.Stream()
+    for _ in range(4):
+        for run, out, pool0 in calls:
+            out["pool"].copy_(pool0)
+            out["y"].zero_()
+            out["states"].zero_()
+        side.wait_stream(main)
+        calls[0][0](main)
+        calls[1][0](side)
+        torch.cuda.synchronize()
+        for (run, out, pool0), r in zip(calls, ref):
+            assert int(out["flag"].item()) == 0
+            assert torch.equal(out["y"], r["y"])
+            assert torch.equal(out["states"], r["states"])
+            assert torch.equal(out["pool"], r["pool"])
+
+
 def test_argument_struct_keeps_its_tensors_alive():
     """An argument struct built from temporaries (every token, metadata and index tensor
     dropped by the caller) still runs correctly after a garbage collection and a burst of
