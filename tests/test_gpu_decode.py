@@ -208,3 +208,18 @@ def test_f16_pool_saturates_to_inf():
         err = np.abs(g[under] - st[under])
         assert np.all(err <= 2.0 ** -10 * np.abs(st[under]) + 1e-6 * scale), f"slot {slot}"
     assert n_inf > 0, "the case must overflow fp16 somewhere"
+
+
+@pytest.mark.parametrize("dtype,P,N,a_kind", [("bf16", 64, 256, "scalar"),
+                                              ("f32", 128, 128, "scalar"),
+                                              ("bf16", 1, 16, "diag")])
+def test_largest_token_count_and_state(dtype, P, N, a_kind):
+    """The instantiated maxima: 1+15 speculative tokens per row (every restore column
+    1..16 drawn) with the largest state per head (P*N = 16384) for the dense kernel, and
+    the same token count for the Mamba1 kernel."""
+    H = 4 if a_kind == "scalar" else 64
+    inp = make_decode(70 + P, in_dtype=dtype, B_pad=8, n_live=5, ntok=16, H=H, P=P, G=1, N=N,
+                      pool_slots=5 * 16 + 2, a_kind=a_kind)
+    got = run_decode(inp)
+    assert got["flag"] == 0
+    _check(inp, got)
