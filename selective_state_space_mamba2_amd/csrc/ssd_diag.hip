@@ -16,6 +16,8 @@
 // through LDS with coalesced loads (64 channels = 128 B per token for bf16), delta is
 // prepared once per (token, channel) while staging, and y leaves through an LDS tile as
 // coalesced rows.  Checkpoints are written at the chunk ends listed by the chunk metadata.
+#include <algorithm>
+#include <atomic>
 #include <cstdint>
 #include <type_traits>
 
@@ -34,20 +36,62 @@ namespace ssd {
 // lanes and a workgroup owns CH = 256 / LPC channels.
 template <int NS, int SPL>
 struct DiagCfg {
-  static_assert(SPL % 4 == 0 && NS % SPL == 0, "states move to and from the pool four at a time");
+  static_assert((SPL % 4 == 0 || SPL == 2) && NS % SPL == 0, "states move 4 (or 2) at a time");
   static constexpr int N = NS, LPC = N / SPL, CH = 256 / LPC;
 };
+
+// The SPL states of a lane to and from the pool (any pool dtype) and the fp32 checkpoint
+// output: four at a time, or two (8 bytes of fp32, 4 of a 2-byte pool) when SPL is 2.
+template <int SPL>
+__device__ __forceinline__ void diag_pool_ld(const void* pool, int kind, int64_t e, float* h) {
+  if constexpr (SPL == 2) {
+    if (kind == SSD_F32) {
+      const float2_v v = *reinterpret_cast<const float2_v*>(static_cast<const float*>(pool) + e);
+      h[0] = v.x; h[1] = v.y;
+    } else {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(pool) + e);
+      h[0] = kind == SSD_BF16 ? bf16_to_f32(bf16_t(w & 0xffffu)) : f16_to_f32(w);
+      h[1] = kind == SSD_BF16 ? bf16_to_f32(bf16_t(w >> 16)) : f16_to_f32(w >> 16);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < SPL; i += 4) {
+      const float4_v v = pool_ld4(pool, kind, e + i);
+      h[i] = v.x; h[i + 1] = v.y; h[i + 2] = v.z; h[i + 3] = v.w;
+    }
+  }
+}
+template <int SPL>
+__device__ __forceinline__ void diag_pool_st(void* pool, int kind, int64_t e, const float* h) {
+  if constexpr (SPL == 2) {
+    if (kind == SSD_F32) {
+      *reinterpret_cast<float2_v*>(static_cast<float*>(pool) + e) = float2_v{h[0], h[1]};
+    } else {
+      *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(pool) + e) =
+          kind == SSD_BF16 ? pack_bf16x2(h[0], h[1]) : pack_f16x2(h[0], h[1]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < SPL; i += 4)
+      pool_st4(pool, kind, e + i, float4_v{h[i], h[i + 1], h[i + 2], h[i + 3]});
+  }
+}
 
 // Sum of v over the aligned group of LPC (2, 4, 8 or 16) lanes, on every lane of the
 // group: DPP quad permutations (lane ^ 1, then lane ^ 2), then rotations by 4 and 8 lanes
 // inside the 16-lane row, feed the adds directly, with no LDS trip.
 template <int LPC>
 __device__ __forceinline__ float group_sum(float v) {
-  static_assert(LPC == 1 || LPC == 2 || LPC == 4 || LPC == 16, "lanes per channel within a row");
+  static_assert(LPC == 1 || LPC == 2 || LPC == 4 || LPC == 8 || LPC == 16,
+                "lanes per channel within a row");
   if constexpr (LPC >= 2)
     v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
   if constexpr (LPC >= 4)
     v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
+  if constexpr (LPC == 8) {
+    // the other quad of the 8-lane half row: row_half_mirror (lane i of the half reads 7-i)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, true));
+  }
   if constexpr (LPC >= 16) {
     // quad sums q0..q3 of the row: + row_ror:4 gives q_i + q_(i+1), + row_ror:8 the total
     v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x124, 0xF, 0xF, true));
@@ -63,8 +107,15 @@ __host__ __device__ __forceinline__ int diag_blocks_per_group(int H, int G, int 
 }
 
 // kScalarA: A is [H] (Mamba2 at head_dim 1), else [H, NS] (Mamba1).
+// The channels of one workgroup: [c0, c0 + nch) of group g, sequence r; `lead` is the
+// workgroup that reports the sequence's metadata and slot faults (one per sequence).
+struct DiagWork {
+  int r, g, c0, nch;
+  bool lead;
+};
+
 template <typename T, int NS, int SPL, bool kScalarA>
-__global__ __launch_bounds__(256) void k_diag_scan(PrefillParams p) {
+__device__ __forceinline__ void diag_body(const PrefillParams& p, const DiagWork w) {
   using Cfg = DiagCfg<NS, SPL>;
   constexpr int N = NS;                // states per channel
   constexpr int LPC = Cfg::LPC;        // lanes per channel
@@ -80,12 +131,8 @@ __global__ __launch_bounds__(256) void k_diag_scan(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) float s_c[TT][N];
 
   const int tid = threadIdx.x;
-  const int r = blockIdx.y;
+  const int r = w.r, g = w.g, c0 = w.c0, nch = w.nch;
   const int H = p.H, HPG = p.H / p.G;
-  const int nb = diag_blocks_per_group(H, p.G, CH);
-  const int g = blockIdx.x / nb, jb = blockIdx.x % nb;
-  const int c0 = g * HPG + jb * CH;               // first channel of the workgroup
-  const int nch = min(CH, HPG - jb * CH);         // channels of the workgroup (all one group)
   const int cl = tid / LPC, ng = tid % LPC;
   const int c = c0 + cl;
   const bool valid = cl < nch;
@@ -93,7 +140,7 @@ __global__ __launch_bounds__(256) void k_diag_scan(PrefillParams p) {
   const int t0 = p.cu_seqlens[r], t1 = p.cu_seqlens[r + 1];
   int k = r == 0 ? 0 : p.last_chunk[r - 1] + 1;
   const int klast = p.last_chunk[r];
-  const bool first_wg = blockIdx.x == 0;
+  const bool first_wg = w.lead;
   if (t0 < 0 || t1 > p.T || t1 <= t0 || k < 0 || klast < k || klast >= p.C || p.cu_chunk[k] != t0 ||
       p.cu_chunk[klast + 1] != t1) {
     if (tid == 0 && first_wg) raise_flag(p.flag, SSD_DEVERR_CHUNK_RANGE);
@@ -116,12 +163,7 @@ __global__ __launch_bounds__(256) void k_diag_scan(PrefillParams p) {
 #pragma unroll
     for (int i = 0; i < NA; ++i) A2[i] = (kScalarA ? p.A[c] : p.A[c * N + ng * SPL + i]) * kLog2e;
     if (src >= 0) {
-      const int64_t e = int64_t(src) * p.slot_stride + int64_t(c) * N + ng * SPL;
-#pragma unroll
-      for (int i = 0; i < SPL; i += 4) {
-        const float4_v v = pool_ld4(p.pool, p.pool_kind, e + i);
-        h[i] = v.x; h[i + 1] = v.y; h[i + 2] = v.z; h[i + 3] = v.w;
-      }
+      diag_pool_ld<SPL>(p.pool, p.pool_kind, int64_t(src) * p.slot_stride + int64_t(c) * N + ng * SPL, h);
     }
   } else {
 #pragma unroll
@@ -142,15 +184,17 @@ __global__ __launch_bounds__(256) void k_diag_scan(PrefillParams p) {
   constexpr int NBCI = (NBC + 255) / 256;        // ... per thread
   T rd[NE], rx[NE];
   float4_v rbc[NBCI];
-  // Vector path (bf16, 8 channels per thread): thread t owns channels 8*(t % 8) .. +7 of
-  // tile row t / 8, moved as one 16-byte access per tensor; it needs whole 8-channel
-  // groups (H/G % 8 == 0) and 16-byte aligned rows.  Otherwise one element per access.
-  constexpr bool kVecT = std::is_same<T, bf16_t>::value && NE == 8 && CH == 64;
+  // Vector path (bf16, 8 channels per thread): thread t owns channels 8*(t % VPR) .. +7 of
+  // tile row t / VPR (VPR = CH / 8 threads per row; rows past the tile idle), moved as one
+  // 16-byte access per tensor; it needs whole 8-channel groups (H/G % 8 == 0) and 16-byte
+  // aligned rows.  Otherwise one element per access.
+  constexpr int VPR = CH / 8;
+  constexpr bool kVecT = std::is_same<T, bf16_t>::value && CH % 8 == 0 && 256 / VPR >= TT;
   const bool vec = kVecT && HPG % 8 == 0 && p.x_st % 8 == 0 && p.dt_st % 8 == 0 &&
                    p.y_st % 8 == 0 &&
                    ((reinterpret_cast<uintptr_t>(p.x) | reinterpret_cast<uintptr_t>(p.dt) |
                      reinterpret_cast<uintptr_t>(p.y)) & 15) == 0;
-  const int vtt = tid / 8, vc8 = (tid % 8) * 8, vch = c0 + vc8;
+  const int vtt = tid / VPR, vc8 = (tid % VPR) * 8, vch = c0 + vc8;
   const bool vin = vc8 < nch;
   u32x4_v vd = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
   auto fetch = [&](int tb) {
@@ -198,10 +242,12 @@ __global__ __launch_bounds__(256) void k_diag_scan(PrefillParams p) {
         dv8[2 * k] = in ? p.prep(__uint_as_float(vd[k] << 16), vch + 2 * k) : 0.f;
         dv8[2 * k + 1] = in ? p.prep(__uint_as_float(vd[k] & 0xffff0000u), vch + 2 * k + 1) : 0.f;
       }
-      *reinterpret_cast<float4_v*>(&s_d[vtt][vc8]) = float4_v{dv8[0], dv8[1], dv8[2], dv8[3]};
-      *reinterpret_cast<float4_v*>(&s_d[vtt][vc8 + 4]) = float4_v{dv8[4], dv8[5], dv8[6], dv8[7]};
-      *reinterpret_cast<float4_v*>(&s_x[vtt][vc8]) = float4_v{xv8[0], xv8[1], xv8[2], xv8[3]};
-      *reinterpret_cast<float4_v*>(&s_x[vtt][vc8 + 4]) = float4_v{xv8[4], xv8[5], xv8[6], xv8[7]};
+      if (vtt < TT) {
+        *reinterpret_cast<float4_v*>(&s_d[vtt][vc8]) = float4_v{dv8[0], dv8[1], dv8[2], dv8[3]};
+        *reinterpret_cast<float4_v*>(&s_d[vtt][vc8 + 4]) = float4_v{dv8[4], dv8[5], dv8[6], dv8[7]};
+        *reinterpret_cast<float4_v*>(&s_x[vtt][vc8]) = float4_v{xv8[0], xv8[1], xv8[2], xv8[3]};
+        *reinterpret_cast<float4_v*>(&s_x[vtt][vc8 + 4]) = float4_v{xv8[4], xv8[5], xv8[6], xv8[7]};
+      }
     } else {
 #pragma unroll
       for (int u = 0; u < NE; ++u) {
@@ -272,19 +318,14 @@ __global__ __launch_bounds__(256) void k_diag_scan(PrefillParams p) {
 #pragma unroll 1
         for (; tt < cut; ++tt) steps(tt, std::integral_constant<int, 1>{});
         if (valid && p.states) {   // end of chunk k: checkpoint
-          float* dst = p.states + (int64_t(k) * H + c) * N + ng * SPL;
-#pragma unroll
-          for (int i = 0; i < SPL; i += 4)
-            *reinterpret_cast<float4_v*>(dst + i) = float4_v{h[i], h[i + 1], h[i + 2], h[i + 3]};
+          diag_pool_st<SPL>(p.states, SSD_F32, (int64_t(k) * H + c) * N + ng * SPL, h);
         }
         if (valid && p.block_size > 0) {   // the all cache mode: a block ends here
           const int col = block_end_col(p, r, t0, p.cu_chunk[k], next_end, report);
           const int bslot = col >= 0 ? pool_slot(p, r, col, report) : -1;
           if (bslot >= 0) {
-            const int64_t e = int64_t(bslot) * p.slot_stride + int64_t(c) * N + ng * SPL;
-#pragma unroll
-            for (int i = 0; i < SPL; i += 4)
-              pool_st4(p.pool, p.pool_kind, e + i, float4_v{h[i], h[i + 1], h[i + 2], h[i + 3]});
+            diag_pool_st<SPL>(p.pool, p.pool_kind,
+                              int64_t(bslot) * p.slot_stride + int64_t(c) * N + ng * SPL, h);
           }
         }
         ++k;
@@ -317,10 +358,36 @@ __global__ __launch_bounds__(256) void k_diag_scan(PrefillParams p) {
   }
   if (k != klast + 1 && tid == 0 && first_wg) raise_flag(p.flag, SSD_DEVERR_CHUNK_RANGE);
   if (valid && fin >= 0) {
-    const int64_t e = int64_t(fin) * p.slot_stride + int64_t(c) * N + ng * SPL;
-#pragma unroll
-    for (int i = 0; i < SPL; i += 4)
-      pool_st4(p.pool, p.pool_kind, e + i, float4_v{h[i], h[i + 1], h[i + 2], h[i + 3]});
+    diag_pool_st<SPL>(p.pool, p.pool_kind, int64_t(fin) * p.slot_stride + int64_t(c) * N + ng * SPL, h);
+  }
+}
+
+// One workgroup per (group, block of CH channels) and sequence (blockIdx.y).
+template <typename T, int NS, int SPL, bool kScalarA>
+__global__ __launch_bounds__(256) void k_diag_scan(PrefillParams p) {
+  constexpr int CH = DiagCfg<NS, SPL>::CH;
+  const int HPG = p.H / p.G, nb = diag_blocks_per_group(p.H, p.G, CH);
+  const int g = blockIdx.x / nb, jb = blockIdx.x % nb;
+  diag_body<T, NS, SPL, kScalarA>(
+      p, DiagWork{int(blockIdx.y), g, g * HPG + jb * CH, min(CH, HPG - jb * CH), blockIdx.x == 0});
+}
+
+// Mamba1 (one group) in workgroups of two sizes: per sequence nbig blocks of 64 channels
+// with 4 states per lane over channels [0, 64 nbig), then nsmall blocks of 32 channels with
+// 2 states per lane over the rest; every sequence's large workgroups come first in the grid.
+// Dispatched one workgroup per CU per pass, a grid of two large to one small workgroup puts
+// two of each on every CU instead of three large ones on half of the CUs and two on the
+// rest (the work of a small workgroup is about 0.6 of a large one's).
+template <typename T>
+__global__ __launch_bounds__(256) void k_diag_scan_mixed(PrefillParams p, int nbig, int nsmall) {
+  const int b = blockIdx.x;
+  if (b < p.S * nbig) {
+    const int r = b / nbig, j = b - r * nbig;
+    diag_body<T, kDiagN, 4, false>(p, DiagWork{r, 0, 64 * j, 64, j == 0});
+  } else {
+    const int b2 = b - p.S * nbig, r = b2 / nsmall, j = b2 - r * nsmall;
+    const int c0 = 64 * nbig + 32 * j;
+    diag_body<T, kDiagN, 2, false>(p, DiagWork{r, 0, c0, min(32, p.H - c0), nbig == 0 && j == 0});
   }
 }
 
@@ -331,8 +398,53 @@ static void launch_diag(const PrefillParams& p, hipStream_t s) {
   hipLaunchKernelGGL((k_diag_scan<T, NS, SPL, kScalarA>), grid, dim3(256), 0, s, p);
 }
 
+// CUs of the current device (cached per device; 256 on MI355X).
+static int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// The Mamba1 scan's grid: the uniform one (64-channel workgroups), or the mixed one when
+// it spreads the work more evenly over the CUs.  Model: workgroups land one per CU per pass
+// in grid order, a CU's time is its large workgroups plus kSmallCost per small one.
+constexpr double kSmallCost = 0.6;
+struct Mamba1Grid {
+  bool mixed;
+  int nbig, nsmall;
+};
+static Mamba1Grid mamba1_grid(int S, int H, int cus) {
+  const int nu = S * ((H + 63) / 64);
+  const double t_uni = double((nu + cus - 1) / cus);
+  const int nbig = 2 * (H / 160), nsmall = (H - 64 * nbig + 31) / 32;
+  if (S <= 0 || nsmall <= 0) return {false, 0, 0};
+  const int big = S * nbig, total = S * (nbig + nsmall);
+  double t_mix = 0.0;
+  for (int c = 0; c < cus && c < total; ++c) {
+    const int nb_c = c < big ? (big - 1 - c) / cus + 1 : 0;
+    const int ns_c = c < total ? (total - 1 - c) / cus + 1 - nb_c : 0;
+    t_mix = std::max(t_mix, nb_c + kSmallCost * ns_c);
+  }
+  return {t_mix < t_uni - 0.05, nbig, nsmall};
+}
+
 template <typename T>
 static hipError_t launch_diag_t(const PrefillParams& p, bool scalar_a, hipStream_t s) {
+  if (!scalar_a && p.N == kDiagN && p.G == 1) {
+    const Mamba1Grid mg = mamba1_grid(p.S, p.H, device_cus());
+    if (mg.mixed) {
+      hipLaunchKernelGGL((k_diag_scan_mixed<T>), dim3(p.S * (mg.nbig + mg.nsmall)), dim3(256), 0, s,
+                         p, mg.nbig, mg.nsmall);
+      return hipSuccess;
+    }
+  }
   if (!scalar_a && p.N == kDiagN) launch_diag<T, 16, SSD_DIAG_SPL, false>(p, s);
   else if (scalar_a && p.N == 16) launch_diag<T, 16, 4, true>(p, s);
   else if (scalar_a && p.N == 128) launch_diag<T, 128, 8, true>(p, s);

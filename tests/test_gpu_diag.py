@@ -93,3 +93,19 @@ def test_full_mamba1_long_diag():
     assert len(got["metadata"][1]) == 64
     chans = [0, 2501, 5119]
     check_prefill(inp, got, oracle_prefill(inp, seqs=[3], heads=chans), heads=chans)
+
+
+@pytest.mark.parametrize("dtype,pool", [("bf16", "f32"), ("bf16", "bf16"), ("f32", "f16")])
+def test_diag_mixed_workgroup_grid(dtype, pool):
+    """A Mamba1 batch wide enough (4 sequences x 5120 channels) for the grid of 64-channel
+    workgroups with 4 states per lane and 32-channel ones with 2 states per lane: every
+    channel of both kinds, its checkpoints and its pool entries against the oracle."""
+    from gpu_helpers import pool_tol, rounded_pool
+    inp = make_prefill(44, in_dtype=dtype, H=5120, P=1, G=1, N=16, chunk_size=64,
+                       lengths=[150, 97, 130, 64], num_computed=[0, 5, 60, 3], a_kind="diag",
+                       init="pool", pool_slots=8)
+    if pool != "f32":
+        rounded_pool(inp, pool)
+    got = run_prefill(inp)
+    assert got["flag"] == 0
+    check_prefill(inp, got, oracle_prefill(inp), pool_tol=pool_tol(inp))

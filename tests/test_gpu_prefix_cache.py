@@ -132,14 +132,16 @@ def test_prefill_writes_every_block_entry(dtype, P, N, cs, bs, write_final):
     _check(inp, got, refs, writes, TOL[dtype])
 
 
+@pytest.mark.parametrize("H", [200, 5120])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("write_final", [True, False])
-def test_prefill_diag_writes_every_block_entry(dtype, write_final):
-    """The Mamba1 scan (diagonal A [200, 16]; 200 channels leave a ragged last workgroup) in
-    the all cache mode: y, the chunk states, every block-end entry and the final entry."""
+def test_prefill_diag_writes_every_block_entry(dtype, write_final, H):
+    """The Mamba1 scan (diagonal A [H, 16]; 200 channels leave a ragged last workgroup, 5120
+    run the grid of 64- and 32-channel workgroups) in the all cache mode: y, the chunk
+    states, every block-end entry and the final entry."""
     cs, bs = 64, 128
     lengths, nc = _lengths(cs, bs)
-    inp, table, lc, ls = _case(55, dtype, 1, 16, cs, bs, lengths, nc, H=200, G=1,
+    inp, table, lc, ls = _case(55, dtype, 1, 16, cs, bs, lengths, nc, H=H, G=1,
                                a_kind="diag")
     got = _run(inp, table, bs, lc, ls, write_final=write_final)
     refs, writes = _expected(inp, table, bs, lc, ls, write_final)
