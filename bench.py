@@ -565,7 +565,7 @@ def bench_diag(torch, steps, warmup, with_cpu=True, cpu_budget_s=10.0):
     import ctypes
     import numpy as np
     from selective_state_space_mamba2_amd import api
-    from selective_state_space_mamba2_amd._abi import check, lib
+    from selective_state_space_mamba2_amd._abi import SSD_PREFILL_MAX_KERNELS, check, lib
     from selective_state_space_mamba2_amd.inputs import workload
     inp = workload("mamba1_long_diag")
     cuc, sidx, last = api.ssd_build_chunk_metadata(inp.cu_seqlens, None, inp.chunk_size)
@@ -580,6 +580,11 @@ def bench_diag(torch, steps, warmup, with_cpu=True, cpu_budget_s=10.0):
     flag = _error_flag(torch)
     a = api.prefill_args(x, dt, A, B, Cm, inp.chunk_size, *md, y, D=D, chunk_states_out=states,
                          device_error_flag=flag)
+    nk = ctypes.c_int32(0)
+    names = (ctypes.c_char_p * SSD_PREFILL_MAX_KERNELS)()
+    check("ssd_prefill_kernel_count", lib().ssd_prefill_kernel_count(ctypes.byref(a),
+                                                                     ctypes.byref(nk), names))
+    kname = names[0].decode()    # the uniform or the mixed-workgroup grid
     sp = torch.cuda.current_stream().cuda_stream
     for _ in range(warmup):
         check("ssd_prefill", lib().ssd_prefill(ctypes.byref(a), None, 0, sp))
@@ -607,11 +612,11 @@ def bench_diag(torch, steps, warmup, with_cpu=True, cpu_budget_s=10.0):
            "ms_per_step": round(ms, 5), "kernel_ms": round(kms, 5),
            "roofline": _roofline("alu", lane_ops / (kms * 1e-3) / 1e12,
                                  round(VALU_LANE_OPS / 1e12, 2), "T lane-op/s",
-                                 _counter_traffic("k_diag_scan", "mamba1_long_diag",
+                                 _counter_traffic(kname, "mamba1_long_diag",
                                                   _source_digest("ssd_diag.hip", "ssd_device.h")),
-                                 "k_diag_scan"),
+                                 kname),
            "hbm": _roofline("hbm", w["bytes"] / (kms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s",
-                            None, "k_diag_scan", w),
+                            None, kname, w),
            "hbm_gb_s": round(w["bytes"] / (kms * 1e-3) / 1e9, 1), "alg_bytes": w["bytes"]}
     del x, dt, B, Cm, y
     if with_cpu:

@@ -256,7 +256,9 @@ typedef struct ssd_prefill_args {
 
 /* Number of kernels ssd_prefill launches for these arguments (2 for SSD_A_SCALAR, 1 for
  * SSD_A_DIAG, 0 for an empty batch) and, when `names` is not NULL, a static name for each
- * kernel in launch order (names must hold SSD_PREFILL_MAX_KERNELS entries). */
+ * kernel in launch order (names must hold SSD_PREFILL_MAX_KERNELS entries).  The diagonal
+ * scan's grid, and so its kernel's name, depends on the batch and on the current device's
+ * compute-unit count (256 when no device is present). */
 ssd_status ssd_prefill_kernel_count(const ssd_prefill_args* args, int32_t* count,
                                     const char** names);
 

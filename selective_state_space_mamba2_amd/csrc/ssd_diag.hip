@@ -435,15 +435,17 @@ static Mamba1Grid mamba1_grid(int S, int H, int cus) {
   return {t_mix < t_uni - 0.05, nbig, nsmall};
 }
 
+bool diag_mixed_grid(bool scalar_a, int S, int H, int G, int N) {
+  return !scalar_a && N == kDiagN && G == 1 && mamba1_grid(S, H, device_cus()).mixed;
+}
+
 template <typename T>
 static hipError_t launch_diag_t(const PrefillParams& p, bool scalar_a, hipStream_t s) {
-  if (!scalar_a && p.N == kDiagN && p.G == 1) {
+  if (diag_mixed_grid(scalar_a, p.S, p.H, p.G, p.N)) {
     const Mamba1Grid mg = mamba1_grid(p.S, p.H, device_cus());
-    if (mg.mixed) {
-      hipLaunchKernelGGL((k_diag_scan_mixed<T>), dim3(p.S * (mg.nbig + mg.nsmall)), dim3(256), 0, s,
-                         p, mg.nbig, mg.nsmall);
-      return hipSuccess;
-    }
+    hipLaunchKernelGGL((k_diag_scan_mixed<T>), dim3(p.S * (mg.nbig + mg.nsmall)), dim3(256), 0, s,
+                       p, mg.nbig, mg.nsmall);
+    return hipSuccess;
   }
   if (!scalar_a && p.N == kDiagN) launch_diag<T, 16, SSD_DIAG_SPL, false>(p, s);
   else if (scalar_a && p.N == 16) launch_diag<T, 16, 4, true>(p, s);

@@ -166,10 +166,13 @@ ssd_status ssd_prefill_kernel_count(const ssd_prefill_args* a, int32_t* count,
   static const char* const kChunked[] = {"k_chunk_prep", "k_chunk_march"};
   static const char* const kChain[] = {"k_chunk_prep", "k_chunk_chain"};
   static const char* const kDiag[] = {"k_diag_scan"};
+  static const char* const kDiagMixed[] = {"k_diag_scan_mixed"};
   *count = 0;
   if (a->num_seqs == 0) return SSD_OK;
-  const char* const* list = plan.kind == ssd::PrefillKind::kChunked
-                                ? (plan.chain ? kChain : kChunked) : kDiag;
+  const char* const* list =
+      plan.kind == ssd::PrefillKind::kChunked ? (plan.chain ? kChain : kChunked)
+      : ssd::diag_mixed_grid(a->a_kind == SSD_A_SCALAR, a->num_seqs, a->H, a->G, a->N)
+          ? kDiagMixed : kDiag;
   *count = plan.kind == ssd::PrefillKind::kChunked ? 2 : 1;
   if (names)
     for (int i = 0; i < *count; ++i) names[i] = list[i];

@@ -137,6 +137,9 @@ hipError_t launch_chunked_prefill(int variant, const PrefillParams& p, hipStream
 // per-(channel, state) A [H, N].
 hipError_t launch_diag_prefill(int in_dtype, bool scalar_a, const PrefillParams& p, hipStream_t s,
                                void* const* events);
+// True when the sequential scan of S sequences runs the grid of 64- and 32-channel
+// workgroups (k_diag_scan_mixed) on the current device, false for k_diag_scan.
+bool diag_mixed_grid(bool scalar_a, int S, int H, int G, int N);
 hipError_t launch_state_update(int in_dtype, const DecodeParams& p, hipStream_t s,
                                void* const* events);
 

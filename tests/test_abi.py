@@ -177,6 +177,11 @@ def test_kernel_count():
     diag = _good_prefill(a_kind=_abi.SSD_A_DIAG, H=64, P=1, G=1, N=16, x_stride_t=64,
                          y_stride_t=64, dt_stride_t=64, bc_stride_t=16)
     assert lib().ssd_prefill_kernel_count(ctypes.byref(diag), ctypes.byref(n), names) == 0
+    # 64 channels in a small batch: two 32-channel workgroups per sequence beat one of 64
+    assert n.value == 1 and names[0] == b"k_diag_scan_mixed"
+    diag.H = 200   # 2 + 3 workgroups per sequence would not shorten the launch
+    diag.x_stride_t = diag.y_stride_t = diag.dt_stride_t = 200
+    assert lib().ssd_prefill_kernel_count(ctypes.byref(diag), ctypes.byref(n), names) == 0
     assert n.value == 1 and names[0] == b"k_diag_scan"
     empty = _good_prefill(T=0, num_seqs=0, num_chunks=0)
     assert lib().ssd_prefill_kernel_count(ctypes.byref(empty), ctypes.byref(n), None) == 0
