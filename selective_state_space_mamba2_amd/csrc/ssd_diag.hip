@@ -376,8 +376,11 @@ __global__ __launch_bounds__(256) void k_diag_scan(PrefillParams p) {
 // with 4 states per lane over channels [0, 64 nbig), then nsmall blocks of 32 channels with
 // 2 states per lane over the rest; every sequence's large workgroups come first in the grid.
 // Dispatched one workgroup per CU per pass, a grid of two large to one small workgroup puts
-// two of each on every CU instead of three large ones on half of the CUs and two on the
-// rest (the work of a small workgroup is about 0.6 of a large one's).
+// two large and one small workgroup on every CU instead of three large ones on half of the
+// CUs and two on the rest (the work of a small workgroup is about 0.6 of a large one's).
+// The two small workgroups of one 64-channel block split each 128-byte row segment of x,
+// delta and y; their workgroup ids differ by 8, which puts them on the same XCD (ids go
+// round-robin over the 8 XCDs), so the segment is fetched into one L2, not two.
 template <typename T>
 __global__ __launch_bounds__(256) void k_diag_scan_mixed(PrefillParams p, int nbig, int nsmall) {
   const int b = blockIdx.x;
@@ -385,7 +388,11 @@ __global__ __launch_bounds__(256) void k_diag_scan_mixed(PrefillParams p, int nb
     const int r = b / nbig, j = b - r * nbig;
     diag_body<T, kDiagN, 4, false>(p, DiagWork{r, 0, 64 * j, 64, j == 0});
   } else {
-    const int b2 = b - p.S * nbig, r = b2 / nsmall, j = b2 - r * nsmall;
+    // ids base .. base+15 take the even and then the odd halves of blocks base/2 .. +7
+    // (a last partial run of 16 keeps the identity order)
+    const int i = b - p.S * nbig, base = i & ~15;
+    const int b2 = base + 16 <= p.S * nsmall ? base + 2 * (i & 7) + ((i >> 3) & 1) : i;
+    const int r = b2 / nsmall, j = b2 - r * nsmall;
     const int c0 = 64 * nbig + 32 * j;
     diag_body<T, kDiagN, 2, false>(p, DiagWork{r, 0, c0, min(32, p.H - c0), nbig == 0 && j == 0});
   }
