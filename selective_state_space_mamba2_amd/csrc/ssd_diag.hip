@@ -40,6 +40,30 @@ struct DiagCfg {
   static constexpr int N = NS, LPC = N / SPL, CH = 256 / LPC;
 };
 
+constexpr int kDiagTT = 32;   // tokens per LDS tile
+
+// A workgroup's LDS: one token tile of delta, x and y per channel and of B and C per state.
+// Declared by the kernels (one object shared by every body a kernel inlines).
+template <int NS, int SPL>
+struct DiagSmem {
+  static constexpr int CH = DiagCfg<NS, SPL>::CH;
+  __attribute__((aligned(16))) float d[kDiagTT][CH];
+  __attribute__((aligned(16))) float x[kDiagTT][CH];
+  __attribute__((aligned(16))) float y[kDiagTT][CH];
+  __attribute__((aligned(16))) float b[kDiagTT][NS];
+  __attribute__((aligned(16))) float c[kDiagTT][NS];
+};
+
+// The 16-byte path of x, delta and y (bf16, 8 channels per thread): whole 8-channel groups
+// (H/G % 8 == 0), row strides in whole 8-element units and 16-byte aligned tensors.
+template <typename T, int CH>
+__device__ __forceinline__ bool diag_vec_ok(const PrefillParams& p) {
+  constexpr bool kVecT = std::is_same<T, bf16_t>::value && CH % 8 == 0 && 256 / (CH / 8) >= kDiagTT;
+  return kVecT && (p.H / p.G) % 8 == 0 && p.x_st % 8 == 0 && p.dt_st % 8 == 0 && p.y_st % 8 == 0 &&
+         ((reinterpret_cast<uintptr_t>(p.x) | reinterpret_cast<uintptr_t>(p.dt) |
+           reinterpret_cast<uintptr_t>(p.y)) & 15) == 0;
+}
+
 // The SPL states of a lane to and from the pool (any pool dtype) and the fp32 checkpoint
 // output: four at a time, or two (8 bytes of fp32, 4 of a 2-byte pool) when SPL is 2.
 template <int SPL>
@@ -114,21 +138,25 @@ struct DiagWork {
   bool lead;
 };
 
-template <typename T, int NS, int SPL, bool kScalarA>
-__device__ __forceinline__ void diag_body(const PrefillParams& p, const DiagWork w) {
+// kVec: the 16-byte path (diag_vec_ok holds), a template argument so that the two paths'
+// loads never meet in one loop (a load of one path would otherwise be waited for in the
+// other).
+template <typename T, int NS, int SPL, bool kScalarA, bool kVec>
+__device__ __forceinline__ void diag_body(const PrefillParams& p, const DiagWork w,
+                                          DiagSmem<NS, SPL>& sm) {
   using Cfg = DiagCfg<NS, SPL>;
   constexpr int N = NS;                // states per channel
   constexpr int LPC = Cfg::LPC;        // lanes per channel
   constexpr int CH = Cfg::CH;          // channels per workgroup
-  constexpr int TT = 32;               // tokens per LDS tile
+  constexpr int TT = kDiagTT;          // tokens per LDS tile
   constexpr int U = SSD_DIAG_UNROLL;   // tokens per step of the scan (divides TT)
   constexpr int NA = kScalarA ? 1 : SPL;   // decay factors per lane and token
   static_assert(TT % U == 0, "unroll");
-  __shared__ __attribute__((aligned(16))) float s_d[TT][CH];
-  __shared__ __attribute__((aligned(16))) float s_x[TT][CH];
-  __shared__ __attribute__((aligned(16))) float s_y[TT][CH];
-  __shared__ __attribute__((aligned(16))) float s_b[TT][N];
-  __shared__ __attribute__((aligned(16))) float s_c[TT][N];
+  auto& s_d = sm.d;
+  auto& s_x = sm.x;
+  auto& s_y = sm.y;
+  auto& s_b = sm.b;
+  auto& s_c = sm.c;
 
   const int tid = threadIdx.x;
   const int r = w.r, g = w.g, c0 = w.c0, nch = w.nch;
@@ -183,23 +211,32 @@ __device__ __forceinline__ void diag_body(const PrefillParams& p, const DiagWork
   constexpr int NBC = TT * 2 * (N / 4);          // B / C float4 items per tile
   constexpr int NBCI = (NBC + 255) / 256;        // ... per thread
   T rd[NE], rx[NE];
-  float4_v rbc[NBCI];
+  T rbc[NBCI][4];   // raw: converted when staged, so the fetch does not wait for its loads
   // Vector path (bf16, 8 channels per thread): thread t owns channels 8*(t % VPR) .. +7 of
   // tile row t / VPR (VPR = CH / 8 threads per row; rows past the tile idle), moved as one
-  // 16-byte access per tensor; it needs whole 8-channel groups (H/G % 8 == 0) and 16-byte
-  // aligned rows.  Otherwise one element per access.
+  // 16-byte access per tensor.  Otherwise one element per access.
   constexpr int VPR = CH / 8;
-  constexpr bool kVecT = std::is_same<T, bf16_t>::value && CH % 8 == 0 && 256 / VPR >= TT;
-  const bool vec = kVecT && HPG % 8 == 0 && p.x_st % 8 == 0 && p.dt_st % 8 == 0 &&
-                   p.y_st % 8 == 0 &&
-                   ((reinterpret_cast<uintptr_t>(p.x) | reinterpret_cast<uintptr_t>(p.dt) |
-                     reinterpret_cast<uintptr_t>(p.y)) & 15) == 0;
+  constexpr bool vec = kVec;
   const int vtt = tid / VPR, vc8 = (tid % VPR) * 8, vch = c0 + vc8;
   const bool vin = vc8 < nch;
   u32x4_v vd = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
   auto fetch = [&](int tb) {
     const int nt = min(TT, t1 - tb);
-    if (vec) {
+    // B / C first: their zero fill then never waits behind the x / delta loads
+#pragma unroll
+    for (int u = 0; u < NBCI; ++u) {
+      const int e = u * 256 + tid;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rbc[u][i] = T(0);
+      const int tt = e / (2 * (N / 4)), q = e % (2 * (N / 4));
+      const int which = q / (N / 4), n4 = q % (N / 4);
+      if (e < NBC && tt < nt) {
+        const T* src = (which ? cg : bg) + int64_t(tb + tt) * p.bc_st + n4 * 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rbc[u][i] = src[i];
+      }
+    }
+    if constexpr (vec) {
       const bool in = vtt < nt && vin;
       vd = in ? *reinterpret_cast<const u32x4_v*>(dg + int64_t(tb + vtt) * p.dt_st + vch)
               : u32x4_v{0u, 0u, 0u, 0u};
@@ -216,31 +253,33 @@ __device__ __forceinline__ void diag_body(const PrefillParams& p, const DiagWork
         rx[u] = in ? xg[t * p.x_st + chc] : T(0);
       }
     }
-#pragma unroll
-    for (int u = 0; u < NBCI; ++u) {
-      const int e = u * 256 + tid;
-      rbc[u] = float4_v{0.f, 0.f, 0.f, 0.f};
-      const int tt = e / (2 * (N / 4)), q = e % (2 * (N / 4));
-      const int which = q / (N / 4), n4 = q % (N / 4);
-      if (e < NBC && tt < nt) {
-        const T* src = (which ? cg : bg) + int64_t(tb + tt) * p.bc_st + n4 * 4;
-        rbc[u] = float4_v{Elem<T>::load(src), Elem<T>::load(src + 1), Elem<T>::load(src + 2),
-                          Elem<T>::load(src + 3)};
-      }
-    }
   };
+  // per-thread constants of the staging: the dt bias of each channel this thread stages
+  // (the 8 of its vector, or the one of its column: 256 is a multiple of CH)
+  static_assert(256 % CH == 0, "one staging column per thread");
+  constexpr int NB = vec ? 8 : 1;
+  float bias[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int cc = vec ? vc8 + i : tid % CH;
+    bias[i] = cc < nch ? p.prep.bias_of(c0 + cc) : 0.f;
+  }
+  // Wait here for the loads above (pool state, A, D, bias): a load still outstanding when
+  // the tile loop starts would be waited for inside it, behind each tile's prefetch.
+  __builtin_amdgcn_s_waitcnt(0);
   fetch(t0);
   for (int tb = t0; tb < t1; tb += TT) {
     const int nt = min(TT, t1 - tb);
-    if (vec) {
+    if constexpr (vec) {
       const bool in = vtt < nt && vin;
       float dv8[8], xv8[8];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         xv8[2 * k] = __uint_as_float(vx[k] << 16);
         xv8[2 * k + 1] = __uint_as_float(vx[k] & 0xffff0000u);
-        dv8[2 * k] = in ? p.prep(__uint_as_float(vd[k] << 16), vch + 2 * k) : 0.f;
-        dv8[2 * k + 1] = in ? p.prep(__uint_as_float(vd[k] & 0xffff0000u), vch + 2 * k + 1) : 0.f;
+        dv8[2 * k] = in ? p.prep.apply(__uint_as_float(vd[k] << 16), bias[2 * k]) : 0.f;
+        dv8[2 * k + 1] = in ? p.prep.apply(__uint_as_float(vd[k] & 0xffff0000u), bias[2 * k + 1])
+                            : 0.f;
       }
       if (vtt < TT) {
         *reinterpret_cast<float4_v*>(&s_d[vtt][vc8]) = float4_v{dv8[0], dv8[1], dv8[2], dv8[3]};
@@ -253,7 +292,7 @@ __device__ __forceinline__ void diag_body(const PrefillParams& p, const DiagWork
       for (int u = 0; u < NE; ++u) {
         const int e = u * 256 + tid, tt = e / CH, cc = e % CH;
         const bool in = tt < nt && cc < nch;
-        s_d[tt][cc] = in ? p.prep(to_f32(rd[u]), c0 + cc) : 0.f;
+        s_d[tt][cc] = in ? p.prep.apply(to_f32(rd[u]), bias[0]) : 0.f;
         s_x[tt][cc] = to_f32(rx[u]);
       }
     }
@@ -263,7 +302,8 @@ __device__ __forceinline__ void diag_body(const PrefillParams& p, const DiagWork
       const int tt = e / (2 * (N / 4)), q = e % (2 * (N / 4));
       const int which = q / (N / 4), n4 = q % (N / 4);
       if (e < NBC)
-        *reinterpret_cast<float4_v*>(which ? &s_c[tt][4 * n4] : &s_b[tt][4 * n4]) = rbc[u];
+        *reinterpret_cast<float4_v*>(which ? &s_c[tt][4 * n4] : &s_b[tt][4 * n4]) =
+            float4_v{to_f32(rbc[u][0]), to_f32(rbc[u][1]), to_f32(rbc[u][2]), to_f32(rbc[u][3])};
     }
     __syncthreads();
     if (tb + TT < t1) fetch(tb + TT);
@@ -340,7 +380,7 @@ __device__ __forceinline__ void diag_body(const PrefillParams& p, const DiagWork
       }
     }
     __syncthreads();
-    if (vec) {
+    if constexpr (vec) {
       if (vtt < nt && vin) {
         const float4_v a = *reinterpret_cast<const float4_v*>(&s_y[vtt][vc8]);
         const float4_v b = *reinterpret_cast<const float4_v*>(&s_y[vtt][vc8 + 4]);
@@ -364,12 +404,21 @@ __device__ __forceinline__ void diag_body(const PrefillParams& p, const DiagWork
 
 // One workgroup per (group, block of CH channels) and sequence (blockIdx.y).
 template <typename T, int NS, int SPL, bool kScalarA>
+__device__ __forceinline__ void diag_run(const PrefillParams& p, const DiagWork w,
+                                         DiagSmem<NS, SPL>& sm) {
+  if (diag_vec_ok<T, DiagCfg<NS, SPL>::CH>(p)) diag_body<T, NS, SPL, kScalarA, true>(p, w, sm);
+  else diag_body<T, NS, SPL, kScalarA, false>(p, w, sm);
+}
+
+template <typename T, int NS, int SPL, bool kScalarA>
 __global__ __launch_bounds__(256) void k_diag_scan(PrefillParams p) {
+  __shared__ DiagSmem<NS, SPL> sm;
   constexpr int CH = DiagCfg<NS, SPL>::CH;
   const int HPG = p.H / p.G, nb = diag_blocks_per_group(p.H, p.G, CH);
   const int g = blockIdx.x / nb, jb = blockIdx.x % nb;
-  diag_body<T, NS, SPL, kScalarA>(
-      p, DiagWork{int(blockIdx.y), g, g * HPG + jb * CH, min(CH, HPG - jb * CH), blockIdx.x == 0});
+  diag_run<T, NS, SPL, kScalarA>(
+      p, DiagWork{int(blockIdx.y), g, g * HPG + jb * CH, min(CH, HPG - jb * CH), blockIdx.x == 0},
+      sm);
 }
 
 // Mamba1 (one group) in workgroups of two sizes: per sequence nbig blocks of 64 channels
@@ -383,10 +432,14 @@ __global__ __launch_bounds__(256) void k_diag_scan(PrefillParams p) {
 // round-robin over the 8 XCDs), so the segment is fetched into one L2, not two.
 template <typename T>
 __global__ __launch_bounds__(256) void k_diag_scan_mixed(PrefillParams p, int nbig, int nsmall) {
+  __shared__ union {
+    DiagSmem<kDiagN, 4> big;
+    DiagSmem<kDiagN, 2> small;
+  } sm;
   const int b = blockIdx.x;
   if (b < p.S * nbig) {
     const int r = b / nbig, j = b - r * nbig;
-    diag_body<T, kDiagN, 4, false>(p, DiagWork{r, 0, 64 * j, 64, j == 0});
+    diag_run<T, kDiagN, 4, false>(p, DiagWork{r, 0, 64 * j, 64, j == 0}, sm.big);
   } else {
     // ids base .. base+15 take the even and then the odd halves of blocks base/2 .. +7
     // (a last partial run of 16 keeps the identity order)
@@ -394,7 +447,8 @@ __global__ __launch_bounds__(256) void k_diag_scan_mixed(PrefillParams p, int nb
     const int b2 = base + 16 <= p.S * nsmall ? base + 2 * (i & 7) + ((i >> 3) & 1) : i;
     const int r = b2 / nsmall, j = b2 - r * nsmall;
     const int c0 = 64 * nbig + 32 * j;
-    diag_body<T, kDiagN, 2, false>(p, DiagWork{r, 0, c0, min(32, p.H - c0), nbig == 0 && j == 0});
+    diag_run<T, kDiagN, 2, false>(p, DiagWork{r, 0, c0, min(32, p.H - c0), nbig == 0 && j == 0},
+                                  sm.small);
   }
 }
 
