@@ -242,35 +242,65 @@ constexpr int kDiagDecodeChannels = 64;   // channels per 256-thread workgroup
 template <typename T, typename S>
 __global__ __launch_bounds__(256) void k_state_update_diag(DecodeParams p) {
   constexpr int N = kDiagN, SPL = 4;
+  constexpr int NBC = (kDecodeMaxTokens * 2 * N + 255) / 256;   // B/C elements per thread
   __shared__ __attribute__((aligned(16))) float s_bc[kDecodeMaxTokens][2][N];
   const int r = blockIdx.y, tid = threadIdx.x;
   const int c = blockIdx.x * kDiagDecodeChannels + tid / SPL, q = tid % SPL;
   const int ntok = p.ntok, H = p.H;
   DecodeRow row;
   if (decode_row(p, r, tid == 0 && blockIdx.x == 0, row) <= 0) return;   // padding or invalid
-  // the source state first (read before any write), then the row's B and C
+  // Every load of the step goes out before the first wait: the source state (read before
+  // any write), A, the row's B and C (raw), and this channel's delta and x of every token
+  // (raw).  Values are converted where they are used, so that no wait inside the token
+  // loop also waits for a later load.
   const bool live = c < H;
   const int cc = live ? c : H - 1;
   float4_v h = PoolIO<S>::ld4(p.pool, int64_t(row.src) * p.slot_stride + int64_t(cc) * N + SPL * q);
   const float4_v a = *reinterpret_cast<const float4_v*>(p.A + int64_t(cc) * N + SPL * q);
-  const float A2[SPL] = {a.x * kLog2e, a.y * kLog2e, a.z * kLog2e, a.w * kLog2e};
   const T* bg = static_cast<const T*>(p.B);
   const T* cg = static_cast<const T*>(p.Cm);
-  for (int e = tid; e < ntok * 2 * N; e += 256) {
+  // (unconditional loads, positions past the row's tokens clamped to its last token; only
+  // the LDS writes below are predicated, after every other load has gone out)
+  T rbc[NBC];
+#pragma unroll
+  for (int u = 0; u < NBC; ++u) {
+    const int e = u * 256 + tid;
     const int j = e / (2 * N), w = (e / N) & 1, n = e % N;
-    s_bc[j][w][n] = Elem<T>::load((w ? cg : bg) + (int64_t(r) * ntok + j) * N + n);
+    rbc[u] = ((w ? cg : bg) + (int64_t(r) * ntok + min(j, ntok - 1)) * N)[n];
+  }
+  const T* xg = static_cast<const T*>(p.x);
+  const T* dg = static_cast<const T*>(p.dt);
+  // raw values one per register (a 16-bit value zero-extended), so that none is packed with
+  // another before the token that uses it
+  using Raw = typename std::conditional<sizeof(T) == 2, uint32_t, float>::type;
+  Raw rd[kDecodeMaxTokens], rx[kDecodeMaxTokens];
+#pragma unroll
+  for (int j = 0; j < kDecodeMaxTokens; ++j) {
+    if (j < ntok) {
+      const int64_t tj = (int64_t(r) * ntok + j) * H + cc;
+      rd[j] = dg[tj];
+      rx[j] = xg[tj];
+    }
+  }
+  const float bias = p.prep.bias_of(cc);
+  const float Dc = p.D ? p.D[cc] : 0.f;
+#pragma unroll
+  for (int u = 0; u < NBC; ++u) {
+    const int e = u * 256 + tid;
+    const int j = e / (2 * N), w = (e / N) & 1, n = e % N;
+    if (j < ntok) s_bc[j][w][n] = to_f32(rbc[u]);
   }
   __syncthreads();
   if (!live) return;   // whole 4-lane groups leave together
 
-  const T* xg = static_cast<const T*>(p.x);
-  const T* dg = static_cast<const T*>(p.dt);
+  const float A2[SPL] = {a.x * kLog2e, a.y * kLog2e, a.z * kLog2e, a.w * kLog2e};
   T* yg = static_cast<T*>(p.y);
-  const float Dc = p.D ? p.D[c] : 0.f;
-  for (int j = 0; j < ntok; ++j) {
+#pragma unroll
+  for (int j = 0; j < kDecodeMaxTokens; ++j) {
+    if (j >= ntok) continue;
     const int64_t tj = (int64_t(r) * ntok + j) * H + c;
-    const float delta = p.prep(Elem<T>::load(dg + tj), c);
-    const float xv = Elem<T>::load(xg + tj);
+    const float delta = p.prep.apply(to_f32(T(rd[j])), bias);
+    const float xv = to_f32(T(rx[j]));
     const float dx = delta * xv;
     const float4_v bv = *reinterpret_cast<const float4_v*>(&s_bc[j][0][SPL * q]);
     const float4_v cv = *reinterpret_cast<const float4_v*>(&s_bc[j][1][SPL * q]);
@@ -283,7 +313,8 @@ __global__ __launch_bounds__(256) void k_state_update_diag(DecodeParams p) {
     acc += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, acc), 0xB1, 0xF, 0xF, true));
     acc += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, acc), 0x4E, 0xF, 0xF, true));
     if (q == 0) Elem<T>::store(yg + tj, acc + Dc * xv);
-    PoolIO<S>::st4_nt(p.pool, int64_t(row.dst(j)) * p.slot_stride + int64_t(c) * N + SPL * q, h);
+    const int dst = row.one >= 0 ? row.one : ld_meta(row.idx, j);   // wave-uniform: scalar
+    PoolIO<S>::st4_nt(p.pool, int64_t(dst) * p.slot_stride + int64_t(c) * N + SPL * q, h);
   }
 }
 
