@@ -188,6 +188,27 @@ def test_kernel_count():
     assert n.value == 0
 
 
+@pytest.mark.parametrize("S,H,mixed", [
+    (8, 5120, True),    # 640 workgroups of 64 channels on 256 CUs: 3 passes on half the CUs
+    (4, 5120, True),    # the shapes of the mixed-grid GPU tests
+    (7, 2312, True),
+    (6, 72, True),
+    (1, 200, False),    # 2 + 3 workgroups: no shorter than the 4 of 64 channels
+    (3, 5000, False),   # uniform grid in one pass; mixed needs two
+])
+def test_diag_grid_choice(S, H, mixed):
+    """The Mamba1 scan's grid as the host picks it on a 256-CU device (the count the
+    library assumes without one): the kernel name ssd_prefill_kernel_count reports."""
+    n = ctypes.c_int32(-1)
+    names = (ctypes.c_char_p * _abi.SSD_PREFILL_MAX_KERNELS)()
+    a = _good_prefill(a_kind=_abi.SSD_A_DIAG, H=H, P=1, G=1, N=16, num_seqs=S, num_chunks=S,
+                      T=64 * S, chunk_size=64, x_stride_t=H, y_stride_t=H, dt_stride_t=H,
+                      bc_stride_t=16)
+    assert lib().ssd_prefill_kernel_count(ctypes.byref(a), ctypes.byref(n), names) == 0
+    assert n.value == 1
+    assert names[0] == (b"k_diag_scan_mixed" if mixed else b"k_diag_scan")
+
+
 @pytest.mark.parametrize("over,status", [
     (dict(H=6, G=4), _abi.SSD_ERR_BAD_SHAPE),             # H % G != 0
     (dict(P=0), _abi.SSD_ERR_BAD_SHAPE),

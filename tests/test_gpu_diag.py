@@ -95,15 +95,30 @@ def test_full_mamba1_long_diag():
     check_prefill(inp, got, oracle_prefill(inp, seqs=[3], heads=chans), heads=chans)
 
 
+MIXED_SHAPES = {
+    # 4 x 5120: 64 large and 32 small workgroups per sequence, the small ones paired in
+    # whole runs of 16 workgroup ids
+    "4x5120": ([150, 97, 130, 64], [0, 5, 60, 3], 5120),
+    # 7 x 2312: 28 large and 17 small per sequence (pairs of small workgroups cross
+    # sequence boundaries, 119 small ones leave a run of 7 unpaired; the last small
+    # workgroup of a sequence holds 8 channels)
+    "7x2312": ([70, 33, 96, 64, 1, 129, 40], [0, 7, 60, 3, 0, 1, 9], 2312),
+    # 6 x 72: small workgroups only (3 per sequence, the third with 8 channels)
+    "6x72": ([90, 64, 3, 130, 65, 20], [1, 0, 2, 63, 64, 0], 72),
+}
+
+
+@pytest.mark.parametrize("shape", sorted(MIXED_SHAPES))
 @pytest.mark.parametrize("dtype,pool", [("bf16", "f32"), ("bf16", "bf16"), ("f32", "f16")])
-def test_diag_mixed_workgroup_grid(dtype, pool):
-    """A Mamba1 batch wide enough (4 sequences x 5120 channels) for the grid of 64-channel
-    workgroups with 4 states per lane and 32-channel ones with 2 states per lane: every
-    channel of both kinds, its checkpoints and its pool entries against the oracle."""
+def test_diag_mixed_workgroup_grid(dtype, pool, shape):
+    """Mamba1 batches for which the host picks the grid of 64-channel workgroups with 4
+    states per lane and 32-channel ones with 2 states per lane (on 256 CUs): every channel
+    of both kinds, its checkpoints and its pool entries against the oracle."""
     from gpu_helpers import pool_tol, rounded_pool
-    inp = make_prefill(44, in_dtype=dtype, H=5120, P=1, G=1, N=16, chunk_size=64,
-                       lengths=[150, 97, 130, 64], num_computed=[0, 5, 60, 3], a_kind="diag",
-                       init="pool", pool_slots=8)
+    lengths, computed, H = MIXED_SHAPES[shape]
+    inp = make_prefill(44, in_dtype=dtype, H=H, P=1, G=1, N=16, chunk_size=64,
+                       lengths=lengths, num_computed=computed, a_kind="diag",
+                       init="pool", pool_slots=2 * len(lengths))
     if pool != "f32":
         rounded_pool(inp, pool)
     got = run_prefill(inp)
