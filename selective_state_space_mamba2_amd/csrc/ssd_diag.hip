@@ -16,6 +16,11 @@
 // through LDS with coalesced loads (64 channels = 128 B per token for bf16), delta is
 // prepared once per (token, channel) while staging, and y leaves through an LDS tile as
 // coalesced rows.  Checkpoints are written at the chunk ends listed by the chunk metadata.
+//
+// Two grids: k_diag_scan, one workgroup per (sequence, group, block of CH channels), and
+// for Mamba1 (N = 16, one group) k_diag_scan_mixed, which covers part of the channels with
+// 32-channel workgroups of two states per lane when that spreads the work more evenly over
+// the SIMDs (the host picks it with a model of the dispatch, see mamba1_grid).
 #include <algorithm>
 #include <atomic>
 #include <cstdint>
