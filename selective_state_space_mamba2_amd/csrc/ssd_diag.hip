@@ -347,10 +347,15 @@ __device__ __forceinline__ void diag_body(const PrefillParams& p, const DiagWork
         }
       }
 #pragma unroll
-      for (int u = 0; u < V; ++u) acc[u] = group_sum<LPC>(acc[u]);
+      for (int u = 0; u < V; ++u) {
+        acc[u] = group_sum<LPC>(acc[u]) + Dc * xv[u];
+        // y complete on every lane here: left to the branch below, the last add of each
+        // sum moves into it and its permutation becomes a separate instruction
+        asm volatile("" ::"v"(acc[u]));
+      }
       if (ng == 0) {
 #pragma unroll
-        for (int u = 0; u < V; ++u) s_y[tt + u][cl] = acc[u] + Dc * xv[u];
+        for (int u = 0; u < V; ++u) s_y[tt + u][cl] = acc[u];
       }
     };
     int tt = 0;
