@@ -77,10 +77,14 @@ def test_diag_several_checkpoints_per_token_tile():
     check_prefill(inp, got, oracle_prefill(inp))
 
 
-def test_diag_softplus_and_long_memory():
-    inp = make_prefill(41, in_dtype="f32", H=64, P=1, G=1, N=16, chunk_size=64,
+@pytest.mark.parametrize("dtype,H", [("f32", 64), ("bf16", 64), ("bf16", 200)])
+def test_diag_softplus_and_long_memory(dtype, H):
+    """dt bias, softplus and a dt limit with slow decays (long memory): the element path
+    (fp32), and the 16-byte path of the 32-channel (64 channels) and the 64-channel (200
+    channels) workgroups, each with its own per-channel bias registers."""
+    inp = make_prefill(41, in_dtype=dtype, H=H, P=1, G=1, N=16, chunk_size=64,
                        lengths=[500], a_kind="diag", A_range=(1e-3, 1e-2))
-    bias = np.random.default_rng(1).normal(-1, 0.3, 64).astype(np.float32).astype(np.float64)
+    bias = np.random.default_rng(1).normal(-1, 0.3, H).astype(np.float32).astype(np.float64)
     got = run_prefill(inp, dt_bias=bias, softplus=True, dt_limit=(0.0, 0.5))
     check_prefill(inp, got, oracle_prefill(inp, dt_bias=bias, softplus=True,
                                            dt_limit=(0.0, 0.5)))
