@@ -128,3 +128,53 @@ def test_diag_mixed_workgroup_grid(dtype, pool, shape):
     got = run_prefill(inp)
     assert got["flag"] == 0
     check_prefill(inp, got, oracle_prefill(inp), pool_tol=pool_tol(inp))
+
+
+@pytest.mark.parametrize("H,lengths,computed", [
+    (5120, [150, 97, 130, 64], [0, 5, 60, 3]),    # the mixed grid
+    (200, [150, 77], [0, 9]),                     # the uniform grid
+])
+def test_diag_graph_capture_and_replay(H, lengths, computed):
+    """The Mamba1 scan captured in a HIP graph and replayed several times with eager work
+    in between gives the eager call's y, checkpoints and pool on every replay."""
+    import torch
+    from gpu_helpers import dev_f32, dev_i32, dev_token, prefill_metadata
+    from selective_state_space_mamba2_amd import api
+    inp = make_prefill(46, in_dtype="bf16", H=H, P=1, G=1, N=16, chunk_size=64,
+                       lengths=lengths, num_computed=computed, a_kind="diag", init="pool",
+                       pool_slots=2 * len(lengths))
+    cuc, sidx, last = prefill_metadata(inp)
+    x, dt, B, C = (dev_token(inp, n) for n in ("x", "dt", "B", "C"))
+    A, D = dev_f32(inp.A), dev_f32(inp.D)
+    md = [dev_i32(inp.cu_seqlens), dev_i32(cuc), dev_i32(sidx), dev_i32(last)]
+    pool0 = torch.from_numpy(inp.pool).cuda()
+    pool = pool0.clone()
+    y = torch.zeros_like(x)
+    states = torch.zeros(len(sidx), H, 1, 16, device="cuda")
+    kw = dict(y=y, D=D, state_pool=pool, state_indices=dev_i32(inp.state_indices),
+              has_initial_state=dev_i32(inp.has_initial_state), write_final_to_pool=True,
+              chunk_states_out=states)
+    args = api.prefill_args(x, dt, A, B, C, 64, *md, **kw)
+    ws = torch.empty(max(api.ssd_prefill_workspace_size(args), 256), dtype=torch.uint8,
+                     device="cuda")
+    api.ssd_prefill(x, dt, A, B, C, 64, *md, workspace=ws, **kw)
+    torch.cuda.synchronize()
+    y_eager, st_eager, pool_eager = y.clone(), states.clone(), pool.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            api.ssd_prefill(x, dt, A, B, C, 64, *md, workspace=ws, stream=s, **kw)
+    torch.cuda.current_stream().wait_stream(s)
+    for _ in range(3):
+        pool.copy_(pool0)
+        y.zero_()
+        states.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager)
+        assert torch.equal(states, st_eager)
+        assert torch.equal(pool, pool_eager)
+        _ = (x.float() * 2).sum().item()       # unrelated eager work between replays
