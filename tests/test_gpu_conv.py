@@ -180,3 +180,52 @@ def test_update_padded_batch(dtype, layout, ntok):
         np.testing.assert_array_equal(ph[slot], st, f"slot {slot}")
     untouched = sorted(set(range(inp.pool.shape[0])) - set(writes))
     np.testing.assert_array_equal(ph[untouched], inp.pool[untouched])
+
+
+def test_prefill_and_update_graph_capture_and_replay():
+    """The conv prefill (output and state write-back kernels) followed by a decode update,
+    captured in one HIP graph and replayed several times with eager work in between, gives
+    the eager calls' outputs and pool on every replay."""
+    t = torch()
+    inp = make_conv(68, in_dtype="bf16", D=1040, lengths=LENGTHS, num_computed=NC,
+                    pool_slots=12)
+    cuc, sidx, _ = api.ssd_build_chunk_metadata(inp.cu_seqlens, inp.num_computed, 64)
+    xd = _dev_x(inp, inp.x)
+    w, b = _f32(inp.weight), _f32(inp.bias)
+    md = [_i32(inp.cu_seqlens), _i32(cuc), _i32(sidx)]
+    pool0 = _dev_pool(inp, "sd")
+    pool = pool0.clone()
+    out = t.zeros_like(xd)
+    S = len(LENGTHS)
+    xu = _dev_x(inp, inp.x[:S]).reshape(S, 1, inp.D)      # one decode input per sequence
+    out_u = t.zeros_like(xu)
+    idx, has = _i32(inp.state_indices), _i32(inp.has_initial_state)
+
+    def step(stream=None):
+        api.ssd_conv1d_prefill(xd, w, b, *md, out=out, activation=True, conv_states=pool,
+                               state_indices=idx, has_initial_state=has, stream=stream)
+        api.ssd_conv1d_update(xu, w, b, pool, idx, out=out_u, activation=True,
+                              null_block_id=0, stream=stream)
+
+    step()
+    t.cuda.synchronize()
+    out_eager, out_u_eager, pool_eager = out.clone(), out_u.clone(), pool.clone()
+    s = t.cuda.Stream()
+    s.wait_stream(t.cuda.current_stream())
+    g = t.cuda.CUDAGraph()
+    pool.copy_(pool0)
+    with t.cuda.stream(s):
+        with t.cuda.graph(g, stream=s):
+            step(stream=s)
+    t.cuda.current_stream().wait_stream(s)
+    for _ in range(3):
+        pool.copy_(pool0)
+        out.zero_()
+        out_u.zero_()
+        t.cuda.synchronize()
+        g.replay()
+        t.cuda.synchronize()
+        assert t.equal(out, out_eager)
+        assert t.equal(out_u, out_u_eager)
+        assert t.equal(pool, pool_eager)
+        _ = (xd.float() * 2).sum().item()       # unrelated eager work between replays
