@@ -126,7 +126,8 @@ EXPORTS = {
     "ssd_conv1d_prefill": (ctypes.c_int, [ctypes.POINTER(Conv1dArgs), _vp]),
     "ssd_conv1d_update": (ctypes.c_int, [ctypes.POINTER(Conv1dUpdateArgs), _vp]),
     # include/ssd_probe.h (measurement aid)
-    "ssd_probe_stream": (ctypes.c_int, [_vp, ctypes.c_size_t, _vp, ctypes.c_size_t, _vp, _vp]),
+    "ssd_probe_stream": (ctypes.c_int, [_vp, ctypes.c_size_t, _vp, ctypes.c_size_t, _vp,
+                                        ctypes.c_int32, _vp]),
 }
 
 _lib = None

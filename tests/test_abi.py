@@ -416,12 +416,14 @@ def test_conv1d_update_host_checks(over, status):
 
 def test_probe_stream_host_checks():
     f = lib().ssd_probe_stream
-    assert f(FAKE, 16, FAKE, 16, None, None) == _abi.SSD_ERR_NULL_POINTER      # no sink
-    assert f(None, 16, FAKE, 0, FAKE, None) == _abi.SSD_ERR_NULL_POINTER
-    assert f(FAKE, 15, FAKE, 16, FAKE, None) == _abi.SSD_ERR_BAD_SHAPE
-    assert f(FAKE + 4, 16, FAKE, 16, FAKE, None) == _abi.SSD_ERR_UNSUPPORTED
-    assert f(FAKE, (1 << 35) + 16, FAKE, 0, FAKE, None) == _abi.SSD_ERR_BAD_SHAPE
-    assert f(None, 0, None, 0, FAKE, None) == 0                               # nothing to move
+    assert f(FAKE, 16, FAKE, 16, None, 0, None) == _abi.SSD_ERR_NULL_POINTER   # no sink
+    assert f(None, 16, FAKE, 0, FAKE, 0, None) == _abi.SSD_ERR_NULL_POINTER
+    assert f(FAKE, 15, FAKE, 16, FAKE, 0, None) == _abi.SSD_ERR_BAD_SHAPE
+    assert f(FAKE + 4, 16, FAKE, 16, FAKE, 0, None) == _abi.SSD_ERR_UNSUPPORTED
+    assert f(FAKE, (1 << 35) + 16, FAKE, 0, FAKE, 0, None) == _abi.SSD_ERR_BAD_SHAPE
+    assert f(FAKE, 16, FAKE, 16, FAKE, 12, None) == _abi.SSD_ERR_BAD_SHAPE    # no such form
+    assert f(FAKE, 16, FAKE, 16, FAKE, -1, None) == _abi.SSD_ERR_BAD_SHAPE
+    assert f(None, 0, None, 0, FAKE, 11, None) == 0                           # nothing to move
 
 
 def test_prefill_noalloc_host_checks():
